@@ -1,0 +1,345 @@
+"""Pins of the CPU oracle to things other than itself: values the pages and the
+OCP fp8 spec fix, library routines, closed forms, brute force, and invariants
+the pages state.  No GPU."""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+import oracle as O
+from oracle import harness as H
+from workloads import CONFIGS, make_workload, small_variant
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _golden(name):
+    with open(os.path.join(GOLDEN, name)) as f:
+        return json.load(f)
+
+
+# --------------------------------------------------------------------------- formats
+
+
+def test_bf16_decode_matches_torch_on_every_pattern():
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    ours = O.bf16_bits_to_f64(bits)
+    ref = torch.from_numpy(bits.view(np.int16)).view(torch.bfloat16).to(torch.float64).numpy()
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+
+
+def test_e4m3_code_values_match_the_ocp_table():
+    g = _golden("e4m3_codes.json")
+    vals = O.e4m3_code_values()
+    for code, want in g["codes"].items():
+        got = vals[int(code, 16)]
+        assert got == want and math.copysign(1, got) == math.copysign(1, want), code
+    for code in g["nan_codes"]:
+        assert math.isnan(vals[int(code, 16)])
+    finite = vals[~np.isnan(vals)]
+    assert len(finite) == 254 and finite.max() == 448.0 and finite.min() == -448.0
+
+
+def test_e4m3_encode_golden_cases():
+    g = _golden("e4m3_codes.json")
+    for case in g["encode_cases"]:
+        x = float(case["x"])
+        assert int(O.e4m3_encode(np.array([x]))[0]) == int(case["code"], 16), case["why"]
+    assert int(O.e4m3_encode(np.array([np.nan]))[0]) & 0x7F == 0x7F
+
+
+def test_e4m3_decode_matches_torch():
+    codes = np.arange(256, dtype=np.uint8)
+    ref = torch.from_numpy(codes).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ours = O.e4m3_decode(codes)
+    same = (ours == ref) | (np.isnan(ours) & np.isnan(ref))
+    assert same.all()
+
+
+@pytest.mark.parametrize("inv_scale", [1.0, 1.0 / 3.7, 448.0 / 4.5, 0.001, 37.0])
+def test_e4m3_quantiser_matches_torch_cast_on_all_bf16_inputs(inv_scale):
+    """The pool cast (bf16 -> fp32 * inv_scale -> e4m3, RNE, saturating) against
+    torch's float8_e4m3fn cast of the same fp32 product.  torch does not
+    saturate (beyond the rounding range it yields NaN), so the comparison is
+    restricted to products that round to a finite value, and saturation is
+    pinned separately above."""
+    bits = np.arange(1 << 16, dtype=np.uint32).astype(np.uint16)
+    x = O.bf16_bits_to_f64(bits)
+    keep = np.isfinite(x)
+    bits, x = bits[keep], x[keep]
+    prod32 = (torch.from_numpy(x).to(torch.float32) * torch.tensor(np.float32(inv_scale))).to(torch.float32)
+    in_range = prod32.abs() < 464.0
+    ref = prod32[in_range].to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    ours = O.encode_for_pool(bits, O.BF16, O.FP8, inv_scale)[in_range.numpy()]
+    assert np.array_equal(ours, ref)
+    sat = O.encode_for_pool(bits, O.BF16, O.FP8, inv_scale)[~in_range.numpy()]
+    assert np.all((sat & 0x7F) == 0x7E)
+
+
+# --------------------------------------------------------------------------- metadata
+
+
+def test_slot_mapping_ragged_chunk_worked_example():
+    """P2: after one 24-token chunk in 16-token blocks, the next chunk's first
+    slot is the history's tail block * 16 + 8."""
+    g = _golden("window_geometry.json")["ragged_chunk"]
+    ids = [5, 9, 2]  # any physical blocks for logical blocks 0, 1, 2
+    first = int(O.slot_mapping(ids, [g["chunk"]], g["block"])[0])
+    assert first == ids[1] * 16 + 8
+    # and the whole chunk is contiguous with its history
+    slots = O.slot_mapping(ids, np.arange(24, 48), 16)
+    assert list(slots[:8]) == [9 * 16 + o for o in range(8, 16)]
+    assert list(slots[8:24]) == [2 * 16 + o for o in range(16)]
+
+
+def test_frame_geometry_numbers():
+    g = _golden("window_geometry.json")
+    assert (480 // 16) * (832 // 16) == g["frame_tokens"]
+    assert g["frame_tokens"] % 16 == g["frame_mod_block"]
+    assert -(-g["frame_tokens"] // 16) == g["blocks_per_frame"]
+
+
+def test_visible_window_slid_worked_example():
+    g = _golden("window_geometry.json")["slid_window"]
+    end = g["history"] + g["query"]
+    ids = np.arange(10_000, 10_000 + -(-end // 16))
+    win = O.visible_window(ids, end, g["sink_chunks"] * g["chunk"], g["window_tokens"], g["block"])
+    assert win.kv_len == g["expected_kv_len"]
+    assert len(win.table) == g["expected_table_len"]
+    lo, hi = g["expected_sink_blocks"]
+    assert win.table[: hi + 1] == list(ids[lo : hi + 1])
+    assert win.table[hi + 1] == ids[g["expected_recent_first_block"]]
+    assert win.positions[1567] == 1567 and win.positions[1568] == 487 * 16
+
+
+def _index_range_window(ids, history, q, sink, window, B):
+    """P1 ``video_block_table`` in its own (index-range) formulation, as a second
+    statement of the rule: sink blocks and blocks from the recent start onward,
+    the current chunk's blocks always listed, blocks wholly between the two
+    ranges skipped, lengths ``min(B, end - first)``."""
+    end = history + q
+    recent_start = end - window
+    hist_blocks = -(-history // B)
+    sink_blocks = min(-(-sink // B), hist_blocks)
+    recent_first = max(max(recent_start, 0) // B, sink_blocks)
+    first_pos = {}
+    for i in [*range(sink_blocks), *range(recent_first, hist_blocks)]:
+        if ids[i] >= 0:
+            first_pos.setdefault(ids[i], i * B)
+    cur_first = history - history % B
+    for n in range(-(-(history % B + q) // B)):
+        first_pos.setdefault(ids[cur_first // B + n], cur_first + n * B)
+    table, length = [], 0
+    for blk, first in sorted(first_pos.items(), key=lambda kv: kv[1]):
+        if first >= sink and first + B <= recent_start:
+            continue
+        table.append(int(blk))
+        length += min(B, end - first)
+    return table, length
+
+
+@pytest.mark.parametrize("chunk,sink_chunks,window_chunks", [(24, 1, 2), (24, 0, 2), (24, 1, 3), (1560, 9, 9), (16, 1, 2), (40, 2, 3)])
+def test_visible_window_agrees_with_index_range_rule_and_page_invariants(chunk, sink_chunks, window_chunks):
+    B = 16
+    rng = np.random.default_rng(chunk * 31 + sink_chunks)
+    frames_per_tick = 3 if chunk == 1560 else 1
+    sink, window = sink_chunks * chunk, window_chunks * chunk
+    total_ticks = 12
+    ids = rng.permutation(10 * (total_ticks * frames_per_tick * chunk // B + 4))
+    widths = set()
+    for tick in range(total_ticks):
+        q = frames_per_tick * chunk
+        history = tick * q
+        end = history + q
+        win = O.visible_window(ids, end, sink, window, B)
+        ref_table, ref_len = _index_range_window(ids, history, q, sink, window, B)
+        assert win.table == ref_table and win.kv_len == ref_len
+        # every kept token is read, in order, and each read slot holds its position
+        kept = set(range(min(sink, end))) | set(range(max(end - window, 0), end))
+        assert kept <= set(win.positions)
+        assert win.positions == sorted(win.positions)
+        assert win.kv_len == len(win.positions)
+        # whole blocks: at most B - 1 extra tokens at each of the two boundaries (P2)
+        assert win.kv_len <= min(end, sink + window) + 2 * (B - 1)
+        for n, p in enumerate(win.positions):
+            assert win.table[n // B] == ids[p // B] and n % B == p % B
+        widths.add(len(win.table))
+    assert max(widths) <= -(-sink // B) + -(-window // B) + 1
+
+
+def test_segments_golden():
+    for case in _golden("segments.json")["cases"]:
+        segs = O.build_segments([tuple(s) for s in case["spans"]], case["query_offset"], case["query_len"])
+        assert [[s.q_start, s.q_end, s.kv_end, s.mode] for s in segs] == case["segments"], case["why"]
+
+
+def test_row_limits_against_the_docstring_rule_by_enumeration():
+    """P3's docstring: a row inside a full span [a, b) sees keys < b; any other
+    row is causal and sees keys <= its own position.  Enumerate random span sets
+    and compare every row."""
+    rng = np.random.default_rng(7)
+    for _ in range(300):
+        s = int(rng.integers(1, 60))
+        q = int(rng.integers(1, s + 1))
+        cuts = sorted(set(rng.integers(0, s + 1, size=int(rng.integers(0, 7))).tolist()))
+        spans = [(cuts[i], cuts[i + 1]) for i in range(0, len(cuts) - 1, 2) if cuts[i] < cuts[i + 1]]
+        segs = O.build_segments(spans, s - q, q)
+        # tiling
+        assert segs[0].q_start == s - q and segs[-1].q_end == s
+        assert all(a.q_end == b.q_start for a, b in zip(segs, segs[1:]))
+        lim = O.row_limits(segs, s, q)
+        for i in range(q):
+            g = s - q + i
+            inside = [b for a, b in spans if a <= g < b]
+            want = inside[0] if inside else g + 1
+            assert lim[i] == want
+        assert np.all(np.diff(lim) >= 0) or spans  # causal-only limits are increasing
+
+
+# --------------------------------------------------------------------------- write / gather
+
+
+def test_write_is_a_bit_exact_scatter_and_leaves_other_slots():
+    rng = np.random.default_rng(3)
+    pool = np.full((64 * 16, 2, 8), np.uint16(0x7FC0), dtype=np.uint16)
+    src = rng.integers(0, 1 << 16, size=(40, 2, 8)).astype(np.uint16)
+    slots = rng.permutation(64 * 16)[:40]
+    O.paged_write(pool, src, slots, O.BF16, O.BF16)
+    assert np.array_equal(pool[slots], src)
+    others = np.setdiff1d(np.arange(64 * 16), slots)
+    assert np.all(pool[others] == 0x7FC0)
+    with pytest.raises(ValueError):
+        O.paged_write(pool, src[:2], [1, 1], O.BF16, O.BF16)
+
+
+def test_gather_matches_index_select_and_keeps_sentinel():
+    """P2 history-staging test: staging equals torch.index_select of the blocks,
+    and rows outside the restaged range keep a -7 sentinel."""
+    rng = np.random.default_rng(4)
+    B = 16
+    pool = rng.standard_normal((50 * B, 3, 8)).astype(np.float32)
+    ids = rng.permutation(50)[:12]
+    stage = np.full((15 * B, 3, 8), -7.0, dtype=np.float32)
+    O.gather(pool, ids, 12, 4, stage, B)
+    ref = torch.index_select(torch.from_numpy(pool).view(50, B, 3, 8), 0, torch.from_numpy(ids[4:12])).reshape(-1, 3, 8)
+    assert np.array_equal(stage[4 * B : 12 * B], ref.numpy())
+    assert np.all(stage[: 4 * B] == -7.0) and np.all(stage[12 * B :] == -7.0)
+
+
+# --------------------------------------------------------------------------- attention
+
+
+def _tiny_case(seed, q_len, s, Hq, Hkv, D):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((q_len, Hq, D))
+    k = rng.standard_normal((s, Hkv, D))
+    v = rng.standard_normal((s, Hkv, D))
+    return q, k, v
+
+
+@pytest.mark.parametrize("spans", [None, [], [(2, 9)], [(0, 5), (7, 12)]])
+def test_attention_matches_scalar_bruteforce(spans):
+    s, q_len = 14, 8
+    q, k, v = _tiny_case(1, q_len, s, 4, 2, 5)
+    segs = O.segments_for_rows([spans], [q_len], [s])[0]
+    lim = O.row_limits(segs, s, q_len)
+    scale = 5 ** -0.5
+    fast = O.dense_attention(q, k, v, lim, scale)
+    slow = O.attention_bruteforce(q, k, v, lim, scale)
+    assert np.max(np.abs(fast - slow)) < 1e-12
+
+
+def test_attention_reduces_to_torch_sdpa_with_explicit_mask():
+    s, q_len, Hq, Hkv, D = 70, 33, 6, 3, 16
+    q, k, v = _tiny_case(2, q_len, s, Hq, Hkv, D)
+    segs = O.segments_for_rows([[(40, 50), (60, 66)]], [q_len], [s])[0]
+    lim = O.row_limits(segs, s, q_len)
+    scale = D ** -0.5
+    ours = O.dense_attention(q, k, v, lim, scale)
+    mask = torch.arange(s)[None, :] < torch.from_numpy(lim)[:, None]
+    tq = torch.from_numpy(q).permute(1, 0, 2)
+    tk = torch.from_numpy(k).repeat_interleave(Hq // Hkv, dim=1).permute(1, 0, 2)
+    tv = torch.from_numpy(v).repeat_interleave(Hq // Hkv, dim=1).permute(1, 0, 2)
+    ref = torch.nn.functional.scaled_dot_product_attention(tq, tk, tv, attn_mask=mask, scale=scale)
+    assert np.max(np.abs(ours - ref.permute(1, 0, 2).numpy())) < 1e-12
+
+
+def test_attention_closed_forms():
+    s, q_len, D = 30, 10, 8
+    _, k, v = _tiny_case(3, q_len, s, 2, 2, D)
+    segs = O.segments_for_rows([[(22, 26)]], [q_len], [s])[0]
+    lim = O.row_limits(segs, s, q_len)
+    # Q = 0: uniform weights -> each row is the mean of the values it may see
+    zero = O.dense_attention(np.zeros((q_len, 2, D)), k, v, lim, 1.0)
+    for i in range(q_len):
+        assert np.allclose(zero[i], v[: lim[i]].mean(axis=0), atol=1e-14)
+    # one visible key -> the output is that value
+    one = O.dense_attention(np.ones((1, 2, D)), k[:1], v[:1], np.array([1]), 0.3)
+    assert np.array_equal(one[0], v[0])
+    # identical keys -> mean of values whatever the query
+    same_k = np.repeat(k[:1], s, axis=0)
+    qq = np.random.default_rng(9).standard_normal((q_len, 2, D))
+    out = O.dense_attention(qq, same_k, v, np.full(q_len, s), 0.7)
+    assert np.allclose(out, v.mean(axis=0)[None], atol=1e-12)
+
+
+def test_causal_row_ignores_later_keys_and_full_row_sees_its_span():
+    s, q_len = 24, 12
+    q, k, v = _tiny_case(5, q_len, s, 2, 2, 4)
+    segs = O.segments_for_rows([[(16, 20)]], [q_len], [s])[0]
+    lim = O.row_limits(segs, s, q_len)
+    base = O.dense_attention(q, k, v, lim, 0.5)
+    k2, v2 = k.copy(), v.copy()
+    k2[21:] += 3.0
+    v2[21:] -= 2.0
+    moved = O.dense_attention(q, k2, v2, lim, 0.5)
+    g = np.arange(s - q_len, s)
+    causal_rows = np.nonzero(lim <= 21)[0]
+    assert np.array_equal(base[causal_rows], moved[causal_rows])
+    # full rows of span [16, 20) see keys < 20 only, so changing key 19 moves them
+    k3 = k.copy()
+    k3[19] += 1.0
+    moved3 = O.dense_attention(q, k3, v, lim, 0.5)
+    full_rows = np.nonzero((g >= 16) & (g < 20))[0]
+    assert np.all(np.abs(moved3[full_rows] - base[full_rows]).max(axis=(1, 2)) > 0)
+
+
+def test_paged_view_equals_dense_over_window_positions():
+    """P2's pattern: paged attention over a permuted pool equals dense attention
+    over the K/V of the positions the window keeps (here with a slid window,
+    ragged chunks and a history ending mid-block)."""
+    geom = small_variant(
+        CONFIGS["frame_bf16"],
+        name="ragged_window",
+        num_q_heads=4,
+        num_kv_heads=2,
+        head_dim=16,
+        history_lens=(7 * 24, 5 * 24),
+        query_lens=(24, 24),
+        sink_tokens=(24, 24),
+        window_tokens=(72, 48),
+        full_spans=(None, None),
+    )
+    wl = make_workload(geom)
+    li = wl.layer(0)
+    meta, kp, vp, out = H.run_layer(wl, li=li)
+    k_all = torch.cat([li.k_hist[: geom.history_lens[0]], li.k_cur[:24]]).float().double().numpy()
+    v_all = torch.cat([li.v_hist[: geom.history_lens[0]], li.v_cur[:24]]).float().double().numpy()
+    pos = meta.positions[0]
+    lim = np.full(24, len(pos))
+    ref = O.dense_attention(li.q[:24].float().double().numpy(), k_all[pos], v_all[pos], lim, H.softmax_scale(16))
+    assert np.max(np.abs(out[:24] - ref)) < 1e-12
+    assert meta.kv_lens[0] < geom.history_lens[0] + 24  # the window actually slid
+
+
+def test_unwritten_slots_never_reach_the_output():
+    """The oracle pool starts as NaN everywhere; a finite output shows only
+    written slots were read (P2's NaN-poisoning test)."""
+    wl = make_workload(CONFIGS["tiny_f32"])
+    _, _, _, out = H.run_layer(wl)
+    assert np.isfinite(out).all()
