@@ -1,0 +1,322 @@
+"""Throughput of the paged-attention hot path on one MI355X.
+
+A step is one pass of the path over one batch: the current chunk's K/V is
+scattered into the pools through the slot mapping (pkv_paged_write), then the
+chunk's queries attend over the visible history through the block table
+(pkv_paged_attn).  The 40-layer workload runs that pair once per layer, each
+layer with its own pools and inputs, all sharing one metadata plan.  Inputs,
+pools and metadata are resident in HBM before timing starts; the history is
+written (untimed) during setup.
+
+Prints one JSON line.  `value` is algorithmic attention TFLOP/s over whole
+steps (4 * D * Hq * visible query-key pairs per call).  `roofline` is for the
+paged_attn call (main MFMA kernel plus the split combine when the key range is
+split), timed with HIP events on the stream the library launches on.  The
+history-staging gather and the contiguous path that reads it are timed too
+and reported under `parts`.
+
+    python bench.py [--steps K] [--warmup W] [--workload frame_bf16]
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged-attn TFLOP/s + KV GB/s (% roofline), 1560-tok chunk over windowed history"
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
+ELT = {"f32": 4, "bf16": 2, "fp8": 1}
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="frame_bf16")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    return ap.parse_args()
+
+
+def _softmax_scale(d):
+    return float(np.float32(d ** -0.5))
+
+
+def setup(geom, device="cuda"):
+    import paged_kv_cache_174_amd as P
+    from workloads import make_workload
+
+    wl = make_workload(geom, device=device)
+    plan = P.ForwardPlan.build(
+        wl.block_ids, geom.history_lens, geom.query_lens, geom.sink_tokens, geom.window_tokens,
+        geom.full_spans, geom.causal_default, geom.block_size, device=device,
+    )
+    plan.validate(geom.pool_blocks())
+    rows = geom.pool_blocks() * geom.block_size
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[geom.pool_dtype]
+    layers = []
+    for layer in range(geom.num_layers):
+        li = wl.layer(layer)
+        kp = torch.zeros((rows, geom.num_kv_heads, geom.head_dim), dtype=dt, device=device)
+        vp = torch.zeros_like(kp)
+        pools = P.Pools(kp, vp, geom.block_size, li.k_scale, li.v_scale, li.k_inv_scale, li.v_inv_scale)
+        if li.k_hist.shape[0]:
+            P.pkv_paged_write(li.k_hist, li.v_hist, plan.history_slot_mapping, pools)
+        li.k_hist = li.v_hist = None  # history now lives in the pools only
+        layers.append((li, pools, torch.empty_like(li.q)))
+    ws_bytes = P.pkv_paged_attn_workspace_size(
+        sum(geom.query_lens), geom.num_q_heads, geom.num_kv_heads, geom.head_dim, geom.num_seqs,
+        plan.max_query_len, plan.max_seq_len,
+    )
+    ws = torch.empty(max(ws_bytes, 16), dtype=torch.uint8, device=device) if ws_bytes else None
+    torch.cuda.synchronize()
+    return wl, plan, layers, ws
+
+
+def attn_bytes(geom, plan):
+    """Algorithmic bytes of one attention call: each visible K and V element once
+    per (sequence, KV head) at storage width, Q once, O once, the table entries read."""
+    kv = sum(plan.kv_lens) * geom.num_kv_heads * geom.head_dim * ELT[geom.pool_dtype] * 2
+    qo = sum(geom.query_lens) * geom.num_q_heads * geom.head_dim * ELT[geom.q_dtype] * 2
+    table = sum(-(-s // geom.block_size) for s in plan.kv_lens) * 4
+    return kv + qo + table
+
+
+def write_bytes(geom):
+    t = sum(geom.query_lens) * geom.num_kv_heads * geom.head_dim
+    return 2 * t * (ELT[geom.q_dtype] + ELT[geom.pool_dtype]) + 8 * sum(geom.query_lens)
+
+
+def run_bench(args, geom):
+    import paged_kv_cache_174_amd as P
+
+    wl, plan, layers, ws = setup(geom)
+    scale = _softmax_scale(geom.head_dim)
+    stream = torch.cuda.current_stream()
+
+    def step(ev=None):
+        for li, pools, out in layers:
+            if ev is not None:
+                ev[0].record(stream)
+            P.pkv_paged_write(li.k_cur, li.v_cur, plan.slot_mapping, pools)
+            if ev is not None:
+                ev[1].record(stream)
+            P.pkv_paged_attn(li.q, pools, plan.block_table, plan.query_start_loc, plan.seq_lens, plan.segments,
+                             plan.segment_start_loc, scale, plan.max_query_len, plan.max_seq_len, out=out,
+                             workspace=ws)
+            if ev is not None:
+                ev[2].record(stream)
+                ev = ev[3:]
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    # whole-step timing (the number `value` is computed from)
+    t0 = torch.cuda.Event(enable_timing=True)
+    t1 = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    t0.record(stream)
+    for _ in range(args.steps):
+        step()
+    t1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    step_ms = t0.elapsed_time(t1) / args.steps
+
+    # per-call timing of the same steps, events between the calls
+    nl = len(layers)
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3 * nl)] for _ in range(args.steps)]
+    for k in range(args.steps):
+        step(evs[k])
+    torch.cuda.synchronize()
+    write_ms = np.mean([e[3 * i].elapsed_time(e[3 * i + 1]) for e in evs for i in range(nl)])
+    attn_ms = np.mean([e[3 * i + 1].elapsed_time(e[3 * i + 2]) for e in evs for i in range(nl)])
+
+    # the history-staging gather over the whole visible window, and the
+    # contiguous path that attends over the staged buffer (identity table)
+    li, pools, out = layers[0]
+    width = plan.block_table_host.shape[1]
+    n_total = width * plan.num_seqs
+    sk = torch.empty((n_total * geom.block_size, geom.num_kv_heads, geom.head_dim), dtype=pools.key.dtype,
+                     device="cuda")
+    sv = torch.empty_like(sk)
+    ids = [torch.from_numpy(t.astype(np.int32)).cuda() for t in plan.tables]
+    staged = P.Pools(sk, sv, geom.block_size, pools.k_scale, pools.v_scale, pools.k_inv_scale, pools.v_inv_scale)
+    ident = torch.arange(n_total, dtype=torch.int32, device="cuda").reshape(plan.num_seqs, width).contiguous()
+    rows_per_seq = width * geom.block_size
+
+    def gather_all():
+        for b in range(plan.num_seqs):
+            r = slice(b * rows_per_seq, (b + 1) * rows_per_seq)
+            P.pkv_gather(pools, ids[b], len(plan.tables[b]), 0, sk[r], sv[r])
+
+    def staged_attn():
+        P.pkv_paged_attn(li.q, staged, ident, plan.query_start_loc, plan.seq_lens, plan.segments,
+                         plan.segment_start_loc, scale, plan.max_query_len, plan.max_seq_len, out=out,
+                         workspace=ws)
+
+    for _ in range(2):
+        gather_all()
+        staged_attn()
+    ge = [torch.cuda.Event(enable_timing=True) for _ in range(3 * args.steps)]
+    for k in range(args.steps):
+        ge[3 * k].record(stream)
+        gather_all()
+        ge[3 * k + 1].record(stream)
+        staged_attn()
+        ge[3 * k + 2].record(stream)
+    torch.cuda.synchronize()
+    gather_ms = np.mean([ge[3 * k].elapsed_time(ge[3 * k + 1]) for k in range(args.steps)])
+    staged_ms = np.mean([ge[3 * k + 1].elapsed_time(ge[3 * k + 2]) for k in range(args.steps)])
+
+    flops = plan.attn_flops(geom.num_q_heads, geom.head_dim)
+    abytes = attn_bytes(geom, plan)
+    gbytes = 2 * 2 * sum(len(t) for t in plan.tables) * geom.block_size * geom.num_kv_heads * geom.head_dim * ELT[geom.pool_dtype]
+    wbytes = write_bytes(geom)
+    achieved = flops / (attn_ms * 1e-3) / 1e12
+    value = flops * nl / (step_ms * 1e-3) / 1e12
+    return {
+        "step_ms": step_ms,
+        "wall_s": wall,
+        "value": value,
+        "flops": flops,
+        "attn_ms": attn_ms,
+        "achieved_tflops": achieved,
+        "attn_bytes": abytes,
+        "kv_gbps": abytes / (attn_ms * 1e-3) / 1e9,
+        "write_ms": write_ms,
+        "write_gbps": wbytes / (write_ms * 1e-3) / 1e9,
+        "gather_ms": gather_ms,
+        "gather_gbps": gbytes / (gather_ms * 1e-3) / 1e9,
+        "staged_attn_ms": staged_ms,
+        "plan": plan,
+        "layers": nl,
+    }
+
+
+def cpu_baseline(geom, budget_s):
+    """The float64 oracle on the host cores, on a bounded sample of the same
+    workload: the oracle's own metadata, pool writes and attention for as many
+    (sequence, query head) pairs of layer 0 as fit the budget."""
+    from oracle import harness as H
+    from workloads import make_workload
+
+    wl = make_workload(geom, device="cpu")
+    li = wl.layer(0)
+    t0 = time.perf_counter()
+    meta = H.metadata(wl)
+    kp, vp = H.empty_pool(geom), H.empty_pool(geom)
+    H.write_history(geom, meta, li, kp, vp, seqs=[0])
+    H.write_current(geom, meta, li, kp, vp, seqs=[0])
+    setup_s = time.perf_counter() - t0
+    q0 = geom.query_lens[0]
+    rows = list(range(q0))
+    done_heads, flops, t_attn = 0, 0.0, 0.0
+    s = meta.kv_lens[0]
+    per_head = 4.0 * geom.head_dim * sum(H.O.row_limits(meta.segments[0], s, q0))
+    while done_heads < geom.num_q_heads and (t_attn + setup_s) < budget_s:
+        t1 = time.perf_counter()
+        H.attention(geom, meta, li, kp, vp, heads=[done_heads], rows=rows)
+        t_attn += time.perf_counter() - t1
+        flops += per_head
+        done_heads += 1
+    total = setup_s + t_attn
+    threads = os.cpu_count()
+    try:
+        from threadpoolctl import threadpool_info
+
+        threads = max(int(i.get("num_threads", 0)) for i in threadpool_info()) or threads
+    except Exception:
+        pass
+    return {
+        "value": flops / total / 1e12,
+        "unit": "TFLOP/s",
+        "cores": threads,
+        "kind": "oracle",
+        "sample": f"sequence 0 of layer 0, {done_heads} of {geom.num_q_heads} query heads, all {q0} query rows "
+                  f"over {s} keys, float64 numpy; includes the oracle's metadata and its pool writes for that "
+                  f"sequence ({total:.1f} s wall)",
+    }
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; run with --gpus 1"}))
+        sys.exit(2)
+    from workloads import CONFIGS
+
+    geom = CONFIGS[args.workload]
+    import paged_kv_cache_174_amd as P
+
+    P.lib()  # fail loudly if the HIP library is missing
+    r = run_bench(args, geom)
+    plan = r.pop("plan")
+    cpu = None if args.no_cpu_baseline else cpu_baseline(geom, args.cpu_budget_s)
+    line = {
+        "metric": METRIC,
+        "value": round(r["value"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["step_ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if geom.pool_dtype == "bf16" else f"bf16 q / {geom.pool_dtype} kv",
+        "data": "synthetic",
+        "config": {
+            "workload": geom.name,
+            "num_seqs": geom.num_seqs,
+            "query_lens": sorted(set(geom.query_lens)),
+            "seq_lens": sorted(set(plan.kv_lens))[:4],
+            "num_q_heads": geom.num_q_heads,
+            "num_kv_heads": geom.num_kv_heads,
+            "head_dim": geom.head_dim,
+            "block_size": geom.block_size,
+            "layers": r["layers"],
+            "pool_dtype": geom.pool_dtype,
+        },
+        "roofline": {
+            "bound": "mfma",
+            "achieved": round(r["achieved_tflops"], 2),
+            "peak": PEAK_BF16_TFLOPS,
+            "unit": "TFLOP/s",
+            "frac": round(r["achieved_tflops"] / PEAK_BF16_TFLOPS, 4),
+            "traffic": None,
+            "kernel": "paged_attn call (attn_mfma_kernel + split combine)",
+            "flop_per_launch": r["flops"],
+            "avg_launch_ms": round(r["attn_ms"], 5),
+        },
+        "kv": {
+            "achieved_gbps": round(r["kv_gbps"], 1),
+            "peak_gbps": PEAK_HBM_GBPS,
+            "frac": round(r["kv_gbps"] / PEAK_HBM_GBPS, 4),
+            "bytes_per_launch": r["attn_bytes"],
+        },
+        "parts": {
+            "paged_write": {"ms": round(r["write_ms"], 5), "gbps": round(r["write_gbps"], 1)},
+            "gather_whole_window": {"ms": round(r["gather_ms"], 5), "gbps": round(r["gather_gbps"], 1)},
+            "attn_over_staged_buffer_ms": round(r["staged_attn_ms"], 5),
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,233 @@
+/*
+ * pkv -- paged K/V cache write, history-staging gather and paged self-attention
+ * for autoregressive video diffusion, on AMD Instinct MI355X (gfx950).
+ *
+ * Source of the semantics: four vllm-omni pages, cited by tag and function:
+ *   P1 "vllm_omni/experimental/ar_diffusion/kv_cache/paged_attention.py"
+ *   P2 "tests/diffusion/ar_diffusion/test_paged_attention.py"
+ *   P3 "vllm_omni/diffusion/attention/backends/utils/piecewise_attn.py"
+ *   P4 "vllm_omni/diffusion/diffusion_kv/paged_attention_adapter.py"
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Pools are per layer, one for K and one for V, each
+ *   [num_blocks * block_size, num_kv_heads, head_dim] row-major: a "slot" is one
+ *   token row of num_kv_heads * head_dim contiguous elements, and block b holds
+ *   slots [b * block_size, (b + 1) * block_size)  (P1 ARDiffusionPagedLayerInputs,
+ *   P1 _paged_write_attn_impl: the flat pool is viewed as [blocks, block, heads, dim]).
+ * - Activations are token-major [tokens, heads, head_dim], contiguous.
+ * - Pointers named "device" must point to device memory of the current HIP
+ *   device; pointers named "host" to host memory.  The caller owns every
+ *   buffer; the library never allocates device memory behind the caller's back
+ *   and never frees anything it was given.
+ * - `stream` is a hipStream_t (NULL = the legacy default stream).  Device
+ *   calls only enqueue work and return; ordering between a write and the
+ *   attention that reads it comes from issuing both on one stream (P1 keeps
+ *   write -> read ordering inside one op for the same reason).
+ * - Return value: PKV_OK, or a negative pkv_status.  Argument errors are
+ *   detected on the host before anything is enqueued; the message is then
+ *   available from pkv_last_error() (thread-local).  Device-side metadata
+ *   (slot mappings, block tables, seq_lens, segments) is trusted in the device
+ *   calls, as FlashAttention trusts its seqused_k; pkv_validate_metadata_host
+ *   checks host copies of it against the pages' rules.
+ */
+#ifndef PKV_H_
+#define PKV_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  PKV_F32 = 0,      /* IEEE binary32 */
+  PKV_BF16 = 1,     /* bfloat16 */
+  PKV_FP8_E4M3 = 2  /* OCP float8 e4m3fn, per-tensor scale (pools only) */
+} pkv_dtype;
+
+typedef enum {
+  PKV_OK = 0,
+  PKV_EINVAL = -1,        /* bad argument (message in pkv_last_error) */
+  PKV_EUNSUPPORTED = -2,  /* valid request this build has no kernel for */
+  PKV_EHIP = -3,          /* a HIP runtime call or kernel launch failed */
+  PKV_ERANGE = -4,        /* an output buffer is too small */
+  PKV_EWINDOW = -5        /* visible window would read past a partly written block */
+} pkv_status;
+
+typedef enum { PKV_SEG_CAUSAL = 0, PKV_SEG_FULL = 1 } pkv_seg_mode;
+
+/* One layer's K and V pools (device memory owned by the caller). */
+typedef struct {
+  void* key;            /* device, [num_blocks * block_size, num_kv_heads, head_dim] */
+  void* value;          /* device, same shape and dtype as key */
+  int64_t num_blocks;
+  int32_t block_size;   /* 16: the kernels page K/V in 16-token blocks (P1 supported_kernel_block_sizes) */
+  int32_t num_kv_heads;
+  int32_t head_dim;     /* 128 for bf16/fp8 pools; 64 or 128 for f32 pools */
+  int32_t dtype;        /* pkv_dtype of the pools */
+  float k_scale;        /* dequantisation multipliers: stored value * scale = real value (1 unless FP8) */
+  float v_scale;
+  float k_inv_scale;    /* quantisation multipliers used by pkv_paged_write for FP8 (1 unless FP8) */
+  float v_inv_scale;
+} pkv_pools;
+
+/* ------------------------------------------------------------------ device calls */
+
+/*
+ * Slot-mapping scatter of the current chunk's K/V into the pools
+ * (P1 _paged_write_attn_impl: each pool indexed by the slot mapping is
+ * assigned the current K/V converted to the pool's dtype).
+ *
+ *   key, value    device, [num_tokens, num_kv_heads, head_dim] of src_dtype
+ *   src_dtype     PKV_F32 into an F32 pool, PKV_BF16 into a BF16 or FP8_E4M3 pool
+ *   slot_mapping  device int64 [num_tokens]; token t goes to slot slot_mapping[t]
+ *
+ * Same dtype: a bit-exact copy.  BF16 -> FP8_E4M3: fp32(x) * k_inv_scale (or
+ * v_inv_scale) rounded once to fp32 (nearest-even), then to e4m3fn by
+ * round-to-nearest-even with saturation to +-448; NaN stays NaN.
+ * Preconditions (not checked on the device): slots unique and in
+ * [0, num_blocks * block_size).  num_tokens == 0 is a no-op.
+ */
+int pkv_paged_write(const void* key, const void* value, int32_t src_dtype, int64_t num_tokens,
+                    const int64_t* slot_mapping, const pkv_pools* pools, void* stream);
+
+/*
+ * History staging gather (P1 _stage_window): the staging buffers, seen as
+ * [n_blocks, block_size, num_kv_heads, head_dim], receive pool block
+ * block_ids[i] at block row i for first_block <= i < n_blocks.  Rows outside
+ * [first_block * block_size, n_blocks * block_size) are not touched.
+ * A bit-exact copy in the pool's dtype.
+ *
+ *   block_ids    device int32 [n_blocks]; entries must be in [0, num_blocks)
+ *   stage_key    device, at least n_blocks * block_size token rows
+ *   stage_value  device, same size
+ * Errors: first_block < 0 or first_block > n_blocks -> PKV_EINVAL.
+ * first_block == n_blocks is a no-op.
+ */
+int pkv_gather(const pkv_pools* pools, const int32_t* block_ids, int32_t n_blocks, int32_t first_block,
+               void* stage_key, void* stage_value, void* stream);
+
+/*
+ * Varlen paged attention with a piecewise full/causal mask.
+ *
+ * Sequence b has query rows q[query_start_loc[b] : query_start_loc[b+1]] and
+ * seq_lens[b] visible keys, read through block_table[b]: key j lives in slot
+ * block_table[b][j / block_size] * block_size + j % block_size
+ * (P1 _reference_paged_attention).  Only the first ceil(seq_lens[b] /
+ * block_size) table entries are read.  The queries are the suffix of the
+ * sequence: query row i sits at key position g = seq_lens[b] - q_len + i
+ * (P3 piecewise_attn; P4 refuses rows that do not end at seq_len).
+ *
+ * Mask (P3 module docstring and build_segments): segments
+ * [segment_start_loc[b], segment_start_loc[b+1]) of `segments`, each
+ * {q_start, q_end, kv_end, mode} in key coordinates, tile
+ * [seq_len - q_len, seq_len) in order.  A row g in a FULL segment sees keys
+ * j < kv_end; in a CAUSAL segment keys j <= g (bottom-right alignment).
+ * The AR default of P1 (causal=False) is one FULL segment with kv_end = seq_len.
+ *
+ * GQA: query head h reads KV head h / (num_q_heads / num_kv_heads) (P4 requires
+ * num_q_heads % num_kv_heads == 0).
+ * out[t, h, :] = sum_j softmax_j(softmax_scale * q.k_j) v_j, accumulated in fp32
+ * and rounded to q_dtype.
+ *
+ *   q                 device [num_q_tokens, num_q_heads, head_dim]; q_dtype PKV_F32 with
+ *                     F32 pools, PKV_BF16 with BF16 or FP8_E4M3 pools
+ *   block_table       device int32 [num_seqs, table_width]
+ *   query_start_loc   device int32 [num_seqs + 1], query_start_loc[num_seqs] == num_q_tokens
+ *   seq_lens          device int32 [num_seqs]
+ *   max_query_len     host bound on every query length (grid sizing)
+ *   max_seq_len       host bound on every seq_lens[b] (a capacity, P1 build_block_table)
+ *   segments          device int32 [num_segments][4]
+ *   segment_start_loc device int32 [num_seqs + 1] (CSR into segments)
+ *   out               device, same shape and dtype as q
+ *   workspace         device scratch for split-key partial results, or NULL;
+ *                     pkv_paged_attn_workspace_size() gives the size that lets the
+ *                     library use every split it would like.  With less (or none)
+ *                     it uses fewer splits; the result is the same up to rounding.
+ * Errors: PKV_EINVAL for inconsistent host arguments (head counts, dtypes,
+ * null pointers, max_query_len > max_seq_len, ...); PKV_EUNSUPPORTED for a
+ * head_dim or dtype pair without a kernel.
+ */
+int pkv_paged_attn(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads,
+                   const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
+                   const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
+                   int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
+                   const int32_t* segment_start_loc, float softmax_scale, void* out, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
+/* Workspace bytes pkv_paged_attn would like for these sizes on the current device. */
+size_t pkv_paged_attn_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t num_seqs, int32_t max_query_len,
+                                     int32_t max_seq_len);
+
+/* ------------------------------------------------------------------ host metadata */
+
+/*
+ * Slot mapping (P1 ensure_video_slots / compute_slot_mapping): for the
+ * num_tokens positions p = first_position + t,
+ * out_slots[t] = block_ids[p / block_size] * block_size + p % block_size.
+ * All arrays host.  Errors: a position whose block index is >= num_block_ids,
+ * or a negative block id -> PKV_EINVAL.
+ */
+int pkv_slot_mapping(const int32_t* block_ids, int64_t num_block_ids, int64_t first_position,
+                     int64_t num_tokens, int32_t block_size, int64_t* out_slots);
+
+/*
+ * Visible-window block table (P1 video_block_table).  block_ids[i] (host) is
+ * the physical block holding positions [i * B, (i + 1) * B) of the sequence,
+ * or a negative value for a block that is no longer resident.  Positions
+ * [0, history_tokens + query_tokens) are written.  The window keeps the sink
+ * [0, sink_tokens) and the most recent window_tokens positions (current chunk
+ * included); every resident block holding a kept position is listed, in
+ * position order, and read whole.  Writes the list to out_table (host,
+ * capacity entries), its length to *out_count and the number of tokens the
+ * kernel reads to *out_kv_len.
+ * Errors: PKV_ERANGE if capacity is too small; PKV_EWINDOW if a partly written
+ * block would be followed by another (P1 raises RuntimeError); PKV_EINVAL for
+ * bad sizes (window_tokens < query_tokens, too few block ids, ...).
+ */
+int pkv_window_table(const int32_t* block_ids, int64_t num_block_ids, int64_t history_tokens,
+                     int64_t query_tokens, int64_t sink_tokens, int64_t window_tokens, int32_t block_size,
+                     int32_t* out_table, int32_t capacity, int32_t* out_count, int32_t* out_kv_len);
+
+/*
+ * Piecewise segments (P3 build_segments): full_spans (host, [num_spans][2],
+ * half-open, key coordinates, sorted and disjoint) are clipped to the query
+ * range [query_offset, query_offset + query_len); rows before a clipped span
+ * that no span claimed become a CAUSAL segment, the clipped span a FULL
+ * segment whose kv_end is the span's unclipped end, and the rest after the
+ * last span a CAUSAL segment.  out_segments (host, [capacity][4]) receives
+ * {q_start, q_end, kv_end, mode}; *out_count their number.
+ * Errors: PKV_EINVAL for unsorted/overlapping/empty spans or query_len <= 0;
+ * PKV_ERANGE if capacity is too small.
+ */
+int pkv_build_segments(const int32_t* full_spans, int32_t num_spans, int32_t query_offset, int32_t query_len,
+                       int32_t* out_segments, int32_t capacity, int32_t* out_count);
+
+/*
+ * Checks host copies of the attention metadata against the rules the pages
+ * enforce (P3 build_paged_piecewise_plan, P4 row and layout checks):
+ * 1 <= q_len <= seq_len <= max_seq_len, q_len <= max_query_len, query_start_loc
+ * starts at 0 and is non-decreasing, ceil(seq_len / block_size) <= table_width,
+ * referenced table entries in [0, num_blocks), segments tile
+ * [seq_len - q_len, seq_len) in order with causal kv_end == q_end and
+ * full kv_end in [q_end, seq_len].  Returns PKV_OK or PKV_EINVAL with a message.
+ */
+int pkv_validate_metadata_host(const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
+                               const int32_t* block_table, int32_t table_width, int64_t num_blocks,
+                               int32_t block_size, int32_t max_query_len, int32_t max_seq_len,
+                               const int32_t* segments, const int32_t* segment_start_loc);
+
+/* Thread-local description of the last error returned on this thread ("" if none). */
+const char* pkv_last_error(void);
+
+/* Library version string. */
+const char* pkv_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKV_H_ */

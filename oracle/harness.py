@@ -81,22 +81,31 @@ def empty_pool(geom) -> np.ndarray:
     return np.full(shape, POISON[geom.pool_dtype], dtype=_NP_BITS[geom.pool_dtype])
 
 
-def write_history(geom, meta: OracleMeta, li, k_pool, v_pool) -> None:
-    src = O.F32 if geom.q_dtype == O.F32 else O.BF16
-    k_bits, v_bits = storage_bits(li.k_hist), storage_bits(li.v_hist)
-    off = 0
-    for b in range(geom.num_seqs):
-        h = geom.history_lens[b]
-        O.paged_write(k_pool, k_bits[off : off + h], meta.hist_slots[b], src, geom.pool_dtype, li.k_inv_scale)
-        O.paged_write(v_pool, v_bits[off : off + h], meta.hist_slots[b], src, geom.pool_dtype, li.v_inv_scale)
-        off += h
+def _seq_list(geom, seqs):
+    return range(geom.num_seqs) if seqs is None else sorted(set(int(b) for b in seqs))
 
 
-def write_current(geom, meta: OracleMeta, li, k_pool, v_pool) -> None:
+def write_history(geom, meta: OracleMeta, li, k_pool, v_pool, seqs=None) -> None:
+    """Writes the history of the given sequences (all by default) into the pools."""
     src = O.F32 if geom.q_dtype == O.F32 else O.BF16
-    slots = np.concatenate(meta.cur_slots)
-    O.paged_write(k_pool, storage_bits(li.k_cur), slots, src, geom.pool_dtype, li.k_inv_scale)
-    O.paged_write(v_pool, storage_bits(li.v_cur), slots, src, geom.pool_dtype, li.v_inv_scale)
+    offs = np.concatenate([[0], np.cumsum(geom.history_lens)])
+    for b in _seq_list(geom, seqs):
+        lo, hi = int(offs[b]), int(offs[b + 1])
+        if hi == lo:
+            continue
+        kb, vb = storage_bits(li.k_hist[lo:hi]), storage_bits(li.v_hist[lo:hi])
+        O.paged_write(k_pool, kb, meta.hist_slots[b], src, geom.pool_dtype, li.k_inv_scale)
+        O.paged_write(v_pool, vb, meta.hist_slots[b], src, geom.pool_dtype, li.v_inv_scale)
+
+
+def write_current(geom, meta: OracleMeta, li, k_pool, v_pool, seqs=None) -> None:
+    src = O.F32 if geom.q_dtype == O.F32 else O.BF16
+    offs = np.concatenate([[0], np.cumsum(geom.query_lens)])
+    for b in _seq_list(geom, seqs):
+        lo, hi = int(offs[b]), int(offs[b + 1])
+        kb, vb = storage_bits(li.k_cur[lo:hi]), storage_bits(li.v_cur[lo:hi])
+        O.paged_write(k_pool, kb, meta.cur_slots[b], src, geom.pool_dtype, li.k_inv_scale)
+        O.paged_write(v_pool, vb, meta.cur_slots[b], src, geom.pool_dtype, li.v_inv_scale)
 
 
 def softmax_scale(head_dim: int) -> float:
@@ -125,14 +134,17 @@ def attention(geom, meta: OracleMeta, li, k_pool, v_pool, heads=None, rows=None)
     )
 
 
-def run_layer(wl, layer: int = 0, heads=None, rows=None, li=None):
+def run_layer(wl, layer: int = 0, heads=None, rows=None, li=None, seqs=None):
     """Full oracle pass for one layer: pools written (history, then the current
-    chunk) and attention over them.  Returns (meta, k_pool, v_pool, out)."""
+    chunk) and attention over them.  Returns (meta, k_pool, v_pool, out).
+
+    ``seqs`` restricts the pool writes to some sequences (sampled checks of
+    large workloads); ``rows`` must then lie in those sequences."""
     geom = wl.geom
     li = wl.layer(layer) if li is None else li
     meta = metadata(wl)
     k_pool, v_pool = empty_pool(geom), empty_pool(geom)
-    write_history(geom, meta, li, k_pool, v_pool)
-    write_current(geom, meta, li, k_pool, v_pool)
+    write_history(geom, meta, li, k_pool, v_pool, seqs)
+    write_current(geom, meta, li, k_pool, v_pool, seqs)
     out = attention(geom, meta, li, k_pool, v_pool, heads=heads, rows=rows)
     return meta, k_pool, v_pool, out

@@ -1,0 +1,393 @@
+// C-ABI front end of libpkv: argument validation, kernel selection and launch,
+// and the host-side metadata helpers (slot mapping, visible-window table,
+// piecewise segments, metadata validation).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <vector>
+
+#include "pkv_internal.hpp"
+
+namespace pkv {
+
+namespace {
+thread_local char g_error[1024] = "";
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr int kMaxDevices = 64;
+int g_cu_count[kMaxDevices] = {0};
+
+int cu_count() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 256;
+  if (g_cu_count[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+    g_cu_count[dev] = n;
+  }
+  return g_cu_count[dev];
+}
+
+int64_t dtype_size(int dt) { return dt == PKV_F32 ? 4 : dt == PKV_BF16 ? 2 : dt == PKV_FP8_E4M3 ? 1 : 0; }
+
+int check_pools(const pkv_pools* p) {
+  if (!p) return fail(PKV_EINVAL, "pools is NULL");
+  if (!p->key || !p->value) return fail(PKV_EINVAL, "pool pointers must not be NULL");
+  if (dtype_size(p->dtype) == 0) return fail(PKV_EINVAL, "unknown pool dtype %d", p->dtype);
+  if (p->block_size != 16) return fail(PKV_EUNSUPPORTED, "block_size %d: the kernels page in 16-token blocks", p->block_size);
+  if (p->num_blocks <= 0 || p->num_kv_heads <= 0 || p->head_dim <= 0)
+    return fail(PKV_EINVAL, "pool sizes must be positive (blocks %lld, kv heads %d, head_dim %d)",
+                static_cast<long long>(p->num_blocks), p->num_kv_heads, p->head_dim);
+  if ((static_cast<int64_t>(p->num_kv_heads) * p->head_dim) % 16 != 0)
+    return fail(PKV_EUNSUPPORTED, "num_kv_heads * head_dim must be a multiple of 16");
+  if (p->dtype == PKV_FP8_E4M3) {
+    if (!(p->k_scale > 0.f) || !(p->v_scale > 0.f) || !std::isfinite(p->k_scale) || !std::isfinite(p->v_scale))
+      return fail(PKV_EINVAL, "fp8 pools need positive finite k_scale and v_scale");
+  }
+  return PKV_OK;
+}
+
+struct SplitPlan {
+  int row_tiles;
+  int splits;
+  int split_len;
+};
+
+// Number of key splits for the MFMA kernel: enough workgroups to fill the
+// device's compute units in whole waves, without cutting the key range into
+// pieces shorter than 512 keys, and never more than the workspace holds.
+SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, int num_seqs, int max_query_len,
+                      int max_seq_len, size_t workspace_bytes, bool have_workspace) {
+  SplitPlan p{};
+  const int group = num_q_heads / num_kv_heads;
+  p.row_tiles = static_cast<int>((static_cast<int64_t>(max_query_len) * group + kMfmaRows - 1) / kMfmaRows);
+  const int64_t base = static_cast<int64_t>(num_seqs) * num_kv_heads * p.row_tiles;
+  const int cus = cu_count();
+  const int max_by_len = std::max(1, max_seq_len / 512);
+  const int64_t per_split_bytes = num_q_tokens * num_q_heads * (128 + 2) * static_cast<int64_t>(sizeof(float));
+  int best = 1;
+  double best_score = -1.0;
+  for (int sp = 1; sp <= std::min(16, max_by_len); ++sp) {
+    if (sp > 1 && have_workspace && static_cast<int64_t>(workspace_bytes) < per_split_bytes * sp) break;
+    if (sp > 1 && !have_workspace) break;
+    const double x = static_cast<double>(base) * sp / cus;
+    const double eff = x / std::ceil(x);
+    const double score = eff * (1.0 - 0.03 * (sp - 1));
+    if (score > best_score + 1e-9) {
+      best_score = score;
+      best = sp;
+    }
+  }
+  p.splits = best;
+  const int per = (max_seq_len + best - 1) / best;
+  p.split_len = ((per + kMfmaKeyTile - 1) / kMfmaKeyTile) * kMfmaKeyTile;
+  if (p.split_len <= 0) p.split_len = kMfmaKeyTile;
+  return p;
+}
+
+}  // namespace
+
+int fail(int code, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  std::vsnprintf(g_error, sizeof(g_error), fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+}  // namespace pkv
+
+using namespace pkv;
+
+extern "C" {
+
+const char* pkv_last_error(void) { return g_error; }
+
+const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
+
+int pkv_paged_write(const void* key, const void* value, int32_t src_dtype, int64_t num_tokens,
+                    const int64_t* slot_mapping, const pkv_pools* pools, void* stream) {
+  g_error[0] = '\0';
+  if (int rc = check_pools(pools)) return rc;
+  if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens must be >= 0");
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !slot_mapping) return fail(PKV_EINVAL, "key, value and slot_mapping must not be NULL");
+  int mode;
+  if (src_dtype == PKV_F32 && pools->dtype == PKV_F32) mode = 0;
+  else if (src_dtype == PKV_BF16 && pools->dtype == PKV_BF16) mode = 1;
+  else if (src_dtype == PKV_BF16 && pools->dtype == PKV_FP8_E4M3) mode = 2;
+  else return fail(PKV_EUNSUPPORTED, "no write from dtype %d into a dtype %d pool", src_dtype, pools->dtype);
+  WriteArgs a{key, value, slot_mapping, pools->key, pools->value, num_tokens,
+              static_cast<int64_t>(pools->num_kv_heads) * pools->head_dim, pools->k_inv_scale, pools->v_inv_scale};
+  if (hipError_t e = launch_write(a, mode, static_cast<hipStream_t>(stream)); e != hipSuccess)
+    return fail(PKV_EHIP, "write launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+int pkv_gather(const pkv_pools* pools, const int32_t* block_ids, int32_t n_blocks, int32_t first_block,
+               void* stage_key, void* stage_value, void* stream) {
+  g_error[0] = '\0';
+  if (int rc = check_pools(pools)) return rc;
+  if (n_blocks < 0 || first_block < 0 || first_block > n_blocks)
+    return fail(PKV_EINVAL, "need 0 <= first_block <= n_blocks (got first_block %d, n_blocks %d)", first_block, n_blocks);
+  if (first_block == n_blocks) return PKV_OK;
+  if (!block_ids || !stage_key || !stage_value) return fail(PKV_EINVAL, "block_ids and staging buffers must not be NULL");
+  GatherArgs a{pools->key, pools->value, block_ids, stage_key, stage_value, first_block, n_blocks,
+               static_cast<int64_t>(pools->block_size) * pools->num_kv_heads * pools->head_dim * dtype_size(pools->dtype)};
+  if (hipError_t e = launch_gather(a, static_cast<hipStream_t>(stream)); e != hipSuccess)
+    return fail(PKV_EHIP, "gather launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+size_t pkv_paged_attn_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
+                                     int32_t head_dim, int32_t num_seqs, int32_t max_query_len,
+                                     int32_t max_seq_len) {
+  if (num_q_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim != 128 ||
+      num_seqs <= 0 || max_query_len <= 0 || max_seq_len <= 0)
+    return 0;
+  SplitPlan p = plan_splits(num_q_tokens, num_q_heads, num_kv_heads, num_seqs, max_query_len, max_seq_len,
+                            static_cast<size_t>(-1), true);
+  if (p.splits <= 1) return 0;
+  return static_cast<size_t>(p.splits) * static_cast<size_t>(num_q_tokens) * num_q_heads * (head_dim + 2) * sizeof(float);
+}
+
+int pkv_paged_attn(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads,
+                   const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
+                   const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
+                   int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
+                   const int32_t* segment_start_loc, float softmax_scale, void* out, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  g_error[0] = '\0';
+  if (int rc = check_pools(pools)) return rc;
+  if (!q || !out || !block_table || !query_start_loc || !seq_lens || !segments || !segment_start_loc)
+    return fail(PKV_EINVAL, "q, out and every metadata pointer must be non-NULL");
+  if (num_seqs <= 0) return fail(PKV_EINVAL, "num_seqs must be positive");
+  if (num_q_tokens <= 0) return fail(PKV_EINVAL, "num_q_tokens must be positive");
+  if (num_q_heads <= 0 || num_q_heads % pools->num_kv_heads)
+    return fail(PKV_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", num_q_heads,
+                pools->num_kv_heads);
+  if (table_width <= 0) return fail(PKV_EINVAL, "table_width must be positive");
+  if (max_query_len <= 0 || max_seq_len <= 0 || max_query_len > max_seq_len)
+    return fail(PKV_EINVAL, "need 0 < max_query_len <= max_seq_len (got %d, %d)", max_query_len, max_seq_len);
+  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(table_width) * pools->block_size)
+    return fail(PKV_EINVAL, "max_seq_len %d exceeds what a %d-entry block table can address", max_seq_len, table_width);
+  if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
+    return fail(PKV_EINVAL, "softmax_scale must be positive and finite");
+  const bool f32 = pools->dtype == PKV_F32;
+  if (f32 ? q_dtype != PKV_F32 : q_dtype != PKV_BF16)
+    return fail(PKV_EINVAL, "query dtype %d does not go with pool dtype %d (f32 with f32, bf16 with bf16 or fp8)",
+                q_dtype, pools->dtype);
+
+  AttnArgs a{};
+  a.q = q;
+  a.out = out;
+  a.kpool = pools->key;
+  a.vpool = pools->value;
+  a.block_table = block_table;
+  a.qsl = query_start_loc;
+  a.seq_lens = seq_lens;
+  a.segments = segments;
+  a.seg_loc = segment_start_loc;
+  a.num_q_tokens = num_q_tokens;
+  a.table_width = table_width;
+  a.num_seqs = num_seqs;
+  a.num_q_heads = num_q_heads;
+  a.num_kv_heads = pools->num_kv_heads;
+  a.group = num_q_heads / pools->num_kv_heads;
+  a.head_dim = pools->head_dim;
+  a.block_size = pools->block_size;
+  const float k_scale = pools->dtype == PKV_FP8_E4M3 ? pools->k_scale : 1.f;
+  a.v_scale = pools->dtype == PKV_FP8_E4M3 ? pools->v_scale : 1.f;
+  a.scale_log2 = softmax_scale * k_scale * kLog2e;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+
+  if (f32) {
+    if (pools->head_dim != 64 && pools->head_dim != 128)
+      return fail(PKV_EUNSUPPORTED, "f32 attention supports head_dim 64 and 128, not %d", pools->head_dim);
+    a.num_splits = 1;
+    a.row_tiles = 0;
+    a.split_len = 0;
+    if (hipError_t e = launch_attn_f32(a, max_query_len, st); e != hipSuccess)
+      return fail(PKV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+    return PKV_OK;
+  }
+  if (pools->head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "bf16/fp8 attention supports head_dim 128, not %d", pools->head_dim);
+  SplitPlan p = plan_splits(num_q_tokens, num_q_heads, pools->num_kv_heads, num_seqs, max_query_len, max_seq_len,
+                            workspace_bytes, workspace != nullptr);
+  a.row_tiles = p.row_tiles;
+  a.num_splits = p.splits;
+  a.split_len = p.split_len;
+  if (p.splits > 1) {
+    const int64_t rows = num_q_tokens * num_q_heads;
+    a.ws_o = static_cast<float*>(workspace);
+    a.ws_ml = a.ws_o + static_cast<int64_t>(p.splits) * rows * 128;
+  }
+  if (hipError_t e = launch_attn_mfma(a, pools->dtype == PKV_FP8_E4M3, st); e != hipSuccess)
+    return fail(PKV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+  if (p.splits > 1) {
+    if (hipError_t e = launch_attn_combine(a, st); e != hipSuccess)
+      return fail(PKV_EHIP, "split combine launch failed: %s", hipGetErrorString(e));
+  }
+  return PKV_OK;
+}
+
+// ------------------------------------------------------------------ host metadata
+
+int pkv_slot_mapping(const int32_t* block_ids, int64_t num_block_ids, int64_t first_position, int64_t num_tokens,
+                     int32_t block_size, int64_t* out_slots) {
+  g_error[0] = '\0';
+  if (block_size <= 0) return fail(PKV_EINVAL, "block_size must be positive");
+  if (num_tokens < 0 || first_position < 0) return fail(PKV_EINVAL, "positions must be non-negative");
+  if (num_tokens == 0) return PKV_OK;
+  if (!block_ids || !out_slots) return fail(PKV_EINVAL, "NULL pointer");
+  for (int64_t t = 0; t < num_tokens; ++t) {
+    const int64_t p = first_position + t;
+    const int64_t bi = p / block_size;
+    if (bi >= num_block_ids) return fail(PKV_EINVAL, "position %lld needs block index %lld of %lld",
+                                         static_cast<long long>(p), static_cast<long long>(bi),
+                                         static_cast<long long>(num_block_ids));
+    const int64_t blk = block_ids[bi];
+    if (blk < 0) return fail(PKV_EINVAL, "position %lld falls in a non-resident block", static_cast<long long>(p));
+    out_slots[t] = blk * block_size + p % block_size;
+  }
+  return PKV_OK;
+}
+
+int pkv_window_table(const int32_t* block_ids, int64_t num_block_ids, int64_t history_tokens, int64_t query_tokens,
+                     int64_t sink_tokens, int64_t window_tokens, int32_t block_size, int32_t* out_table,
+                     int32_t capacity, int32_t* out_count, int32_t* out_kv_len) {
+  g_error[0] = '\0';
+  if (!block_ids || !out_table || !out_count || !out_kv_len) return fail(PKV_EINVAL, "NULL pointer");
+  if (block_size <= 0 || history_tokens < 0 || query_tokens <= 0 || sink_tokens < 0)
+    return fail(PKV_EINVAL, "bad sizes");
+  if (window_tokens < query_tokens)
+    return fail(PKV_EINVAL, "the recent window (%lld) must hold the current chunk (%lld)",
+                static_cast<long long>(window_tokens), static_cast<long long>(query_tokens));
+  const int64_t B = block_size;
+  const int64_t end = history_tokens + query_tokens;
+  const int64_t need_blocks = (end + B - 1) / B;
+  if (num_block_ids < need_blocks)
+    return fail(PKV_EINVAL, "%lld block ids given, %lld needed", static_cast<long long>(num_block_ids),
+                static_cast<long long>(need_blocks));
+  // Index ranges that can hold a kept token (P1 video_block_table): the sink's
+  // blocks, then every block from the one holding the recent window's first
+  // position to the last written one.  A block is read whole, so its length
+  // is min(B, end - first_position).
+  const int64_t sink_end = std::min(sink_tokens, end);
+  const int64_t sink_blocks = (sink_end + B - 1) / B;
+  const int64_t recent_start = std::max<int64_t>(end - window_tokens, 0);
+  const int64_t recent_first = std::max(recent_start / B, sink_blocks);
+  int32_t count = 0;
+  int64_t kv_len = 0;
+  int64_t prev_len = B;
+  auto take = [&](int64_t i) -> int {
+    const int32_t blk = block_ids[i];
+    if (blk < 0) return PKV_OK;  // evicted: nothing of it is read
+    if (prev_len != B)
+      return fail(PKV_EWINDOW, "block %d is partly written but block %d follows it", out_table[count - 1], blk);
+    if (count >= capacity) return fail(PKV_ERANGE, "table capacity %d too small", capacity);
+    const int64_t len = std::min<int64_t>(B, end - i * B);
+    out_table[count++] = blk;
+    kv_len += len;
+    prev_len = len;
+    return PKV_OK;
+  };
+  for (int64_t i = 0; i < sink_blocks; ++i)
+    if (int rc = take(i)) return rc;
+  for (int64_t i = recent_first; i < need_blocks; ++i)
+    if (int rc = take(i)) return rc;
+  if (count == 0) return fail(PKV_EINVAL, "the window holds no resident block");
+  if (kv_len > INT32_MAX) return fail(PKV_ERANGE, "window longer than 2^31 tokens");
+  *out_count = count;
+  *out_kv_len = static_cast<int32_t>(kv_len);
+  return PKV_OK;
+}
+
+int pkv_build_segments(const int32_t* full_spans, int32_t num_spans, int32_t query_offset, int32_t query_len,
+                       int32_t* out_segments, int32_t capacity, int32_t* out_count) {
+  g_error[0] = '\0';
+  if (!out_segments || !out_count || (num_spans > 0 && !full_spans)) return fail(PKV_EINVAL, "NULL pointer");
+  if (query_len <= 0 || query_offset < 0 || num_spans < 0) return fail(PKV_EINVAL, "bad query range or span count");
+  int32_t prev_end = 0;
+  for (int32_t k = 0; k < num_spans; ++k) {
+    const int32_t a = full_spans[2 * k], b = full_spans[2 * k + 1];
+    if (a < prev_end || a < 0 || a >= b)
+      return fail(PKV_EINVAL, "full spans must be sorted, non-empty and non-overlapping (span %d = [%d, %d))", k, a, b);
+    prev_end = b;
+  }
+  const int32_t lo = query_offset, hi = query_offset + query_len;
+  int32_t n = 0;
+  auto emit = [&](int32_t qs, int32_t qe, int32_t kv, int32_t mode) -> int {
+    if (n >= capacity) return fail(PKV_ERANGE, "segment capacity %d too small", capacity);
+    out_segments[4 * n + 0] = qs;
+    out_segments[4 * n + 1] = qe;
+    out_segments[4 * n + 2] = kv;
+    out_segments[4 * n + 3] = mode;
+    ++n;
+    return PKV_OK;
+  };
+  int32_t cursor = lo;
+  for (int32_t k = 0; k < num_spans; ++k) {
+    const int32_t a = std::max(full_spans[2 * k], lo);
+    const int32_t b = std::min(full_spans[2 * k + 1], hi);
+    if (a >= b) continue;  // span misses the query range
+    if (cursor < a)
+      if (int rc = emit(cursor, a, a, PKV_SEG_CAUSAL)) return rc;
+    if (int rc = emit(a, b, full_spans[2 * k + 1], PKV_SEG_FULL)) return rc;
+    cursor = b;
+  }
+  if (cursor < hi)
+    if (int rc = emit(cursor, hi, hi, PKV_SEG_CAUSAL)) return rc;
+  *out_count = n;
+  return PKV_OK;
+}
+
+int pkv_validate_metadata_host(const int32_t* qsl, const int32_t* seq_lens, int32_t num_seqs,
+                               const int32_t* block_table, int32_t table_width, int64_t num_blocks,
+                               int32_t block_size, int32_t max_query_len, int32_t max_seq_len,
+                               const int32_t* segments, const int32_t* seg_loc) {
+  g_error[0] = '\0';
+  if (!qsl || !seq_lens || !block_table || !segments || !seg_loc) return fail(PKV_EINVAL, "NULL pointer");
+  if (num_seqs <= 0 || table_width <= 0 || block_size <= 0) return fail(PKV_EINVAL, "bad sizes");
+  if (qsl[0] != 0) return fail(PKV_EINVAL, "query_start_loc[0] must be 0");
+  if (seg_loc[0] != 0) return fail(PKV_EINVAL, "segment_start_loc[0] must be 0");
+  for (int32_t b = 0; b < num_seqs; ++b) {
+    const int32_t q = qsl[b + 1] - qsl[b];
+    const int32_t s = seq_lens[b];
+    if (q < 1) return fail(PKV_EINVAL, "sequence %d: query length %d must be >= 1", b, q);
+    if (s < q) return fail(PKV_EINVAL, "sequence %d: seq_len %d shorter than its query %d", b, s, q);
+    if (q > max_query_len) return fail(PKV_EINVAL, "sequence %d: query length %d > max_query_len %d", b, q, max_query_len);
+    if (s > max_seq_len) return fail(PKV_EINVAL, "sequence %d: seq_len %d > max_seq_len %d", b, s, max_seq_len);
+    const int64_t nb = (static_cast<int64_t>(s) + block_size - 1) / block_size;
+    if (nb > table_width) return fail(PKV_EINVAL, "sequence %d: %lld blocks do not fit a %d-wide table", b,
+                                      static_cast<long long>(nb), table_width);
+    for (int64_t i = 0; i < nb; ++i) {
+      const int32_t blk = block_table[static_cast<int64_t>(b) * table_width + i];
+      if (blk < 0 || blk >= num_blocks)
+        return fail(PKV_EINVAL, "sequence %d: table entry %lld = %d outside the pool", b, static_cast<long long>(i), blk);
+    }
+    const int32_t s0 = seg_loc[b], s1 = seg_loc[b + 1];
+    if (s1 <= s0) return fail(PKV_EINVAL, "sequence %d has no segments", b);
+    int32_t cursor = s - q;
+    for (int32_t k = s0; k < s1; ++k) {
+      const int32_t qs = segments[4 * k], qe = segments[4 * k + 1], kv = segments[4 * k + 2], mode = segments[4 * k + 3];
+      if (qs != cursor || qe <= qs) return fail(PKV_EINVAL, "sequence %d: segments must tile the query in order", b);
+      if (mode == PKV_SEG_CAUSAL) {
+        if (kv != qe) return fail(PKV_EINVAL, "sequence %d: a causal segment's kv_end must equal its q_end", b);
+      } else if (mode == PKV_SEG_FULL) {
+        if (kv < qe || kv > s) return fail(PKV_EINVAL, "sequence %d: a full segment's kv_end must lie in [q_end, seq_len]", b);
+      } else {
+        return fail(PKV_EINVAL, "sequence %d: unknown segment mode %d", b, mode);
+      }
+      cursor = qe;
+    }
+    if (cursor != s) return fail(PKV_EINVAL, "sequence %d: segments end at %d, not at seq_len %d", b, cursor, s);
+  }
+  return PKV_OK;
+}
+
+}  // extern "C"

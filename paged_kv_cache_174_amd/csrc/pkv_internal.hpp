@@ -1,0 +1,82 @@
+// Internal declarations shared by the C-ABI front end (pkv_api.cpp) and the
+// HIP kernels.  Not installed; the public interface is include/pkv.h.
+#pragma once
+
+#include <hip/hip_runtime.h>
+
+#include <cstddef>
+#include <cstdint>
+
+#include "../../include/pkv.h"
+
+namespace pkv {
+
+// Records a printf-style message as the thread's last error and returns `code`.
+int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+
+// ----------------------------------------------------------------- write / gather
+
+struct WriteArgs {
+  const void* key;
+  const void* value;
+  const int64_t* slots;
+  void* kpool;
+  void* vpool;
+  int64_t num_tokens;
+  int64_t row_elems;  // num_kv_heads * head_dim
+  float k_inv_scale;
+  float v_inv_scale;
+};
+// mode 0: 4-byte copy, 1: 2-byte copy, 2: bf16 -> e4m3 quantise
+hipError_t launch_write(const WriteArgs& a, int mode, hipStream_t s);
+
+struct GatherArgs {
+  const void* kpool;
+  const void* vpool;
+  const int32_t* block_ids;
+  void* kstage;
+  void* vstage;
+  int32_t first_block;
+  int32_t n_blocks;
+  int64_t block_bytes;  // block_size * num_kv_heads * head_dim * element size
+};
+hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
+
+// ----------------------------------------------------------------- attention
+
+struct AttnArgs {
+  const void* q;
+  void* out;
+  const void* kpool;
+  const void* vpool;
+  const int32_t* block_table;
+  const int32_t* qsl;
+  const int32_t* seq_lens;
+  const int32_t* segments;
+  const int32_t* seg_loc;
+  float* ws_o;   // [splits][rows][head_dim] partial numerators (split mode)
+  float* ws_ml;  // [splits][rows][2] partial (max, sum)
+  int64_t num_q_tokens;
+  int32_t table_width;
+  int32_t num_seqs;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t group;      // num_q_heads / num_kv_heads
+  int32_t head_dim;
+  int32_t block_size;
+  int32_t row_tiles;  // query-row tiles per (sequence, KV head)
+  int32_t num_splits;
+  int32_t split_len;  // keys per split, a multiple of the key tile
+  float scale_log2;   // softmax_scale * k_scale * log2(e)
+  float v_scale;
+};
+
+// Rows (query token x query head of one KV group) one MFMA workgroup covers.
+constexpr int kMfmaRows = 256;
+constexpr int kMfmaKeyTile = 64;
+
+hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipStream_t s);
+hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s);
+hipError_t launch_attn_f32(const AttnArgs& a, int max_query_len, hipStream_t s);
+
+}  // namespace pkv

@@ -1,0 +1,142 @@
+"""Per-forward host metadata, built once and shared by every layer.
+
+For each sequence this asks the C library for the visible-window block table
+(sink + recent window, whole blocks), the slot mappings of the history and of
+the current chunk, and the piecewise segments; it then pads the table to one
+width and uploads everything once (P1 ``ARDiffusionPagedForwardContext.prepare``
+builds the same metadata once per KV branch for all layers).  Python only
+moves arrays between the C calls and the device.
+"""
+
+from __future__ import annotations
+
+from dataclasses import dataclass
+
+import numpy as np
+import torch
+
+from . import _lib as L
+
+
+@dataclass
+class ForwardPlan:
+    num_seqs: int
+    block_size: int
+    query_lens: list[int]
+    history_lens: list[int]
+    kv_lens: list[int]
+    tables: list[np.ndarray]
+    segments_host: np.ndarray  # [num_segments, 4]
+    segment_start_host: np.ndarray  # [num_seqs + 1]
+    block_table_host: np.ndarray  # [num_seqs, width]
+    query_start_host: np.ndarray  # [num_seqs + 1]
+    cur_slots_host: np.ndarray  # [sum q] int64
+    hist_slots_host: np.ndarray  # [sum h] int64
+    max_query_len: int
+    max_seq_len: int
+    # device copies
+    block_table: torch.Tensor | None = None
+    query_start_loc: torch.Tensor | None = None
+    seq_lens: torch.Tensor | None = None
+    segments: torch.Tensor | None = None
+    segment_start_loc: torch.Tensor | None = None
+    slot_mapping: torch.Tensor | None = None
+    history_slot_mapping: torch.Tensor | None = None
+
+    @classmethod
+    def build(
+        cls,
+        block_ids,
+        history_lens,
+        query_lens,
+        sink_tokens,
+        window_tokens,
+        full_spans,
+        causal_default: bool = False,
+        block_size: int = 16,
+        table_width: int | None = None,
+        max_seq_len: int | None = None,
+        device=None,
+    ) -> "ForwardPlan":
+        n = len(query_lens)
+        tables, kv_lens, segs, seg_start = [], [], [], [0]
+        cur_slots, hist_slots = [], []
+        for b in range(n):
+            h, q = int(history_lens[b]), int(query_lens[b])
+            table, kv_len = L.pkv_window_table(block_ids[b], h, q, sink_tokens[b], window_tokens[b], block_size)
+            tables.append(table)
+            kv_lens.append(kv_len)
+            hist_slots.append(L.pkv_slot_mapping(block_ids[b], 0, h, block_size))
+            cur_slots.append(L.pkv_slot_mapping(block_ids[b], h, q, block_size))
+            spans = full_spans[b]
+            if spans is None:
+                spans = [] if causal_default else [(kv_len - q, kv_len)]
+            sg = L.pkv_build_segments(list(spans), kv_len - q, q)
+            segs.append(sg)
+            seg_start.append(seg_start[-1] + len(sg))
+        width = max(len(t) for t in tables) if table_width is None else int(table_width)
+        bt = np.zeros((n, width), dtype=np.int32)  # tail padding with block 0, never read
+        for b, t in enumerate(tables):
+            if len(t) > width:
+                raise ValueError(f"sequence {b} needs {len(t)} table entries, width is {width}")
+            bt[b, : len(t)] = t
+        qsl = np.concatenate([[0], np.cumsum(query_lens)]).astype(np.int32)
+        plan = cls(
+            num_seqs=n,
+            block_size=block_size,
+            query_lens=[int(q) for q in query_lens],
+            history_lens=[int(h) for h in history_lens],
+            kv_lens=kv_lens,
+            tables=tables,
+            segments_host=np.concatenate(segs).astype(np.int32),
+            segment_start_host=np.asarray(seg_start, dtype=np.int32),
+            block_table_host=bt,
+            query_start_host=qsl,
+            cur_slots_host=np.concatenate(cur_slots).astype(np.int64),
+            hist_slots_host=np.concatenate(hist_slots).astype(np.int64) if hist_slots else np.zeros(0, np.int64),
+            max_query_len=int(max(query_lens)),
+            max_seq_len=int(max(kv_lens) if max_seq_len is None else max_seq_len),
+        )
+        if device is not None:
+            plan.to(device)
+        return plan
+
+    def to(self, device) -> "ForwardPlan":
+        def up(a):
+            return torch.from_numpy(np.ascontiguousarray(a)).to(device)
+
+        self.block_table = up(self.block_table_host)
+        self.query_start_loc = up(self.query_start_host)
+        self.seq_lens = up(np.asarray(self.kv_lens, dtype=np.int32))
+        self.segments = up(self.segments_host.reshape(-1))
+        self.segment_start_loc = up(self.segment_start_host)
+        self.slot_mapping = up(self.cur_slots_host)
+        self.history_slot_mapping = up(self.hist_slots_host)
+        return self
+
+    def validate(self, num_blocks: int) -> None:
+        L.pkv_validate_metadata_host(
+            self.query_start_host,
+            np.asarray(self.kv_lens, dtype=np.int32),
+            self.block_table_host,
+            num_blocks,
+            self.block_size,
+            self.max_query_len,
+            self.max_seq_len,
+            self.segments_host,
+            self.segment_start_host,
+        )
+
+    def attn_flops(self, num_q_heads: int, head_dim: int) -> float:
+        """Algorithmic FLOPs of one attention call: 4 * D * Hq * (visible
+        query-key pairs), counting each multiply-add of QK^T and PV as 2."""
+        pairs = 0
+        for b in range(self.num_seqs):
+            s, q = self.kv_lens[b], self.query_lens[b]
+            lo, hi = self.segment_start_host[b], self.segment_start_host[b + 1]
+            for qs, qe, kv, mode in self.segments_host[lo:hi]:
+                if mode == L.PKV_SEG_FULL:
+                    pairs += int(qe - qs) * int(kv)
+                else:  # rows g in [qs, qe) see g + 1 keys
+                    pairs += int((qs + 1 + qe) * (qe - qs) // 2)
+        return 4.0 * head_dim * num_q_heads * pairs

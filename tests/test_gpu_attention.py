@@ -1,0 +1,169 @@
+"""Paged attention on the GPU against the float64 oracle.
+
+Tolerances (max |O_gpu - O_oracle|): 1e-4 for fp32, 2e-2 for bf16, 6e-2 for
+fp8 K/V pools.  Small variants span several row and key tiles with ragged
+tails; the configurations at full size are checked in full where the oracle
+takes seconds and on sampled rows otherwise."""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import harness as H
+from workloads import CONFIGS, make_workload, small_variant
+
+from . import gpu_harness as G
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 2e-2, "fp8": 6e-2}
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _lib():
+    G.ensure_built()
+
+
+def _check(geom, out, ref, rows=None, heads=None):
+    got = G.as_f64(out)
+    if rows is not None:
+        got = got[np.asarray(rows)]
+    if heads is not None:
+        got = got[:, np.asarray(heads)]
+    assert np.isfinite(got).all(), "non-finite output (an unwritten slot was read?)"
+    err = np.max(np.abs(got - ref))
+    assert err <= TOL[geom.pool_dtype], f"{geom.name}: max abs error {err:.3e} > {TOL[geom.pool_dtype]}"
+    return err
+
+
+SMALL = [
+    CONFIGS["tiny_f32"],
+    small_variant(CONFIGS["tiny_f32"], name="f32_d128_ragged", head_dim=128, num_q_heads=6, num_kv_heads=2,
+                  history_lens=(70, 5), query_lens=(33, 90), sink_tokens=(0, 0), window_tokens=(1 << 30,) * 2,
+                  full_spans=(((70, 90),), None)),
+    small_variant(CONFIGS["frame_bf16"], name="frame_small_bf16", num_q_heads=3, num_kv_heads=3,
+                  history_lens=(600, 600), query_lens=(300, 300), sink_tokens=(300, 300),
+                  window_tokens=(900, 900)),
+    small_variant(CONFIGS["frame_bf16"], name="slid_window_bf16", num_q_heads=2, num_kv_heads=2,
+                  history_lens=(24 * 9, 24 * 5), query_lens=(24, 24), sink_tokens=(24, 48),
+                  window_tokens=(72, 48)),
+    small_variant(CONFIGS["piecewise_gqa_bf16"], name="piecewise_small_bf16", num_q_heads=10, num_kv_heads=2,
+                  history_lens=(100,), query_lens=(300,), full_spans=(((100, 180), (250, 400)),)),
+    small_variant(CONFIGS["piecewise_gqa_bf16"], name="piecewise_causal_only_bf16", num_q_heads=4, num_kv_heads=4,
+                  history_lens=(0,), query_lens=(333,), full_spans=((),)),
+    small_variant(CONFIGS["varlen_fp8"], name="varlen_small_fp8", num_q_heads=8, num_kv_heads=2,
+                  history_lens=(100, 40, 777, 0, 5), query_lens=(16, 100, 16, 50, 1), sink_tokens=(0,) * 5,
+                  window_tokens=(1 << 30,) * 5, full_spans=(None,) * 5),
+    small_variant(CONFIGS["varlen_fp8"], name="varlen_small_bf16", pool_dtype="bf16", num_q_heads=4,
+                  num_kv_heads=1, history_lens=(1000, 3), query_lens=(64, 1), sink_tokens=(0,) * 2,
+                  window_tokens=(1 << 30,) * 2, full_spans=(None,) * 2),
+    small_variant(CONFIGS["frame_bf16"], name="single_key_bf16", num_q_heads=2, num_kv_heads=1,
+                  history_lens=(0,), query_lens=(1,), sink_tokens=(0,), window_tokens=(1 << 30,),
+                  full_spans=(None,)),
+    small_variant(CONFIGS["frame_bf16"], name="block_aligned_bf16", num_q_heads=2, num_kv_heads=2,
+                  history_lens=(128,), query_lens=(64,), sink_tokens=(0,), window_tokens=(1 << 30,),
+                  full_spans=(None,)),
+]
+
+
+@pytest.mark.parametrize("geom", SMALL, ids=[g.name for g in SMALL])
+@pytest.mark.parametrize("workspace", ["auto", None], ids=["split", "nosplit"])
+def test_small_configs_match_oracle(geom, workspace):
+    wl = make_workload(geom, device="cuda")
+    li = wl.layer(0)
+    G.say("attn", geom.name, workspace)
+    _, _, _, out = G.run(wl, li=li, workspace=workspace)
+    _, _, _, ref = H.run_layer(wl, li=li)
+    _check(geom, out, ref)
+
+
+def test_frame_bf16_full_size_matches_oracle():
+    """The 1560-token frame over 1 sink + 2 window chunks, every output."""
+    geom = CONFIGS["frame_bf16"]
+    wl = make_workload(geom, device="cuda")
+    li = wl.layer(0)
+    G.say("attn full", geom.name)
+    plan, _, _, out = G.run(wl, li=li)
+    assert plan.kv_lens == [6240, 6240]
+    _, _, _, ref = H.run_layer(wl, li=li)
+    _check(geom, out, ref)
+
+
+def _sample_rows(geom, rng, per_seq=24, seqs=None):
+    qsl = np.concatenate([[0], np.cumsum(geom.query_lens)])
+    rows = []
+    for b in range(geom.num_seqs) if seqs is None else seqs:
+        lo, hi = int(qsl[b]), int(qsl[b + 1])
+        picks = {lo, hi - 1, min(lo + 255, hi - 1), min(lo + 256, hi - 1)}
+        picks |= set(rng.integers(lo, hi, size=per_seq).tolist())
+        rows.extend(sorted(picks))
+    return rows
+
+
+def test_piecewise_gqa_full_size_sampled_rows():
+    geom = CONFIGS["piecewise_gqa_bf16"]
+    wl = make_workload(geom, device="cuda")
+    li = wl.layer(0)
+    G.say("attn full", geom.name)
+    _, _, _, out = G.run(wl, li=li)
+    # rows at and around every segment boundary plus random ones
+    edges = [0, 1, 1559, 1560, 1561, 3119, 3120, 3121, 4679]
+    rows = sorted(set(edges) | set(np.random.default_rng(0).integers(0, 4680, 40).tolist()))
+    _, _, _, ref = H.run_layer(wl, li=li, rows=rows)
+    _check(geom, out, ref, rows=rows)
+
+
+def test_varlen_fp8_full_size_sampled_rows():
+    geom = CONFIGS["varlen_fp8"]
+    wl = make_workload(geom, device="cuda")
+    li = wl.layer(0)
+    G.say("attn full", geom.name)
+    _, _, _, out = G.run(wl, li=li)
+    q = np.asarray(geom.query_lens)
+    s = np.asarray(geom.history_lens) + q
+    long_q = int(np.argmax(np.where(q == 1560, s, -1)))
+    short_q = int(np.argmax(np.where(q == 16, s, -1)))
+    seqs = sorted({long_q, short_q, int(np.argmin(s))})
+    rows = _sample_rows(geom, np.random.default_rng(1), per_seq=12, seqs=seqs)
+    heads = [0, 3, 4, 31]
+    _, _, _, ref = H.run_layer(wl, li=li, rows=rows, heads=heads, seqs=seqs)
+    _check(geom, out, ref, rows=rows, heads=heads)
+
+
+def test_ar_step_layers_sampled():
+    """The 40-layer step's shape (2 x 40 heads, 9360 visible keys): write + attend
+    on a few layers, each with its own pools, shared metadata."""
+    geom = CONFIGS["ar_step_40L_bf16"]
+    wl = make_workload(geom, device="cuda")
+    plan = G.make_plan(wl)
+    assert plan.kv_lens == [9360, 9360]
+    for layer in (0, 39):
+        li = wl.layer(layer)
+        G.say("attn layer", layer)
+        pools = G.make_pools(geom, li)
+        G.write_layer(plan, pools, li)
+        out = G.attend(plan, pools, li, geom)
+        torch.cuda.synchronize()
+        rows = _sample_rows(geom, np.random.default_rng(layer), per_seq=6)
+        heads = [0, 17, 39]
+        _, _, _, ref = H.run_layer(wl, li=li, rows=rows, heads=heads)
+        _check(geom, out, ref, rows=rows, heads=heads)
+        del pools, out
+
+
+def test_bad_arguments_raise_before_launch():
+    geom = SMALL[2]
+    wl = make_workload(geom, device="cuda")
+    li = wl.layer(0)
+    plan = G.make_plan(wl)
+    pools = G.make_pools(geom, li)
+    with pytest.raises(ValueError):  # q dtype does not go with a bf16 pool
+        G.P.pkv_paged_attn(li.q.float(), pools, plan.block_table, plan.query_start_loc, plan.seq_lens,
+                           plan.segments, plan.segment_start_loc, 0.1, plan.max_query_len, plan.max_seq_len)
+    with pytest.raises(ValueError):  # max_query_len > max_seq_len
+        G.P.pkv_paged_attn(li.q, pools, plan.block_table, plan.query_start_loc, plan.seq_lens,
+                           plan.segments, plan.segment_start_loc, 0.1, 10_000, plan.max_seq_len)
+    with pytest.raises(ValueError):  # heads not a multiple of KV heads
+        G.P.pkv_paged_attn(li.q[:, :2].contiguous(), pools, plan.block_table, plan.query_start_loc,
+                           plan.seq_lens, plan.segments, plan.segment_start_loc, 0.1, plan.max_query_len,
+                           plan.max_seq_len)
