@@ -44,14 +44,16 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
 constexpr int D = 128;
 constexpr int KT = kMfmaKeyTile;  // keys per tile
-constexpr int NW = 4;             // waves per workgroup
+constexpr int NW = 8;             // waves per workgroup (two per SIMD)
 constexpr int NT = 64 * NW;
 constexpr int KS = D + 8;    // K tile row stride in LDS (bf16): 272 B, breaks bank aliasing
 constexpr int VS = KT + 8;   // V^T tile row stride in LDS (bf16): 144 B
 constexpr int K_ELEMS = KT * KS;
 constexpr int V_ELEMS = D * VS;
 constexpr int BUF = K_ELEMS + V_ELEMS;
-static_assert(kMfmaRows == NW * 64, "rows per workgroup");
+constexpr int kWaveRows = 32;     // query rows per wave: one 32-wide MFMA column block
+static_assert(kMfmaRows == NW * kWaveRows, "rows per workgroup");
+constexpr float kRescaleLog2 = 8.0f;  // stale-max slack before O and l are rescaled
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -97,17 +99,11 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
 }
 
 template <bool FP8>
-struct KvRegs {
-  using T = typename std::conditional<FP8, u32x2, u32x4>::type;  // 8 head-dim elements
-  T k[4];
-  T v[4];
-};
-
-template <bool FP8>
-__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2))) void
 attn_mfma_kernel(AttnArgs a) {
   __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
   constexpr int ELSZ = FP8 ? 1 : 2;
+  using Chunk = typename std::conditional<FP8, u32x2, u32x4>::type;  // 8 head-dim elements
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -143,198 +139,168 @@ attn_mfma_kernel(AttnArgs a) {
   const int k_end = min(k_begin + a.split_len, wg_kmax);
   if (k_begin >= k_end) return;
 
-  const int wr0 = r0 + 64 * w;
+  const int wr0 = r0 + kWaveRows * w;
   int wave_kmin = 0, wave_kmax = 0;
   if (wr0 < R) {
     wave_kmin = row_limit(a.segments, seg0, seg1, gbase + wr0 / G);
-    wave_kmax = row_limit(a.segments, seg0, seg1, gbase + (min(wr0 + 64, R) - 1) / G);
+    wave_kmax = row_limit(a.segments, seg0, seg1, gbase + (min(wr0 + kWaveRows, R) - 1) / G);
   }
 
-  // ---- this lane's two query rows (one per 32-wide column block)
-  int Lc[2], tok[2], head[2];
-  bool valid[2];
-#pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const int r = wr0 + 32 * c + l32;
-    valid[c] = r < R;
-    tok[c] = valid[c] ? r / G : 0;
-    head[c] = hk * G + (valid[c] ? r % G : 0);
-    Lc[c] = valid[c] ? row_limit(a.segments, seg0, seg1, gbase + tok[c]) : 0;
-  }
+  // ---- this lane's query row
+  const int row = wr0 + l32;
+  const bool valid = row < R;
+  const int tok = valid ? row / G : 0;
+  const int head = hk * G + (valid ? row % G : 0);
+  const int Lrow = valid ? row_limit(a.segments, seg0, seg1, gbase + tok) : 0;
 
   // Q^T fragments for S^T = K Q^T: lane holds 8 consecutive head-dim values
   // [16 t + 8 h2, +8) of its query row for each of the 8 k-steps.
-  bf16x8 qf[2][8];
+  bf16x8 qf[8];
   {
-    const __bf16* qb = static_cast<const __bf16*>(a.q);
+    const __bf16* qr = static_cast<const __bf16*>(a.q) +
+                       (static_cast<int64_t>(t0 + tok) * a.num_q_heads + head) * D + 8 * h2;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      const __bf16* qr = qb + (static_cast<int64_t>(t0 + tok[c]) * a.num_q_heads + head[c]) * D + 8 * h2;
-#pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        u32x4 v = {0u, 0u, 0u, 0u};
-        if (valid[c]) v = *reinterpret_cast<const u32x4*>(qr + 16 * t);
-        qf[c][t] = __builtin_bit_cast(bf16x8, v);
-      }
+    for (int t = 0; t < 8; ++t) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (valid) v = *reinterpret_cast<const u32x4*>(qr + 16 * t);
+      qf[t] = __builtin_bit_cast(bf16x8, v);
     }
   }
 
-  // ---- K/V staging geometry
+  // ---- K/V staging: waves 0-3 stage K, waves 4-7 stage V, 4 chunks per lane.
+  const bool stage_k = w < 4;
+  const int sw = w & 3;
   const int64_t row_elems = static_cast<int64_t>(a.num_kv_heads) * D;
-  const uint8_t* kbase = static_cast<const uint8_t*>(a.kpool) + static_cast<int64_t>(hk) * D * ELSZ;
-  const uint8_t* vbase = static_cast<const uint8_t*>(a.vpool) + static_cast<int64_t>(hk) * D * ELSZ;
+  const uint8_t* src = static_cast<const uint8_t*>(stage_k ? a.kpool : a.vpool) + static_cast<int64_t>(hk) * D * ELSZ;
   const int32_t* table = a.block_table + static_cast<int64_t>(b) * a.table_width;
   const int nblk = (s + 15) >> 4;
-  // K: wave w stages keys [16 w, 16 w + 16) of the tile -- exactly tile block w;
-  // lanes 16 apart take consecutive keys, lanes within 16 the 16 head-dim chunks.
-  const int k_sub = lane >> 4;  // key = 16 w + 4 it + k_sub
-  const int k_chunk = lane & 15;
-  // V: lane takes 4 consecutive keys 4 vkq + it of one head-dim chunk, so it can
-  // write them transposed as one 8-byte run per head-dim element.
+  // K: wave sw stages keys [16 sw, 16 sw + 16) -- exactly tile block sw; lanes
+  // 16 apart take consecutive keys, lanes within 16 the 16 head-dim chunks.
+  // V: lane takes 4 consecutive keys 4 vkq + it of head-dim chunk v_chunk and
+  // writes them transposed as one 8-byte run per head-dim element.
   const int vkq = lane & 15;
-  const int v_chunk = 4 * w + (lane >> 4);
+  const int key_of_it0 = stage_k ? 16 * sw + (lane >> 4) : 4 * vkq;  // key of chunk 0
+  const int key_step = stage_k ? 4 : 1;
+  const int chunk = stage_k ? (lane & 15) : 4 * sw + (lane >> 4);
   const int v_pos = 16 * (vkq >> 2) + 8 * (vkq & 1) + 4 * ((vkq >> 1) & 1);
 
-  KvRegs<FP8> pre;
+  Chunk pre[4];
   auto load_tile = [&](int kt) {
-    const int blk0 = kt >> 4;
-    int e[4];
-#pragma unroll
-    for (int x = 0; x < 4; ++x) e[x] = (blk0 + x < nblk) ? table[blk0 + x] : 0;
+    const int blk = (kt >> 4) + (stage_k ? sw : (vkq >> 2));  // one table entry per lane
+    const int e = (blk < nblk) ? table[blk] : 0;
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int kk = 16 * w + 4 * it + k_sub;
-      const int64_t slot = static_cast<int64_t>(e[w]) * 16 + (kk & 15);
-      const uint8_t* p = kbase + (slot * row_elems + 8 * k_chunk) * ELSZ;
-      if constexpr (FP8) {
-        pre.k[it] = (kt + kk < s) ? *reinterpret_cast<const u32x2*>(p) : u32x2{0u, 0u};
-      } else {
-        pre.k[it] = (kt + kk < s) ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-    const int ev = e[vkq >> 2];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int vk = 4 * vkq + it;
-      const int64_t slot = static_cast<int64_t>(ev) * 16 + (vk & 15);
-      const uint8_t* p = vbase + (slot * row_elems + 8 * v_chunk) * ELSZ;
-      if constexpr (FP8) {
-        pre.v[it] = (kt + vk < s) ? *reinterpret_cast<const u32x2*>(p) : u32x2{0u, 0u};
-      } else {
-        pre.v[it] = (kt + vk < s) ? *reinterpret_cast<const u32x4*>(p) : u32x4{0u, 0u, 0u, 0u};
-      }
+      const int kk = key_of_it0 + key_step * it;
+      const int64_t slot = static_cast<int64_t>(e) * 16 + (kk & 15);
+      const uint8_t* p = src + (slot * row_elems + 8 * chunk) * ELSZ;
+      Chunk zero = {};
+      pre[it] = (kt + kk < s) ? *reinterpret_cast<const Chunk*>(p) : zero;
     }
   };
 
   auto store_tile = [&](int buf) {
     __bf16* Kl = lds + buf * BUF;
     __bf16* Vl = Kl + K_ELEMS;
+    u32x4 v[4];
 #pragma unroll
     for (int it = 0; it < 4; ++it) {
-      const int kk = 16 * w + 4 * it + k_sub;
-      u32x4 v;
-      if constexpr (FP8) v = e4m3x8_to_bf16x8(pre.k[it]); else v = pre.k[it];
-      *reinterpret_cast<u32x4*>(Kl + kk * KS + 8 * k_chunk) = v;
+      if constexpr (FP8) v[it] = e4m3x8_to_bf16x8(pre[it]); else v[it] = pre[it];
     }
-    u32x4 vv[4];
+    if (stage_k) {
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      if constexpr (FP8) vv[it] = e4m3x8_to_bf16x8(pre.v[it]); else vv[it] = pre.v[it];
-    }
+      for (int it = 0; it < 4; ++it)
+        *reinterpret_cast<u32x4*>(Kl + (key_of_it0 + 4 * it) * KS + 8 * chunk) = v[it];
+    } else {
 #pragma unroll
-    for (int dd = 0; dd < 8; ++dd) {
-      const int wd = dd >> 1;
-      u32x2 x;
-      if (dd & 1) {
-        x[0] = (vv[0][wd] >> 16) | (vv[1][wd] & 0xFFFF0000u);
-        x[1] = (vv[2][wd] >> 16) | (vv[3][wd] & 0xFFFF0000u);
-      } else {
-        x[0] = (vv[0][wd] & 0xFFFFu) | (vv[1][wd] << 16);
-        x[1] = (vv[2][wd] & 0xFFFFu) | (vv[3][wd] << 16);
+      for (int dd = 0; dd < 8; ++dd) {
+        const int wd = dd >> 1;
+        u32x2 x;
+        if (dd & 1) {
+          x[0] = (v[0][wd] >> 16) | (v[1][wd] & 0xFFFF0000u);
+          x[1] = (v[2][wd] >> 16) | (v[3][wd] & 0xFFFF0000u);
+        } else {
+          x[0] = (v[0][wd] & 0xFFFFu) | (v[1][wd] << 16);
+          x[1] = (v[2][wd] & 0xFFFFu) | (v[3][wd] << 16);
+        }
+        *reinterpret_cast<u32x2*>(Vl + (8 * chunk + dd) * VS + v_pos) = x;
       }
-      *reinterpret_cast<u32x2*>(Vl + (8 * v_chunk + dd) * VS + v_pos) = x;
     }
   };
 
   const float sl = a.scale_log2;
-  float m[2] = {-INFINITY, -INFINITY};
-  float l[2] = {0.f, 0.f};
-  f32x16 o[2][4];
+  float m = -INFINITY;
+  float l = 0.f;
+  f32x16 o[4];
 #pragma unroll
-  for (int c = 0; c < 2; ++c)
+  for (int db = 0; db < 4; ++db)
 #pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int r = 0; r < 16; ++r) o[c][db][r] = 0.f;
+    for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
   auto compute = [&](int buf, int kt) {
     const __bf16* Kl = lds + buf * BUF;
     const __bf16* Vl = Kl + K_ELEMS;
-    f32x16 sacc[2][2];
+    f32x16 sacc[2];
 #pragma unroll
-    for (int c = 0; c < 2; ++c)
+    for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sacc[c][kb][r] = 0.f;
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
         const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kl + (32 * kb + l32) * KS + 16 * t + 8 * h2);
-        sacc[0][kb] = mfma(ka, qf[0][t], sacc[0][kb]);
-        sacc[1][kb] = mfma(ka, qf[1][t], sacc[1][kb]);
+        sacc[kb] = mfma(ka, qf[t], sacc[kb]);
       }
     }
-    const bool need_mask = kt + KT > wave_kmin;
-    bf16x8 pb[2][2][2];
-#pragma unroll
-    for (int c = 0; c < 2; ++c) {
-      if (need_mask) {
-#pragma unroll
-        for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int j = kt + 32 * kb + 8 * (r >> 2) + 4 * h2 + (r & 3);
-            if (j >= Lc[c]) sacc[c][kb][r] = -INFINITY;
-          }
-      }
-      float mx = -INFINITY;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[c][kb][r]);
-      mx = max_halves(mx);
-      const float m_new = fmaxf(m[c], mx);
-      const float m_use = (m_new == -INFINITY) ? 0.f : m_new;
-      const float alpha = __builtin_amdgcn_exp2f((m[c] - m_use) * sl);
-      const float mc = m_use * sl;
-      float ls = 0.f;
+    if (kt + KT > wave_kmin) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const float p = __builtin_amdgcn_exp2f(fmaf(sacc[c][kb][r], sl, -mc));
-          sacc[c][kb][r] = p;
-          ls += p;
+          const int j = kt + 32 * kb + 8 * (r >> 2) + 4 * h2 + (r & 3);
+          if (j >= Lrow) sacc[kb][r] = -INFINITY;
         }
-      l[c] = l[c] * alpha + ls;
-      m[c] = m_new;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
+    mx = max_halves(mx);
+    // Lazy rescaling: the running max only moves (and O, l are rescaled) when
+    // some row's tile max exceeds it by more than 2^kRescaleLog2 in the exp2
+    // domain.  Softmax is exact for any common offset, so a stale max only
+    // lets probabilities reach 2^kRescaleLog2 (well inside fp32/bf16 range)
+    // and leaves the result unchanged up to rounding.
+    const bool grow = (mx - m) * sl > kRescaleLog2;  // false for NaN (-inf - -inf)
+    if (__builtin_amdgcn_ballot_w64(grow)) {
+      const float m_new = fmaxf(m, mx);
+      const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * sl);
+      l *= alpha;
 #pragma unroll
       for (int db = 0; db < 4; ++db)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[c][db][r] *= alpha;
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int k16 = 0; k16 < 2; ++k16) {
-          u32x4 pk;
-#pragma unroll
-          for (int e = 0; e < 4; ++e)
-            pk[e] = pack_bf16_rne(sacc[c][kb][8 * k16 + 2 * e], sacc[c][kb][8 * k16 + 2 * e + 1]);
-          pb[c][kb][k16] = __builtin_bit_cast(bf16x8, pk);
-        }
+        for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+      m = m_new;
     }
+    const float mc = (m == -INFINITY) ? 0.f : m * sl;
+    bf16x8 pb[2][2];
+    float ls = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int k16 = 0; k16 < 2; ++k16) {
+        u32x4 pk;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * k16 + 2 * e], sl, -mc));
+          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * k16 + 2 * e + 1], sl, -mc));
+          ls += p0 + p1;
+          pk[e] = pack_bf16_rne(p0, p1);
+        }
+        pb[kb][k16] = __builtin_bit_cast(bf16x8, pk);
+      }
+    l += ls;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -343,8 +309,7 @@ attn_mfma_kernel(AttnArgs a) {
         for (int db = 0; db < 4; ++db) {
           const bf16x8 va =
               *reinterpret_cast<const bf16x8*>(Vl + (32 * db + l32) * VS + 32 * kb + 16 * k16 + 8 * h2);
-          o[0][db] = mfma(va, pb[0][kb][k16], o[0][db]);
-          o[1][db] = mfma(va, pb[1][kb][k16], o[1][db]);
+          o[db] = mfma(va, pb[kb][k16], o[db]);
         }
   };
 
@@ -359,38 +324,35 @@ attn_mfma_kernel(AttnArgs a) {
   }
 
   // ---- epilogue
+  const float lt = sum_halves(l);
+  if (!valid) return;
   const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
+  const int64_t orow_id = static_cast<int64_t>(t0 + tok) * a.num_q_heads + head;
+  if (a.num_splits > 1) {
+    float* wo = a.ws_o + (static_cast<int64_t>(z) * total_rows + orow_id) * D;
 #pragma unroll
-  for (int c = 0; c < 2; ++c) {
-    const float lt = sum_halves(l[c]);
-    if (!valid[c]) continue;
-    const int64_t row = static_cast<int64_t>(t0 + tok[c]) * a.num_q_heads + head[c];
-    if (a.num_splits > 1) {
-      float* wo = a.ws_o + (static_cast<int64_t>(z) * total_rows + row) * D;
+    for (int db = 0; db < 4; ++db)
 #pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          f32x4 v = {o[c][db][4 * rq], o[c][db][4 * rq + 1], o[c][db][4 * rq + 2], o[c][db][4 * rq + 3]};
-          *reinterpret_cast<f32x4*>(wo + 32 * db + 8 * rq + 4 * h2) = v;
-        }
-      if (h2 == 0) {
-        f32x2 ml = {m[c], lt};
-        *reinterpret_cast<f32x2*>(a.ws_ml + (static_cast<int64_t>(z) * total_rows + row) * 2) = ml;
+      for (int rq = 0; rq < 4; ++rq) {
+        f32x4 v = {o[db][4 * rq], o[db][4 * rq + 1], o[db][4 * rq + 2], o[db][4 * rq + 3]};
+        *reinterpret_cast<f32x4*>(wo + 32 * db + 8 * rq + 4 * h2) = v;
       }
-    } else {
-      const float inv = a.v_scale / lt;
-      __bf16* orow = static_cast<__bf16*>(a.out) + row * D;
-#pragma unroll
-      for (int db = 0; db < 4; ++db)
-#pragma unroll
-        for (int rq = 0; rq < 4; ++rq) {
-          u32x2 v;
-          v[0] = pack_bf16_rne(o[c][db][4 * rq] * inv, o[c][db][4 * rq + 1] * inv);
-          v[1] = pack_bf16_rne(o[c][db][4 * rq + 2] * inv, o[c][db][4 * rq + 3] * inv);
-          *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * rq + 4 * h2) = v;
-        }
+    if (h2 == 0) {
+      f32x2 ml = {m, lt};
+      *reinterpret_cast<f32x2*>(a.ws_ml + (static_cast<int64_t>(z) * total_rows + orow_id) * 2) = ml;
     }
+  } else {
+    const float inv = a.v_scale / lt;
+    __bf16* orow = static_cast<__bf16*>(a.out) + orow_id * D;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        u32x2 v;
+        v[0] = pack_bf16_rne(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
+        v[1] = pack_bf16_rne(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
+        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * rq + 4 * h2) = v;
+      }
   }
 }
 

@@ -56,9 +56,12 @@ struct SplitPlan {
   int split_len;
 };
 
-// Number of key splits for the MFMA kernel: enough workgroups to fill the
-// device's compute units in whole waves, without cutting the key range into
-// pieces shorter than 512 keys, and never more than the workspace holds.
+// Number of key splits for the MFMA kernel.  One workgroup occupies a CU, so
+// the launch runs in ceil(workgroups / CUs) rounds of roughly equal
+// workgroups; splitting the key range shortens each workgroup but costs the
+// partial results' round trip through memory and a combine launch.  Pick the
+// split count with the smallest modelled time, never cutting the key range
+// below 512 keys and never needing more workspace than the caller gave.
 SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, int num_seqs, int max_query_len,
                       int max_seq_len, size_t workspace_bytes, bool have_workspace) {
   SplitPlan p{};
@@ -68,16 +71,20 @@ SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, i
   const int cus = cu_count();
   const int max_by_len = std::max(1, max_seq_len / 512);
   const int64_t per_split_bytes = num_q_tokens * num_q_heads * (128 + 2) * static_cast<int64_t>(sizeof(float));
+  constexpr double kCuFlops = 4.9e12;     // sustained FLOP/s of one CU on this kernel (about half of peak)
+  constexpr double kPartialBw = 5.0e12;   // B/s for writing and re-reading the partials
+  constexpr double kCombineLaunch = 3e-6; // s
   int best = 1;
-  double best_score = -1.0;
+  double best_t = 1e30;
   for (int sp = 1; sp <= std::min(16, max_by_len); ++sp) {
-    if (sp > 1 && have_workspace && static_cast<int64_t>(workspace_bytes) < per_split_bytes * sp) break;
-    if (sp > 1 && !have_workspace) break;
-    const double x = static_cast<double>(base) * sp / cus;
-    const double eff = x / std::ceil(x);
-    const double score = eff * (1.0 - 0.03 * (sp - 1));
-    if (score > best_score + 1e-9) {
-      best_score = score;
+    if (sp > 1 && (!have_workspace || workspace_bytes < static_cast<size_t>(per_split_bytes) * sp)) break;
+    const int64_t keys = ((max_seq_len + sp - 1) / sp + kMfmaKeyTile - 1) / kMfmaKeyTile * kMfmaKeyTile;
+    const double wg_time = static_cast<double>(kMfmaRows) * keys * 128 * 4 / kCuFlops;
+    const double rounds = std::ceil(static_cast<double>(base) * sp / cus);
+    double t = rounds * wg_time;
+    if (sp > 1) t += 2.0 * per_split_bytes * sp / kPartialBw + kCombineLaunch;
+    if (t < best_t * 0.98) {  // a split must buy a clear gain
+      best_t = t;
       best = sp;
     }
   }
