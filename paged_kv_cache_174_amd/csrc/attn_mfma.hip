@@ -5,27 +5,36 @@
 //   A "row" is one (query token, query head) pair of a KV-head group; a
 //   sequence with q tokens and G = Hq / Hkv query heads per KV head has q * G
 //   rows per KV head, ordered token-major, so the G heads that share a K/V
-//   tile are computed from one LDS copy of it (GQA).  A workgroup (4 waves)
-//   owns 256 consecutive rows of one (sequence, KV head) and, when the key
-//   range is split, one range of keys.  Each wave owns 64 rows, as two
-//   32-wide column blocks of the 32x32x16 bf16 MFMA.
+//   tile are computed from one LDS copy of it (GQA).  A workgroup of 8 waves
+//   (two per SIMD) owns 256 consecutive rows of one (sequence, KV head) and,
+//   when the key range is split, one range of keys; each wave owns 32 rows,
+//   one 32-wide column block of the 32x32x16 bf16 MFMA.
 //
-// Per 64-key tile
-//   * the tile's four 16-token blocks are found through the block table (one
-//     table entry per block; entries past ceil(seq_len / 16) are never read),
-//     K rows land in LDS row-major, V rows transposed (head_dim-major) so the
-//     P.V product can read 16-byte fragments; keys at or past seq_len are
-//     written as zeros, never loaded;
-//   * S^T = K Q^T on the MFMA: the accumulator puts one query per lane and 16
-//     keys per lane in registers, so the row max / row sum need one cross-half
-//     swap (v_permlane32_swap) instead of a 32-lane reduction;
+// K/V tiles (64 keys) in LDS
+//   Both K and V tiles are row-major bf16, one 256-byte row per key, with the
+//   sixteen 16-byte chunks of a row permuted by an XOR of the row index so
+//   that every read pattern below is free of bank conflicts.  A tile's four
+//   16-token blocks are found through the block table (one entry per block,
+//   staged in LDS once per workgroup; entries past ceil(seq_len / 16) are
+//   never read).  bf16 pools are copied straight from HBM into LDS with
+//   direct global-to-LDS loads; fp8 pools go through registers, where e4m3 is
+//   widened to bf16 exactly.  Keys outside the workgroup's range read a row
+//   of zeros, so a value row that does not exist is 0, never garbage.
+//
+// Per tile, per wave
+//   * S^T = K Q^T on the MFMA: the accumulator holds one query per lane and
+//     16 keys per lane, so the row max / row sum need one cross-half swap
+//     (v_permlane32_swap) instead of a 32-lane reduction;
 //   * the piecewise mask is a per-row key bound L(g) (full segment: kv_end,
 //     causal: g + 1), applied only on tiles that cross some row's bound;
-//   * online softmax in the exp2 domain (scale * log2 e folded into one FMA);
-//   * O^T += V^T P^T on the MFMA, with P rounded to bf16 as the pages' own
-//     reference rounds probabilities to the value dtype before the product.
-//   The next tile's global loads are issued before the current tile's math
-//   (register prefetch), and LDS is double-buffered: one barrier per tile.
+//   * online softmax in the exp2 domain with a lazily moved running max;
+//   * O^T += V^T P^T on the MFMA, the V^T operand read with the gfx950
+//     transposing LDS read (ds_read_b64_tr_b16) from the row-major V tile,
+//     P rounded to bf16 as the pages' own reference rounds probabilities to
+//     the value dtype before the product.
+//   The loop is software-pipelined over four LDS buffers: iteration t runs
+//   QK for tile t + 1 next to the exponentials of tile t, then PV of tile t,
+//   while tile t + 3 streams into LDS.
 //
 // Split keys: with num_splits > 1 each workgroup writes unnormalised partial
 // (O, max, sum) for its key range to the workspace and a combine kernel merges
@@ -33,6 +42,11 @@
 #include "attn_common.hpp"
 
 namespace pkv {
+
+// Zeros that direct-to-LDS loads of keys outside the staged range read
+// (static device storage starts zeroed and is never written).
+__device__ __attribute__((aligned(16))) uint32_t g_zero_row[64 * 4];
+
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -41,19 +55,44 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef short v4i16 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void* lds_ptr;
+typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
 
 constexpr int D = 128;
 constexpr int KT = kMfmaKeyTile;  // keys per tile
 constexpr int NW = 8;             // waves per workgroup (two per SIMD)
 constexpr int NT = 64 * NW;
-constexpr int KS = D + 8;    // K tile row stride in LDS (bf16): 272 B, breaks bank aliasing
-constexpr int VS = KT + 8;   // V^T tile row stride in LDS (bf16): 144 B
-constexpr int K_ELEMS = KT * KS;
-constexpr int V_ELEMS = D * VS;
-constexpr int BUF = K_ELEMS + V_ELEMS;
+constexpr int kRowBytes = D * 2;            // one bf16 K or V row of an LDS tile
+constexpr int kTileBytes = KT * kRowBytes;   // 16 KB
 constexpr int kWaveRows = 32;     // query rows per wave: one 32-wide MFMA column block
 static_assert(kMfmaRows == NW * kWaveRows, "rows per workgroup");
 constexpr float kRescaleLog2 = 8.0f;  // stale-max slack before O and l are rescaled
+constexpr int kBufs = 4;             // LDS K/V tile buffers: tiles t, t + 1 read while t + 2, t + 3 arrive
+constexpr int kVOff = 0;                           // V tiles [kBufs]
+constexpr int kKOff = kBufs * kTileBytes;          // K tiles [kBufs]
+constexpr int kTblOff = 2 * kBufs * kTileBytes;    // block-table slice
+constexpr int kLdsBytes = kTblOff + kTableSlice * 4;
+static_assert(kLdsBytes <= 160 * 1024, "LDS budget of a gfx950 CU");
+static_assert(kTableSlice * 16 >= kMaxSplitKeys, "table slice must cover a split");
+
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
+// waits for every outstanding global load, which would drain the K/V
+// prefetch issued for later tiles at each tile boundary.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
+// Waits until at most N of this wave's vector-memory loads are outstanding
+// (loads complete in order).  Direct-to-LDS loads are only counted here, so
+// the consumer's barrier must be preceded by this wait.
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
+}
 
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
@@ -101,9 +140,9 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
 template <bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2))) void
 attn_mfma_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) __bf16 lds[2 * BUF];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
+  int32_t* tbl = reinterpret_cast<int32_t*>(lds + kTblOff);  // this workgroup's block-table slice
   constexpr int ELSZ = FP8 ? 1 : 2;
-  using Chunk = typename std::conditional<FP8, u32x2, u32x4>::type;  // 8 head-dim elements
 
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -167,65 +206,86 @@ attn_mfma_kernel(AttnArgs a) {
     }
   }
 
-  // ---- K/V staging: waves 0-3 stage K, waves 4-7 stage V, 4 chunks per lane.
-  const bool stage_k = w < 4;
-  const int sw = w & 3;
-  const int64_t row_elems = static_cast<int64_t>(a.num_kv_heads) * D;
-  const uint8_t* src = static_cast<const uint8_t*>(stage_k ? a.kpool : a.vpool) + static_cast<int64_t>(hk) * D * ELSZ;
+  // ---- block-table slice for this workgroup's keys
   const int32_t* table = a.block_table + static_cast<int64_t>(b) * a.table_width;
   const int nblk = (s + 15) >> 4;
-  // K: wave sw stages keys [16 sw, 16 sw + 16) -- exactly tile block sw; lanes
-  // 16 apart take consecutive keys, lanes within 16 the 16 head-dim chunks.
-  // V: lane takes 4 consecutive keys 4 vkq + it of head-dim chunk v_chunk and
-  // writes them transposed as one 8-byte run per head-dim element.
-  const int vkq = lane & 15;
-  const int key_of_it0 = stage_k ? 16 * sw + (lane >> 4) : 4 * vkq;  // key of chunk 0
-  const int key_step = stage_k ? 4 : 1;
-  const int chunk = stage_k ? (lane & 15) : 4 * sw + (lane >> 4);
-  const int v_pos = 16 * (vkq >> 2) + 8 * (vkq & 1) + 4 * ((vkq >> 1) & 1);
+  const int blk_lo = k_begin >> 4;
+  const int blk_hi = min((k_end + 15) >> 4, nblk);
+  for (int i = threadIdx.x; i < blk_hi - blk_lo; i += NT) tbl[i] = table[blk_lo + i];
+  lds_barrier();
+  // Keys at or past kv_lim are staged as zeros: past seq_len they do not exist,
+  // and past the slice every row of the workgroup masks them anyway.
+  const int kv_lim = min(s, blk_hi * 16);
 
-  Chunk pre[4];
-  auto load_tile = [&](int kt) {
-    const int blk = (kt >> 4) + (stage_k ? sw : (vkq >> 2));  // one table entry per lane
-    const int e = (blk < nblk) ? table[blk] : 0;
+  // ---- staging geometry: wave w stages tile rows [8 w, 8 w + 8) of both the
+  // K and the V tile, four rows (one 1 KB direct load) per step; lane i takes
+  // row 8 w + 4 step + i / 16 and LDS chunk position i % 16.
+  const int64_t row_bytes = static_cast<int64_t>(a.num_kv_heads) * D * ELSZ;
+  const int64_t block_bytes = 16 * row_bytes;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.kpool) + static_cast<int64_t>(hk) * D * ELSZ;
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.vpool) + static_cast<int64_t>(hk) * D * ELSZ;
+  const int st_pos = lane & 15;
+  int st_row[2], k_src_off[2], v_src_off[2];
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const int kk = key_of_it0 + key_step * it;
-      const int64_t slot = static_cast<int64_t>(e) * 16 + (kk & 15);
-      const uint8_t* p = src + (slot * row_elems + 8 * chunk) * ELSZ;
-      Chunk zero = {};
-      pre[it] = (kt + kk < s) ? *reinterpret_cast<const Chunk*>(p) : zero;
-    }
-  };
+  for (int st = 0; st < 2; ++st) {
+    st_row[st] = 8 * w + 4 * st + (lane >> 4);
+    const int rb = st_row[st] & 15;  // row inside its 16-token block
+    k_src_off[st] = static_cast<int>(rb * row_bytes) + (st_pos ^ (st_row[st] & 7)) * 8 * ELSZ;
+    v_src_off[st] = static_cast<int>(rb * row_bytes) + (st_pos ^ ((st_row[st] & 3) << 1)) * 8 * ELSZ;
+  }
+  const uint8_t* zero_row = reinterpret_cast<const uint8_t*>(g_zero_row) + 16 * st_pos;
 
-  auto store_tile = [&](int buf) {
-    __bf16* Kl = lds + buf * BUF;
-    __bf16* Vl = Kl + K_ELEMS;
-    u32x4 v[4];
+  // Issue the loads of the tile at key kt into LDS buffer buf (bf16: direct
+  // to LDS; fp8: into registers, see fp8_store).
+  u32x2 f8k[2], f8v[2];
+  auto stage_load = [&](int kt, int buf) {
+    const int blk = (kt >> 4) + (w >> 1);
+    const int e = (blk < blk_hi) ? tbl[blk - blk_lo] : 0;
+    const int64_t boff = static_cast<int64_t>(e) * block_bytes;
 #pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      if constexpr (FP8) v[it] = e4m3x8_to_bf16x8(pre[it]); else v[it] = pre[it];
-    }
-    if (stage_k) {
-#pragma unroll
-      for (int it = 0; it < 4; ++it)
-        *reinterpret_cast<u32x4*>(Kl + (key_of_it0 + 4 * it) * KS + 8 * chunk) = v[it];
-    } else {
-#pragma unroll
-      for (int dd = 0; dd < 8; ++dd) {
-        const int wd = dd >> 1;
-        u32x2 x;
-        if (dd & 1) {
-          x[0] = (v[0][wd] >> 16) | (v[1][wd] & 0xFFFF0000u);
-          x[1] = (v[2][wd] >> 16) | (v[3][wd] & 0xFFFF0000u);
-        } else {
-          x[0] = (v[0][wd] & 0xFFFFu) | (v[1][wd] << 16);
-          x[1] = (v[2][wd] & 0xFFFFu) | (v[3][wd] << 16);
-        }
-        *reinterpret_cast<u32x2*>(Vl + (8 * chunk + dd) * VS + v_pos) = x;
+    for (int st = 0; st < 2; ++st) {
+      const bool ok = kt + st_row[st] < kv_lim;
+      if constexpr (FP8) {
+        const uint8_t* pk = kpool + boff + k_src_off[st];
+        const uint8_t* pv = vpool + boff + v_src_off[st];
+        f8k[st] = ok ? *reinterpret_cast<const u32x2*>(pk) : u32x2{0u, 0u};
+        f8v[st] = ok ? *reinterpret_cast<const u32x2*>(pv) : u32x2{0u, 0u};
+      } else {
+        const uint8_t* pk = ok ? kpool + boff + k_src_off[st] : zero_row;
+        const uint8_t* pv = ok ? vpool + boff + v_src_off[st] : zero_row;
+        const int dst = buf * kTileBytes + (8 * w + 4 * st) * kRowBytes;
+        __builtin_amdgcn_global_load_lds(pk, (lds_ptr)(lds + kKOff + dst), 16, 0, 0);
+        __builtin_amdgcn_global_load_lds(pv, (lds_ptr)(lds + kVOff + dst), 16, 0, 0);
       }
     }
   };
+  // fp8 only: widen the registers of the last stage_load into LDS buffer buf.
+  auto fp8_store = [&](int buf) {
+#pragma unroll
+    for (int st = 0; st < 2; ++st) {
+      const int dst = buf * kTileBytes + st_row[st] * kRowBytes + 16 * st_pos;
+      *reinterpret_cast<u32x4*>(lds + kKOff + dst) = e4m3x8_to_bf16x8(f8k[st]);
+      *reinterpret_cast<u32x4*>(lds + kVOff + dst) = e4m3x8_to_bf16x8(f8v[st]);
+    }
+  };
+
+  // ---- MFMA operand addresses (bytes, without the buffer offset)
+  int k_rd[8];  // K row 32 kb + l32, chunk 2 t + h2
+#pragma unroll
+  for (int t = 0; t < 8; ++t) k_rd[t] = kKOff + l32 * kRowBytes + 16 * ((2 * t + h2) ^ (l32 & 7));
+  // V^T via transposing reads: in each 16-lane group g, lane 4 j + q names the
+  // 8-byte piece of V row 4 (g / 2) + j holding head-dim [16 (g % 2) + 4 q, +4)
+  // of head-dim block db; the instruction hands lane i of the group element
+  // i % 4 of the pieces named by lanes 4 j + i / 4, i.e. V[key(j)][d(lane)].
+  int v_rd[4];
+  {
+    const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int c = 4 * db + 2 * (g & 1) + (q >> 1);
+      v_rd[db] = kVOff + (4 * (g >> 1) + j) * kRowBytes + 16 * (c ^ (2 * j)) + 8 * (q & 1);
+    }
+  }
 
   const float sl = a.scale_log2;
   float m = -INFINITY;
@@ -236,10 +296,8 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-  auto compute = [&](int buf, int kt) {
-    const __bf16* Kl = lds + buf * BUF;
-    const __bf16* Vl = Kl + K_ELEMS;
-    f32x16 sacc[2];
+  auto qk = [&](auto bufc, f32x16 (&sacc)[2]) {
+    constexpr int B = decltype(bufc)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -248,10 +306,14 @@ attn_mfma_kernel(AttnArgs a) {
     for (int t = 0; t < 8; ++t) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(Kl + (32 * kb + l32) * KS + 16 * t + 8 * h2);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lds + k_rd[t] + B * kTileBytes + kb * 32 * kRowBytes);
         sacc[kb] = mfma(ka, qf[t], sacc[kb]);
       }
     }
+  };
+
+  // Mask, running max (lazily moved) for tile kt.
+  auto mask_and_rescale = [&](int kt, f32x16 (&sacc)[2]) {
     if (kt + KT > wave_kmin) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -267,11 +329,11 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
     mx = max_halves(mx);
-    // Lazy rescaling: the running max only moves (and O, l are rescaled) when
-    // some row's tile max exceeds it by more than 2^kRescaleLog2 in the exp2
-    // domain.  Softmax is exact for any common offset, so a stale max only
-    // lets probabilities reach 2^kRescaleLog2 (well inside fp32/bf16 range)
-    // and leaves the result unchanged up to rounding.
+    // The running max only moves (and O, l are rescaled) when some row's tile
+    // max exceeds it by more than 2^kRescaleLog2 in the exp2 domain.  Softmax
+    // is exact for any common offset, so a stale max only lets probabilities
+    // reach 2^kRescaleLog2 (well inside fp32/bf16 range) and leaves the result
+    // unchanged up to rounding.
     const bool grow = (mx - m) * sl > kRescaleLog2;  // false for NaN (-inf - -inf)
     if (__builtin_amdgcn_ballot_w64(grow)) {
       const float m_new = fmaxf(m, mx);
@@ -283,8 +345,11 @@ attn_mfma_kernel(AttnArgs a) {
         for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
       m = m_new;
     }
+  };
+
+  // Probabilities of a tile, rounded to bf16, and their row sum.
+  auto probs = [&](const f32x16 (&sacc)[2], bf16x8 (&pb)[2][2]) {
     const float mc = (m == -INFINITY) ? 0.f : m * sl;
-    bf16x8 pb[2][2];
     float ls = 0.f;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -301,26 +366,81 @@ attn_mfma_kernel(AttnArgs a) {
         pb[kb][k16] = __builtin_bit_cast(bf16x8, pk);
       }
     l += ls;
+  };
+
+  auto pv = [&](auto bufc, const bf16x8 (&pb)[2][2]) {
+    constexpr int B = decltype(bufc)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
       for (int k16 = 0; k16 < 2; ++k16)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          const bf16x8 va =
-              *reinterpret_cast<const bf16x8*>(Vl + (32 * db + l32) * VS + 32 * kb + 16 * k16 + 8 * h2);
+          uint8_t* base = lds + v_rd[db] + B * kTileBytes + (32 * kb + 16 * k16) * kRowBytes;
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 8 * kRowBytes));
+          const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = mfma(va, pb[kb][k16], o[db]);
         }
   };
 
-  int buf = 0;
-  load_tile(k_begin);
-  for (int kt = k_begin; kt < k_end; kt += KT) {
-    store_tile(buf);
-    __syncthreads();
-    if (kt + KT < k_end) load_tile(kt + KT);
-    if (kt < wave_kmax) compute(buf, kt);
-    buf ^= 1;
+  // ---- software pipeline over tiles t = 0 .. n-1 (tile t: keys k_begin + 64 t,
+  // LDS buffer t % 4).  Iteration t: mask / max of S(t); S(t+1) = K(t+1) Q^T
+  // next to the exponentials of S(t); O += V(t) P(t); then the loads of tile
+  // t + 3 are issued (bf16) or tile t + 2 is widened into LDS and tile t + 3
+  // loaded into registers (fp8).  Buffer (t + 3) % 4 held tile t - 1, whose
+  // last reader was iteration t - 1; the barrier closing iteration t makes
+  // tile t + 2 visible to iteration t + 1.  S(t + 1) of the last tile reads a
+  // stale buffer and is never used.
+  const int ntiles = (k_end - k_begin + KT - 1) / KT;
+  auto kt_of = [&](int t) { return k_begin + t * KT; };
+  if constexpr (FP8) {
+    stage_load(kt_of(0), 0);
+    fp8_store(0);
+    if (ntiles > 1) { stage_load(kt_of(1), 1); fp8_store(1); }
+    if (ntiles > 2) stage_load(kt_of(2), 2);
+  } else {
+    stage_load(kt_of(0), 0);
+    if (ntiles > 1) stage_load(kt_of(1), 1);
+    if (ntiles > 2) {
+      stage_load(kt_of(2), 2);
+      wait_vmcnt<4>();
+    } else {
+      wait_vmcnt<0>();
+    }
+  }
+  lds_barrier();
+  f32x16 sA[2], sB[2];
+  qk(std::integral_constant<int, 0>{}, sA);
+
+  auto iteration = [&](auto bufc, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+    constexpr int B = decltype(bufc)::value;
+    const int kt = kt_of(t);
+    if (kt < wave_kmax) {
+      mask_and_rescale(kt, s_cur);
+      bf16x8 pb[2][2];
+      qk(std::integral_constant<int, (B + 1) % kBufs>{}, s_next);
+      probs(s_cur, pb);
+      pv(bufc, pb);
+    }
+    if constexpr (FP8) {
+      if (t + 2 < ntiles) fp8_store((B + 2) % kBufs);
+      if (t + 3 < ntiles) stage_load(kt_of(t + 3), (B + 3) % kBufs);
+    } else {
+      if (t + 3 < ntiles) {
+        stage_load(kt_of(t + 3), (B + 3) % kBufs);
+        wait_vmcnt<4>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    }
+    lds_barrier();
+  };
+  for (int t = 0; t < ntiles; t += kBufs) {
+    iteration(std::integral_constant<int, 0>{}, t, sA, sB);
+    if (t + 1 < ntiles) iteration(std::integral_constant<int, 1>{}, t + 1, sB, sA);
+    if (t + 2 < ntiles) iteration(std::integral_constant<int, 2>{}, t + 2, sA, sB);
+    if (t + 3 < ntiles) iteration(std::integral_constant<int, 3>{}, t + 3, sB, sA);
   }
 
   // ---- epilogue
@@ -356,10 +476,11 @@ attn_mfma_kernel(AttnArgs a) {
   }
 }
 
-// Merges the key splits of one row per wave, in split order.
+// Merges the key splits of a row, in split order: 32 lanes per row, four
+// head-dim values per lane, eight rows per workgroup.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6);
+  const int sub = threadIdx.x & 31;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
   const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
   if (row >= total_rows) return;
   const int64_t t = row / a.num_q_heads;
@@ -369,20 +490,33 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int g = a.seq_lens[b] - q_len + static_cast<int>(t - t0);
   const int L = row_limit(a.segments, a.seg_loc[b], a.seg_loc[b + 1], g);
   const int nz = min(a.num_splits, (L + a.split_len - 1) / a.split_len);
+  f32x2 ml[kMaxSplits];
+  f32x4 ov[kMaxSplits];
   float M = -INFINITY;
-  for (int zz = 0; zz < nz; ++zz) M = fmaxf(M, a.ws_ml[(zz * total_rows + row) * 2]);
-  float den = 0.f, n0 = 0.f, n1 = 0.f;
-  for (int zz = 0; zz < nz; ++zz) {
-    const f32x2 ml = *reinterpret_cast<const f32x2*>(a.ws_ml + (zz * total_rows + row) * 2);
-    const float wz = __builtin_amdgcn_exp2f((ml[0] - M) * a.scale_log2);
-    const f32x2 ov = *reinterpret_cast<const f32x2*>(a.ws_o + (zz * total_rows + row) * D + 2 * lane);
-    den = fmaf(wz, ml[1], den);
-    n0 = fmaf(wz, ov[0], n0);
-    n1 = fmaf(wz, ov[1], n1);
+#pragma unroll
+  for (int zz = 0; zz < kMaxSplits; ++zz) {
+    if (zz < nz) {
+      ml[zz] = *reinterpret_cast<const f32x2*>(a.ws_ml + (zz * total_rows + row) * 2);
+      ov[zz] = *reinterpret_cast<const f32x4*>(a.ws_o + (zz * total_rows + row) * D + 4 * sub);
+      M = fmaxf(M, ml[zz][0]);
+    }
+  }
+  float den = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int zz = 0; zz < kMaxSplits; ++zz) {
+    if (zz < nz) {
+      const float wz = __builtin_amdgcn_exp2f((ml[zz][0] - M) * a.scale_log2);
+      den = fmaf(wz, ml[zz][1], den);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) num[e] = fmaf(wz, ov[zz][e], num[e]);
+    }
   }
   const float inv = a.v_scale / den;
-  uint32_t* orow = reinterpret_cast<uint32_t*>(static_cast<__bf16*>(a.out) + row * D);
-  orow[lane] = pack_bf16_rne(n0 * inv, n1 * inv);
+  u32x2 packed;
+  packed[0] = pack_bf16_rne(num[0] * inv, num[1] * inv);
+  packed[1] = pack_bf16_rne(num[2] * inv, num[3] * inv);
+  *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.out) + row * D + 4 * sub) = packed;
 }
 
 }  // namespace
@@ -401,7 +535,7 @@ hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipStream_t s) {
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s) {
   const int64_t rows = a.num_q_tokens * a.num_q_heads;
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<unsigned>((rows + 3) / 4)), dim3(256), 0, s, a);
+  hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<unsigned>((rows + 7) / 8)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

@@ -74,9 +74,11 @@ SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, i
   constexpr double kCuFlops = 4.9e12;     // sustained FLOP/s of one CU on this kernel (about half of peak)
   constexpr double kPartialBw = 5.0e12;   // B/s for writing and re-reading the partials
   constexpr double kCombineLaunch = 3e-6; // s
-  int best = 1;
+  // A split's block-table slice is staged in LDS, which bounds its length.
+  const int min_splits = static_cast<int>((static_cast<int64_t>(max_seq_len) + kMaxSplitKeys - 1) / kMaxSplitKeys);
+  int best = min_splits;
   double best_t = 1e30;
-  for (int sp = 1; sp <= std::min(16, max_by_len); ++sp) {
+  for (int sp = min_splits; sp <= std::max(min_splits, std::min(kMaxSplits, max_by_len)); ++sp) {
     if (sp > 1 && (!have_workspace || workspace_bytes < static_cast<size_t>(per_split_bytes) * sp)) break;
     const int64_t keys = ((max_seq_len + sp - 1) / sp + kMfmaKeyTile - 1) / kMfmaKeyTile * kMfmaKeyTile;
     const double wg_time = static_cast<double>(kMfmaRows) * keys * 128 * 4 / kCuFlops;
@@ -225,6 +227,12 @@ int pkv_paged_attn(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t
     return fail(PKV_EUNSUPPORTED, "bf16/fp8 attention supports head_dim 128, not %d", pools->head_dim);
   SplitPlan p = plan_splits(num_q_tokens, num_q_heads, pools->num_kv_heads, num_seqs, max_query_len, max_seq_len,
                             workspace_bytes, workspace != nullptr);
+  if (p.splits > kMaxSplits)
+    return fail(PKV_EUNSUPPORTED, "max_seq_len %d needs more than %d key splits", max_seq_len, kMaxSplits);
+  if (p.splits > 1 && (!workspace ||
+                       workspace_bytes < static_cast<size_t>(p.splits) * num_q_tokens * num_q_heads * (128 + 2) * sizeof(float)))
+    return fail(PKV_EINVAL, "max_seq_len %d needs %d key splits and a workspace of pkv_paged_attn_workspace_size() bytes",
+                max_seq_len, p.splits);
   a.row_tiles = p.row_tiles;
   a.num_splits = p.splits;
   a.split_len = p.split_len;

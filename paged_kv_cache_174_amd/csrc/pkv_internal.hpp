@@ -74,6 +74,12 @@ struct AttnArgs {
 // Rows (query token x query head of one KV group) one MFMA workgroup covers.
 constexpr int kMfmaRows = 256;
 constexpr int kMfmaKeyTile = 64;
+// Most key splits one attention call uses (the combine kernel holds one partial per split in registers).
+constexpr int kMaxSplits = 16;
+// Block-table entries one MFMA workgroup stages in LDS, so one key split spans at most
+// kTableSlice * 16 keys (minus one block for a split that starts mid-block).
+constexpr int kTableSlice = 4096;
+constexpr int kMaxSplitKeys = (kTableSlice - 1) * 16;
 
 hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s);
