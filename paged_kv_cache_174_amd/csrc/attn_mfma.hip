@@ -13,7 +13,7 @@
 // K/V tiles (64 keys) in LDS
 //   Both K and V tiles are row-major bf16, one 256-byte row per key, with the
 //   sixteen 16-byte chunks of a row permuted by an XOR of the row index so
-//   that every read pattern below is free of bank conflicts.  A tile's four
+//   that every read pattern below is free of bank conflicts (k_swz, v_swz).  A tile's four
 //   16-token blocks are found through the block table (one entry per block,
 //   staged in LDS once per workgroup; entries past ceil(seq_len / 16) are
 //   never read).  bf16 pools are copied straight from HBM into LDS with
@@ -69,21 +69,76 @@ constexpr int kWaveRows = 32;     // query rows per wave: one 32-wide MFMA colum
 static_assert(kMfmaRows == NW * kWaveRows, "rows per workgroup");
 constexpr float kRescaleLog2 = 8.0f;  // stale-max slack before O and l are rescaled
 constexpr int kBufs = 4;             // LDS K/V tile buffers: tiles t, t + 1 read while t + 2, t + 3 arrive
-constexpr int kVOff = 0;                           // V tiles [kBufs]
-constexpr int kKOff = kBufs * kTileBytes;          // K tiles [kBufs]
-constexpr int kTblOff = 2 * kBufs * kTileBytes;    // block-table slice
-constexpr int kLdsBytes = kTblOff + kTableSlice * 4;
+constexpr int kLdsBytes = 2 * kBufs * kTileBytes + kTableSlice * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of a gfx950 CU");
+
+// Every K/V tile buffer is its own LDS object: the compiler can then prove
+// that a direct-to-LDS load into one buffer does not alias reads of another,
+// and does not make those reads wait for the load.
+__shared__ __attribute__((aligned(16))) uint8_t s_k0[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t s_k1[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t s_k2[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t s_k3[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t s_v0[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t s_v1[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t s_v2[kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t s_v3[kTileBytes];
+__shared__ int32_t s_tbl[kTableSlice];  // the workgroup's slice of its block-table row
+static_assert(kBufs == 4, "one LDS object per buffer");
+
+template <int B>
+__device__ __forceinline__ uint8_t* kbuf() {
+  if constexpr (B == 0) return s_k0;
+  else if constexpr (B == 1) return s_k1;
+  else if constexpr (B == 2) return s_k2;
+  else return s_k3;
+}
+template <int B>
+__device__ __forceinline__ uint8_t* vbuf() {
+  if constexpr (B == 0) return s_v0;
+  else if constexpr (B == 1) return s_v1;
+  else if constexpr (B == 2) return s_v2;
+  else return s_v3;
+}
+template <int B>
+using Buf = std::integral_constant<int, B>;
+
+// One 16-byte-per-lane direct global-to-LDS load: lane i's 16 bytes from g
+// land at l + 16 i (l is wave-uniform, passed in M0).  Issued as inline
+// assembly so that the compiler does not add waits of its own for it: the
+// kernel waits for these loads explicitly (wait_vmcnt) before the barrier
+// that precedes their first reader.
+__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)l));
+  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0));
+}
 static_assert(kTableSlice * 16 >= kMaxSplitKeys, "table slice must cover a split");
 
-// Workgroup barrier that orders LDS accesses only.  __syncthreads() also
-// waits for every outstanding global load, which would drain the K/V
-// prefetch issued for later tiles at each tile boundary.
+// Workgroup barrier for the K/V tile pipeline.  __syncthreads() -- and any
+// release fence on LDS -- makes every wave wait for all of its outstanding
+// vector-memory loads, including the direct-to-LDS loads of tiles that are
+// only read iterations later, which would drain the prefetch at every tile.
+// Here each wave waits for its own LDS stores (lgkmcnt) and, before calling
+// this, for exactly the direct loads the next iteration reads (wait_vmcnt);
+// the empty asm statements keep the compiler from moving memory accesses
+// across the barrier.
 __device__ __forceinline__ void lds_barrier() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited on
   __builtin_amdgcn_s_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+  asm volatile("" ::: "memory");
 }
+
+// Chunk permutation of LDS tile rows.  The LDS serves 256 bytes per clock
+// from 64 four-byte banks, and a 256-byte row maps onto all of them, so the
+// 16-byte chunk c of row r is stored at position c ^ swz(r):
+//   K: the MFMA reads one chunk from 16 consecutive rows per clock -> XOR with
+//      r mod 16 puts them in 16 distinct positions;
+//   V: a transposing read takes four consecutive rows x 64 bytes (four
+//      chunks 4 k .. 4 k + 3) per clock -> XOR with 4 (r mod 4) moves each row
+//      to its own 64-byte quarter.
+__device__ __forceinline__ int k_swz(int r) { return r & 15; }
+__device__ __forceinline__ int v_swz(int r) { return 4 * (r & 3); }
 
 // Waits until at most N of this wave's vector-memory loads are outstanding
 // (loads complete in order).  Direct-to-LDS loads are only counted here, so
@@ -140,8 +195,7 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
 template <bool FP8>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2))) void
 attn_mfma_kernel(AttnArgs a) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-  int32_t* tbl = reinterpret_cast<int32_t*>(lds + kTblOff);  // this workgroup's block-table slice
+  int32_t* tbl = s_tbl;
   constexpr int ELSZ = FP8 ? 1 : 2;
 
   const int lane = threadIdx.x & 63;
@@ -230,17 +284,21 @@ attn_mfma_kernel(AttnArgs a) {
   for (int st = 0; st < 2; ++st) {
     st_row[st] = 8 * w + 4 * st + (lane >> 4);
     const int rb = st_row[st] & 15;  // row inside its 16-token block
-    k_src_off[st] = static_cast<int>(rb * row_bytes) + (st_pos ^ (st_row[st] & 7)) * 8 * ELSZ;
-    v_src_off[st] = static_cast<int>(rb * row_bytes) + (st_pos ^ ((st_row[st] & 3) << 1)) * 8 * ELSZ;
+    k_src_off[st] = static_cast<int>(rb * row_bytes) + (st_pos ^ k_swz(st_row[st])) * 8 * ELSZ;
+    v_src_off[st] = static_cast<int>(rb * row_bytes) + (st_pos ^ v_swz(st_row[st])) * 8 * ELSZ;
   }
   const uint8_t* zero_row = reinterpret_cast<const uint8_t*>(g_zero_row) + 16 * st_pos;
 
   // Issue the loads of the tile at key kt into LDS buffer buf (bf16: direct
   // to LDS; fp8: into registers, see fp8_store).
   u32x2 f8k[2], f8v[2];
-  auto stage_load = [&](int kt, int buf) {
+  // Block-table entry of the 16 keys this wave stages for the tile at key kt.
+  auto stage_entry = [&](int kt) {
     const int blk = (kt >> 4) + (w >> 1);
-    const int e = (blk < blk_hi) ? tbl[blk - blk_lo] : 0;
+    return (blk < blk_hi) ? tbl[blk - blk_lo] : 0;
+  };
+  auto stage_load = [&](int kt, auto bufc, int e) {
+    constexpr int B = decltype(bufc)::value;
     const int64_t boff = static_cast<int64_t>(e) * block_bytes;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
@@ -253,26 +311,27 @@ attn_mfma_kernel(AttnArgs a) {
       } else {
         const uint8_t* pk = ok ? kpool + boff + k_src_off[st] : zero_row;
         const uint8_t* pv = ok ? vpool + boff + v_src_off[st] : zero_row;
-        const int dst = buf * kTileBytes + (8 * w + 4 * st) * kRowBytes;
-        __builtin_amdgcn_global_load_lds(pk, (lds_ptr)(lds + kKOff + dst), 16, 0, 0);
-        __builtin_amdgcn_global_load_lds(pv, (lds_ptr)(lds + kVOff + dst), 16, 0, 0);
+        const int dst = (8 * w + 4 * st) * kRowBytes;
+        dma16(pk, kbuf<B>() + dst);
+        dma16(pv, vbuf<B>() + dst);
       }
     }
   };
   // fp8 only: widen the registers of the last stage_load into LDS buffer buf.
-  auto fp8_store = [&](int buf) {
+  auto fp8_store = [&](auto bufc) {
+    constexpr int B = decltype(bufc)::value;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const int dst = buf * kTileBytes + st_row[st] * kRowBytes + 16 * st_pos;
-      *reinterpret_cast<u32x4*>(lds + kKOff + dst) = e4m3x8_to_bf16x8(f8k[st]);
-      *reinterpret_cast<u32x4*>(lds + kVOff + dst) = e4m3x8_to_bf16x8(f8v[st]);
+      const int dst = st_row[st] * kRowBytes + 16 * st_pos;
+      *reinterpret_cast<u32x4*>(kbuf<B>() + dst) = e4m3x8_to_bf16x8(f8k[st]);
+      *reinterpret_cast<u32x4*>(vbuf<B>() + dst) = e4m3x8_to_bf16x8(f8v[st]);
     }
   };
 
   // ---- MFMA operand addresses (bytes, without the buffer offset)
   int k_rd[8];  // K row 32 kb + l32, chunk 2 t + h2
 #pragma unroll
-  for (int t = 0; t < 8; ++t) k_rd[t] = kKOff + l32 * kRowBytes + 16 * ((2 * t + h2) ^ (l32 & 7));
+  for (int t = 0; t < 8; ++t) k_rd[t] = l32 * kRowBytes + 16 * ((2 * t + h2) ^ k_swz(l32));
   // V^T via transposing reads: in each 16-lane group g, lane 4 j + q names the
   // 8-byte piece of V row 4 (g / 2) + j holding head-dim [16 (g % 2) + 4 q, +4)
   // of head-dim block db; the instruction hands lane i of the group element
@@ -283,7 +342,7 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int c = 4 * db + 2 * (g & 1) + (q >> 1);
-      v_rd[db] = kVOff + (4 * (g >> 1) + j) * kRowBytes + 16 * (c ^ (2 * j)) + 8 * (q & 1);
+      v_rd[db] = (4 * (g >> 1) + j) * kRowBytes + 16 * (c ^ v_swz(j)) + 8 * (q & 1);
     }
   }
 
@@ -306,7 +365,7 @@ attn_mfma_kernel(AttnArgs a) {
     for (int t = 0; t < 8; ++t) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(lds + k_rd[t] + B * kTileBytes + kb * 32 * kRowBytes);
+        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kbuf<B>() + k_rd[t] + kb * 32 * kRowBytes);
         sacc[kb] = mfma(ka, qf[t], sacc[kb]);
       }
     }
@@ -323,12 +382,16 @@ attn_mfma_kernel(AttnArgs a) {
           if (j >= Lrow) sacc[kb][r] = -INFINITY;
         }
     }
-    float mx = -INFINITY;
+    // Tree reduction: a sequential chain of 32 dependent maxima would cost
+    // 32 VALU latencies.
+    float t16[16];
 #pragma unroll
-    for (int kb = 0; kb < 2; ++kb)
+    for (int r = 0; r < 16; ++r) t16[r] = fmaxf(sacc[0][r], sacc[1][r]);
 #pragma unroll
-      for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sacc[kb][r]);
-    mx = max_halves(mx);
+    for (int w2 = 8; w2 >= 1; w2 >>= 1)
+#pragma unroll
+      for (int r = 0; r < w2; ++r) t16[r] = fmaxf(t16[r], t16[r + w2]);
+    const float mx = max_halves(t16[0]);
     // The running max only moves (and O, l are rescaled) when some row's tile
     // max exceeds it by more than 2^kRescaleLog2 in the exp2 domain.  Softmax
     // is exact for any common offset, so a stale max only lets probabilities
@@ -350,7 +413,7 @@ attn_mfma_kernel(AttnArgs a) {
   // Probabilities of a tile, rounded to bf16, and their row sum.
   auto probs = [&](const f32x16 (&sacc)[2], bf16x8 (&pb)[2][2]) {
     const float mc = (m == -INFINITY) ? 0.f : m * sl;
-    float ls = 0.f;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
@@ -360,12 +423,12 @@ attn_mfma_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * k16 + 2 * e], sl, -mc));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * k16 + 2 * e + 1], sl, -mc));
-          ls += p0 + p1;
+          ls[e] += p0 + p1;
           pk[e] = pack_bf16_rne(p0, p1);
         }
         pb[kb][k16] = __builtin_bit_cast(bf16x8, pk);
       }
-    l += ls;
+    l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
 
   auto pv = [&](auto bufc, const bf16x8 (&pb)[2][2]) {
@@ -376,7 +439,7 @@ attn_mfma_kernel(AttnArgs a) {
       for (int k16 = 0; k16 < 2; ++k16)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          uint8_t* base = lds + v_rd[db] + B * kTileBytes + (32 * kb + 16 * k16) * kRowBytes;
+          uint8_t* base = vbuf<B>() + v_rd[db] + (32 * kb + 16 * k16) * kRowBytes;
           const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
           const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 8 * kRowBytes));
           const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
@@ -395,52 +458,58 @@ attn_mfma_kernel(AttnArgs a) {
   const int ntiles = (k_end - k_begin + KT - 1) / KT;
   auto kt_of = [&](int t) { return k_begin + t * KT; };
   if constexpr (FP8) {
-    stage_load(kt_of(0), 0);
-    fp8_store(0);
-    if (ntiles > 1) { stage_load(kt_of(1), 1); fp8_store(1); }
-    if (ntiles > 2) stage_load(kt_of(2), 2);
+    stage_load(kt_of(0), Buf<0>{}, stage_entry(kt_of(0)));
+    fp8_store(Buf<0>{});
+    if (ntiles > 1) { stage_load(kt_of(1), Buf<1>{}, stage_entry(kt_of(1))); fp8_store(Buf<1>{}); }
+    if (ntiles > 2) stage_load(kt_of(2), Buf<2>{}, stage_entry(kt_of(2)));
   } else {
-    stage_load(kt_of(0), 0);
-    if (ntiles > 1) stage_load(kt_of(1), 1);
+    stage_load(kt_of(0), Buf<0>{}, stage_entry(kt_of(0)));
+    if (ntiles > 1) stage_load(kt_of(1), Buf<1>{}, stage_entry(kt_of(1)));
     if (ntiles > 2) {
-      stage_load(kt_of(2), 2);
+      stage_load(kt_of(2), Buf<2>{}, stage_entry(kt_of(2)));
       wait_vmcnt<4>();
     } else {
       wait_vmcnt<0>();
     }
   }
+  int e_next = stage_entry(kt_of(3));  // entry for the tile staged in iteration 0
   lds_barrier();
   f32x16 sA[2], sB[2];
-  qk(std::integral_constant<int, 0>{}, sA);
+  qk(Buf<0>{}, sA);
 
   auto iteration = [&](auto bufc, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
     constexpr int B = decltype(bufc)::value;
     const int kt = kt_of(t);
+    // Tile t + 3 goes into buffer (t + 3) % 4, free since the barrier that
+    // closed iteration t - 1; bf16 loads are issued first so that they
+    // overlap this iteration's math.
+    const int e_use = e_next;
+    e_next = stage_entry(kt_of(t + 4));
+    if constexpr (!FP8) {
+      if (t + 3 < ntiles) stage_load(kt_of(t + 3), Buf<(B + 3) % kBufs>{}, e_use);
+    }
     if (kt < wave_kmax) {
       mask_and_rescale(kt, s_cur);
       bf16x8 pb[2][2];
-      qk(std::integral_constant<int, (B + 1) % kBufs>{}, s_next);
+      qk(Buf<(B + 1) % kBufs>{}, s_next);
       probs(s_cur, pb);
       pv(bufc, pb);
     }
     if constexpr (FP8) {
-      if (t + 2 < ntiles) fp8_store((B + 2) % kBufs);
-      if (t + 3 < ntiles) stage_load(kt_of(t + 3), (B + 3) % kBufs);
+      if (t + 2 < ntiles) fp8_store(Buf<(B + 2) % kBufs>{});
+      if (t + 3 < ntiles) stage_load(kt_of(t + 3), Buf<(B + 3) % kBufs>{}, e_use);
     } else {
-      if (t + 3 < ntiles) {
-        stage_load(kt_of(t + 3), (B + 3) % kBufs);
-        wait_vmcnt<4>();
-      } else {
-        wait_vmcnt<0>();
-      }
+      // Tile t + 2 (issued one iteration ago) must have landed before the
+      // barrier after which iteration t + 1 reads it.
+      if (t + 3 < ntiles) wait_vmcnt<4>(); else wait_vmcnt<0>();
     }
     lds_barrier();
   };
   for (int t = 0; t < ntiles; t += kBufs) {
-    iteration(std::integral_constant<int, 0>{}, t, sA, sB);
-    if (t + 1 < ntiles) iteration(std::integral_constant<int, 1>{}, t + 1, sB, sA);
-    if (t + 2 < ntiles) iteration(std::integral_constant<int, 2>{}, t + 2, sA, sB);
-    if (t + 3 < ntiles) iteration(std::integral_constant<int, 3>{}, t + 3, sB, sA);
+    iteration(Buf<0>{}, t, sA, sB);
+    if (t + 1 < ntiles) iteration(Buf<1>{}, t + 1, sB, sA);
+    if (t + 2 < ntiles) iteration(Buf<2>{}, t + 2, sA, sB);
+    if (t + 3 < ntiles) iteration(Buf<3>{}, t + 3, sB, sA);
   }
 
   // ---- epilogue
