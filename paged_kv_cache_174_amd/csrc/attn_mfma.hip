@@ -50,6 +50,7 @@ __device__ __attribute__((aligned(16))) uint32_t g_zero_row[64 * 4];
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
@@ -72,34 +73,32 @@ constexpr int kBufs = 4;             // LDS K/V tile buffers: tiles t, t + 1 rea
 constexpr int kLdsBytes = 2 * kBufs * kTileBytes + kTableSlice * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of a gfx950 CU");
 
-// Every K/V tile buffer is its own LDS object: the compiler can then prove
-// that a direct-to-LDS load into one buffer does not alias reads of another,
-// and does not make those reads wait for the load.
-__shared__ __attribute__((aligned(16))) uint8_t s_k0[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t s_k1[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t s_k2[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t s_k3[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t s_v0[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t s_v1[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t s_v2[kTileBytes];
-__shared__ __attribute__((aligned(16))) uint8_t s_v3[kTileBytes];
+// K and V tile buffers.  The direct-to-LDS loads that fill them are inline
+// assembly the compiler does not see as LDS writes, so it adds no waits for
+// them before reads of other buffers; the kernel orders them itself
+// (wait_vmcnt, lds_barrier).
+__shared__ __attribute__((aligned(16))) uint8_t s_k[kBufs][kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t s_v[kBufs][kTileBytes];
 __shared__ int32_t s_tbl[kTableSlice];  // the workgroup's slice of its block-table row
-static_assert(kBufs == 4, "one LDS object per buffer");
 
 template <int B>
-__device__ __forceinline__ uint8_t* kbuf() {
-  if constexpr (B == 0) return s_k0;
-  else if constexpr (B == 1) return s_k1;
-  else if constexpr (B == 2) return s_k2;
-  else return s_k3;
-}
+__device__ __forceinline__ uint8_t* kbuf() { return s_k[B]; }
 template <int B>
-__device__ __forceinline__ uint8_t* vbuf() {
-  if constexpr (B == 0) return s_v0;
-  else if constexpr (B == 1) return s_v1;
-  else if constexpr (B == 2) return s_v2;
-  else return s_v3;
+__device__ __forceinline__ uint8_t* vbuf() { return s_v[B]; }
+
+// LDS byte address of p, hidden from the optimiser: addresses built as
+// opaque base + constant keep the constant (buffer, key block) in the 16-bit
+// offset field of the LDS instruction instead of an add per read.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)p));
+  asm volatile("" : "+v"(a));
+  return a;
 }
+template <typename T>
+__device__ __forceinline__ const __attribute__((address_space(3))) T* lds_at(uint32_t a) {
+  return (const __attribute__((address_space(3))) T*)(a);
+}
+
 template <int B>
 using Buf = std::integral_constant<int, B>;
 
@@ -111,6 +110,12 @@ using Buf = std::integral_constant<int, B>;
 __device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)l));
   asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0));
+}
+// The same with a wave-uniform base address in SGPRs and a per-lane 32-bit
+// byte offset, so the address takes no vector arithmetic.
+__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint8_t* l) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)l));
+  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0));
 }
 static_assert(kTableSlice * 16 >= kMaxSplitKeys, "table slice must cover a split");
 
@@ -185,11 +190,17 @@ __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 c) {
   return r;
 }
 
+// Two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32;
+// converting the two halves separately costs five instructions).
 __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
-  const __bf16 a = static_cast<__bf16>(lo);
-  const __bf16 b = static_cast<__bf16>(hi);
-  return static_cast<uint32_t>(__builtin_bit_cast(uint16_t, a)) |
-         (static_cast<uint32_t>(__builtin_bit_cast(uint16_t, b)) << 16);
+  const f32x2 v = {lo, hi};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
+}
+
+// acc + lo + hi of a packed bf16 pair, accumulated in fp32.
+__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
+                                         __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
 }
 
 template <bool FP8>
@@ -299,21 +310,31 @@ attn_mfma_kernel(AttnArgs a) {
   };
   auto stage_load = [&](int kt, auto bufc, int e) {
     constexpr int B = decltype(bufc)::value;
-    const int64_t boff = static_cast<int64_t>(e) * block_bytes;
+    // The wave's eight rows lie in one 16-key block: its base address is
+    // wave-uniform and lives in SGPRs.
+    const int64_t boff = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(e)) * block_bytes;
+    const uint8_t* kb = kpool + boff;
+    const uint8_t* vb = vpool + boff;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const bool ok = kt + st_row[st] < kv_lim;
-      if constexpr (FP8) {
-        const uint8_t* pk = kpool + boff + k_src_off[st];
-        const uint8_t* pv = vpool + boff + v_src_off[st];
-        f8k[st] = ok ? *reinterpret_cast<const u32x2*>(pk) : u32x2{0u, 0u};
-        f8v[st] = ok ? *reinterpret_cast<const u32x2*>(pv) : u32x2{0u, 0u};
-      } else {
-        const uint8_t* pk = ok ? kpool + boff + k_src_off[st] : zero_row;
-        const uint8_t* pv = ok ? vpool + boff + v_src_off[st] : zero_row;
-        const int dst = (8 * w + 4 * st) * kRowBytes;
-        dma16(pk, kbuf<B>() + dst);
-        dma16(pv, vbuf<B>() + dst);
+      const int dst = (8 * w + 4 * st) * kRowBytes;
+      if (kt + 8 * w + 4 * st + 4 <= kv_lim) {  // all four rows exist (uniform)
+        if constexpr (FP8) {
+          f8k[st] = *reinterpret_cast<const u32x2*>(kb + k_src_off[st]);
+          f8v[st] = *reinterpret_cast<const u32x2*>(vb + v_src_off[st]);
+        } else {
+          dma16(kb, static_cast<uint32_t>(k_src_off[st]), kbuf<B>() + dst);
+          dma16(vb, static_cast<uint32_t>(v_src_off[st]), vbuf<B>() + dst);
+        }
+      } else {  // the tile at the end of the staged keys: rows past kv_lim read zeros
+        const bool ok = kt + st_row[st] < kv_lim;
+        if constexpr (FP8) {
+          f8k[st] = ok ? *reinterpret_cast<const u32x2*>(kb + k_src_off[st]) : u32x2{0u, 0u};
+          f8v[st] = ok ? *reinterpret_cast<const u32x2*>(vb + v_src_off[st]) : u32x2{0u, 0u};
+        } else {
+          dma16(ok ? kb + k_src_off[st] : zero_row, kbuf<B>() + dst);
+          dma16(ok ? vb + v_src_off[st] : zero_row, vbuf<B>() + dst);
+        }
       }
     }
   };
@@ -329,20 +350,20 @@ attn_mfma_kernel(AttnArgs a) {
   };
 
   // ---- MFMA operand addresses (bytes, without the buffer offset)
-  int k_rd[8];  // K row 32 kb + l32, chunk 2 t + h2
+  uint32_t k_rd[8];  // LDS address in buffer 0 of K row 32 kb + l32, chunk 2 t + h2
 #pragma unroll
-  for (int t = 0; t < 8; ++t) k_rd[t] = l32 * kRowBytes + 16 * ((2 * t + h2) ^ k_swz(l32));
+  for (int t = 0; t < 8; ++t) k_rd[t] = lds_addr(s_k[0] + l32 * kRowBytes + 16 * ((2 * t + h2) ^ k_swz(l32)));
   // V^T via transposing reads: in each 16-lane group g, lane 4 j + q names the
   // 8-byte piece of V row 4 (g / 2) + j holding head-dim [16 (g % 2) + 4 q, +4)
   // of head-dim block db; the instruction hands lane i of the group element
   // i % 4 of the pieces named by lanes 4 j + i / 4, i.e. V[key(j)][d(lane)].
-  int v_rd[4];
+  uint32_t v_rd[4];  // LDS address in buffer 0
   {
     const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int c = 4 * db + 2 * (g & 1) + (q >> 1);
-      v_rd[db] = (4 * (g >> 1) + j) * kRowBytes + 16 * (c ^ v_swz(j)) + 8 * (q & 1);
+      v_rd[db] = lds_addr(s_v[0] + (4 * (g >> 1) + j) * kRowBytes + 16 * (c ^ v_swz(j)) + 8 * (q & 1));
     }
   }
 
@@ -365,7 +386,7 @@ attn_mfma_kernel(AttnArgs a) {
     for (int t = 0; t < 8; ++t) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb) {
-        const bf16x8 ka = *reinterpret_cast<const bf16x8*>(kbuf<B>() + k_rd[t] + kb * 32 * kRowBytes);
+        const bf16x8 ka = *lds_at<bf16x8>(k_rd[t] + B * kTileBytes + kb * 32 * kRowBytes);
         sacc[kb] = mfma(ka, qf[t], sacc[kb]);
       }
     }
@@ -382,16 +403,17 @@ attn_mfma_kernel(AttnArgs a) {
           if (j >= Lrow) sacc[kb][r] = -INFINITY;
         }
     }
-    // Tree reduction: a sequential chain of 32 dependent maxima would cost
-    // 32 VALU latencies.
-    float t16[16];
+    // Four independent chains of three-input maxima (v_max3_f32): 18
+    // instructions for the 32 values, with four chains in flight.
+    float c4[4];
 #pragma unroll
-    for (int r = 0; r < 16; ++r) t16[r] = fmaxf(sacc[0][r], sacc[1][r]);
-#pragma unroll
-    for (int w2 = 8; w2 >= 1; w2 >>= 1)
-#pragma unroll
-      for (int r = 0; r < w2; ++r) t16[r] = fmaxf(t16[r], t16[r + w2]);
-    const float mx = max_halves(t16[0]);
+    for (int i = 0; i < 4; ++i) {
+      float c = fmaxf(fmaxf(sacc[0][i], sacc[0][i + 4]), sacc[0][i + 8]);
+      c = fmaxf(fmaxf(c, sacc[0][i + 12]), sacc[1][i]);
+      c = fmaxf(fmaxf(c, sacc[1][i + 4]), sacc[1][i + 8]);
+      c4[i] = fmaxf(c, sacc[1][i + 12]);
+    }
+    const float mx = max_halves(fmaxf(fmaxf(fmaxf(c4[0], c4[1]), c4[2]), c4[3]));
     // The running max only moves (and O, l are rescaled) when some row's tile
     // max exceeds it by more than 2^kRescaleLog2 in the exp2 domain.  Softmax
     // is exact for any common offset, so a stale max only lets probabilities
@@ -423,8 +445,10 @@ attn_mfma_kernel(AttnArgs a) {
         for (int e = 0; e < 4; ++e) {
           const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * k16 + 2 * e], sl, -mc));
           const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * k16 + 2 * e + 1], sl, -mc));
-          ls[e] += p0 + p1;
           pk[e] = pack_bf16_rne(p0, p1);
+          // The row sum takes the bf16-rounded probabilities, the very
+          // weights that multiply V, so the output's weights sum to one.
+          ls[e] = add_bf16_pair(pk[e], ls[e]);
         }
         pb[kb][k16] = __builtin_bit_cast(bf16x8, pk);
       }
@@ -439,7 +463,7 @@ attn_mfma_kernel(AttnArgs a) {
       for (int k16 = 0; k16 < 2; ++k16)
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
-          uint8_t* base = vbuf<B>() + v_rd[db] + (32 * kb + 16 * k16) * kRowBytes;
+          const uint32_t base = v_rd[db] + B * kTileBytes + (32 * kb + 16 * k16) * kRowBytes;
           const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
           const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 8 * kRowBytes));
           const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
