@@ -3,17 +3,21 @@
 A step is one pass of the path over one batch: the current chunk's K/V is
 scattered into the pools through the slot mapping (pkv_paged_write), then the
 chunk's queries attend over the visible history through the block table
-(pkv_paged_attn).  The 40-layer workload runs that pair once per layer, each
-layer with its own pools and inputs, all sharing one metadata plan.  Inputs,
-pools and metadata are resident in HBM before timing starts; the history is
-written (untimed) during setup.
+(pkv_paged_attn, issued as its two halves: the attention kernel, then the
+merge of key splits).  The 40-layer workload runs that pair once per layer,
+each layer with its own pools and inputs, all sharing one metadata plan.
+Inputs, pools and metadata are resident in HBM before timing starts; the
+history is written (untimed) during setup.
 
 Prints one JSON line.  `value` is algorithmic attention TFLOP/s over whole
 steps (4 * D * Hq * visible query-key pairs per call).  `roofline` is for the
-paged_attn call (main MFMA kernel plus the split combine when the key range is
-split), timed with HIP events on the stream the library launches on.  The
-history-staging gather and the contiguous path that reads it are timed too
-and reported under `parts`.
+attention kernel (attn_mfma_kernel), timed with HIP events on the stream the
+library launches on; its `traffic` comes from the committed rocprofv3
+FETCH_SIZE / WRITE_SIZE summary for this workload when that summary was taken
+on the current kernel sources (null otherwise).  `kv_bound` times the same
+kernel on the KV-bound half of the varlen fp8 batch (query length 16) against
+HBM bandwidth.  The merge, the write and the history-staging gather are
+reported under `parts`.
 
     python bench.py [--steps K] [--warmup W] [--workload frame_bf16]
 """
@@ -21,6 +25,7 @@ and reported under `parts`.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -38,6 +43,10 @@ PEAK_HBM_GBPS = 8000.0  # MI355X HBM3E
 ELT = {"f32": 4, "bf16": 2, "fp8": 1}
 
 
+# Sources whose change invalidates a stored traffic measurement of the attention kernel.
+KERNEL_SOURCES = ("attn_mfma.hip", "attn_common.hpp", "pkv_internal.hpp", "pkv_api.cpp")
+
+
 def parse():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -45,8 +54,47 @@ def parse():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="frame_bf16")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-kv-bound", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (the gather kernel) a few times, so that a "
+                         "counter run can scale FETCH_SIZE / WRITE_SIZE by a known byte count")
     return ap.parse_args()
+
+
+def kernel_source_hash() -> str:
+    """SHA-256 of the kernel sources with comments and blank space removed, so
+    that an edit of a comment does not invalidate a measurement."""
+    import re
+
+    h = hashlib.sha256()
+    for name in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_174_amd", "csrc", name)) as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+        text = re.sub(r"//[^\n]*", " ", text)
+        h.update(" ".join(text.split()).encode())
+    return h.hexdigest()
+
+
+def stored_traffic(workload: str):
+    """HBM bytes per attention launch from the committed counter summary, or
+    None when there is none or it was taken on other kernel sources."""
+    path = os.path.join(ROOT, "profiles", f"attn_mfma_{workload}_traffic.txt")
+    if not os.path.exists(path):
+        return None
+    kv = {}
+    with open(path) as f:
+        for line in f:
+            if ":" in line and not line.startswith("#"):
+                k, v = line.split(":", 1)
+                kv[k.strip()] = v.strip()
+    if kv.get("source_sha256") != kernel_source_hash():
+        return None
+    try:
+        return int(kv["fetch_bytes_per_launch"]) + int(kv["write_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
 
 
 def _softmax_scale(d):
@@ -105,19 +153,23 @@ def run_bench(args, geom):
     scale = _softmax_scale(geom.head_dim)
     stream = torch.cuda.current_stream()
 
+    def attn_args(li, pools):
+        return (li.q, pools, plan.block_table, plan.query_start_loc, plan.seq_lens, plan.segments,
+                plan.segment_start_loc, scale, plan.max_query_len, plan.max_seq_len)
+
     def step(ev=None):
-        for li, pools, out in layers:
+        for i, (li, pools, out) in enumerate(layers):
             if ev is not None:
-                ev[0].record(stream)
+                ev[4 * i].record(stream)
             P.pkv_paged_write(li.k_cur, li.v_cur, plan.slot_mapping, pools)
             if ev is not None:
-                ev[1].record(stream)
-            P.pkv_paged_attn(li.q, pools, plan.block_table, plan.query_start_loc, plan.seq_lens, plan.segments,
-                             plan.segment_start_loc, scale, plan.max_query_len, plan.max_seq_len, out=out,
-                             workspace=ws)
+                ev[4 * i + 1].record(stream)
+            P.pkv_paged_attn_main(*attn_args(li, pools), out=out, workspace=ws)
             if ev is not None:
-                ev[2].record(stream)
-                ev = ev[3:]
+                ev[4 * i + 2].record(stream)
+            P.pkv_paged_attn_merge(*attn_args(li, pools), out=out, workspace=ws)
+            if ev is not None:
+                ev[4 * i + 3].record(stream)
 
     for _ in range(args.warmup):
         step()
@@ -136,14 +188,17 @@ def run_bench(args, geom):
     wall = time.perf_counter() - wall0
     step_ms = t0.elapsed_time(t1) / args.steps
 
-    # per-call timing of the same steps, events between the calls
+    # per-launch timing of the same steps, events between the launches
     nl = len(layers)
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3 * nl)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4 * nl)] for _ in range(args.steps)]
     for k in range(args.steps):
         step(evs[k])
     torch.cuda.synchronize()
-    write_ms = np.mean([e[3 * i].elapsed_time(e[3 * i + 1]) for e in evs for i in range(nl)])
-    attn_ms = np.mean([e[3 * i + 1].elapsed_time(e[3 * i + 2]) for e in evs for i in range(nl)])
+
+    def mean_gap(a, b):
+        return float(np.mean([e[4 * i + a].elapsed_time(e[4 * i + b]) for e in evs for i in range(nl)]))
+
+    write_ms, main_ms, merge_ms = mean_gap(0, 1), mean_gap(1, 2), mean_gap(2, 3)
 
     # the history-staging gather over the whole visible window, and the
     # contiguous path that attends over the staged buffer (identity table)
@@ -168,6 +223,9 @@ def run_bench(args, geom):
                          plan.segment_start_loc, scale, plan.max_query_len, plan.max_seq_len, out=out,
                          workspace=ws)
 
+    if args.copy_calibration:
+        copy_calibration(pools)
+
     for _ in range(2):
         gather_all()
         staged_attn()
@@ -186,17 +244,16 @@ def run_bench(args, geom):
     abytes = attn_bytes(geom, plan)
     gbytes = 2 * 2 * sum(len(t) for t in plan.tables) * geom.block_size * geom.num_kv_heads * geom.head_dim * ELT[geom.pool_dtype]
     wbytes = write_bytes(geom)
-    achieved = flops / (attn_ms * 1e-3) / 1e12
-    value = flops * nl / (step_ms * 1e-3) / 1e12
     return {
         "step_ms": step_ms,
         "wall_s": wall,
-        "value": value,
+        "value": flops * nl / (step_ms * 1e-3) / 1e12,
         "flops": flops,
-        "attn_ms": attn_ms,
-        "achieved_tflops": achieved,
+        "main_ms": main_ms,
+        "merge_ms": merge_ms,
+        "achieved_tflops": flops / (main_ms * 1e-3) / 1e12,
         "attn_bytes": abytes,
-        "kv_gbps": abytes / (attn_ms * 1e-3) / 1e9,
+        "kv_gbps": abytes / (main_ms * 1e-3) / 1e9,
         "write_ms": write_ms,
         "write_gbps": wbytes / (write_ms * 1e-3) / 1e9,
         "gather_ms": gather_ms,
@@ -204,6 +261,81 @@ def run_bench(args, geom):
         "staged_attn_ms": staged_ms,
         "plan": plan,
         "layers": nl,
+    }
+
+
+def copy_calibration(pools, total_bytes=1 << 30, reps=3):
+    """A plain device copy of known size for scaling memory counters: the
+    gather kernel copying whole blocks of K and V (reads and writes
+    `total_bytes` each).  Not part of any reported number."""
+    import paged_kv_cache_174_amd as P
+
+    elt = pools.key.element_size()
+    row = pools.num_kv_heads * pools.head_dim * elt
+    n_blocks = total_bytes // 2 // (16 * row)
+    src = torch.empty((n_blocks * 16, pools.num_kv_heads, pools.head_dim), dtype=pools.key.dtype, device="cuda")
+    src.view(torch.uint8).fill_(1)
+    dk, dv = torch.empty_like(src), torch.empty_like(src)
+    cal = P.Pools(src, src, 16, pools.k_scale, pools.v_scale, pools.k_inv_scale, pools.v_inv_scale)
+    ids = torch.arange(n_blocks, dtype=torch.int32, device="cuda")
+    for _ in range(reps):
+        P.pkv_gather(cal, ids, n_blocks, 0, dk, dv)
+    torch.cuda.synchronize()
+    print(f"[copy-calibration] gather_kernel reads {2 * n_blocks * 16 * row} B and writes "
+          f"{2 * n_blocks * 16 * row} B per launch", file=sys.stderr, flush=True)
+
+
+def run_kv_bound(args):
+    """The attention kernel on the KV-bound half of the varlen fp8 batch
+    (query length 16), rotating through independent pools so each launch
+    reads its K/V from HBM, against HBM bandwidth."""
+    import paged_kv_cache_174_amd as P
+    from workloads import CONFIGS
+
+    geom = CONFIGS["varlen_fp8_q16"]
+    wl, plan, layers, ws = setup(geom)
+    scale = _softmax_scale(geom.head_dim)
+    stream = torch.cuda.current_stream()
+
+    def launch(li, pools, out):
+        args_ = (li.q, pools, plan.block_table, plan.query_start_loc, plan.seq_lens, plan.segments,
+                 plan.segment_start_loc, scale, plan.max_query_len, plan.max_seq_len)
+        P.pkv_paged_attn_main(*args_, out=out, workspace=ws)
+
+    for _ in range(max(args.warmup, 1)):
+        for layer in layers:
+            launch(*layer)
+    torch.cuda.synchronize()
+    n = max(args.steps, 5)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n * len(layers))]
+    k = 0
+    for _ in range(n):
+        for layer in layers:
+            ev[k].record(stream)
+            launch(*layer)
+            ev[k + 1].record(stream)
+            P.pkv_paged_attn_merge(layer[0].q, layer[1], plan.block_table, plan.query_start_loc, plan.seq_lens,
+                                   plan.segments, plan.segment_start_loc, scale, plan.max_query_len,
+                                   plan.max_seq_len, out=layer[2], workspace=ws)
+            k += 2
+    torch.cuda.synchronize()
+    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 2)]))
+    abytes = attn_bytes(geom, plan)
+    flops = plan.attn_flops(geom.num_q_heads, geom.head_dim)
+    gbps = abytes / (ms * 1e-3) / 1e9
+    return {
+        "workload": geom.name,
+        "kernel": "attn_mfma_kernel<fp8>",
+        "bound": "hbm",
+        "achieved": round(gbps, 1),
+        "peak": PEAK_HBM_GBPS,
+        "unit": "GB/s",
+        "frac": round(gbps / PEAK_HBM_GBPS, 4),
+        "bytes_per_launch": abytes,
+        "avg_launch_ms": round(ms, 5),
+        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "rotating_pools": len(layers),
+        "seq_lens": [int(x) for x in plan.kv_lens],
     }
 
 
@@ -271,7 +403,9 @@ def main():
     P.lib()  # fail loudly if the HIP library is missing
     r = run_bench(args, geom)
     plan = r.pop("plan")
+    kvb = None if args.no_kv_bound else run_kv_bound(args)
     cpu = None if args.no_cpu_baseline else cpu_baseline(geom, args.cpu_budget_s)
+    traffic = stored_traffic(geom.name)
     line = {
         "metric": METRIC,
         "value": round(r["value"], 2),
@@ -303,10 +437,10 @@ def main():
             "peak": PEAK_BF16_TFLOPS,
             "unit": "TFLOP/s",
             "frac": round(r["achieved_tflops"] / PEAK_BF16_TFLOPS, 4),
-            "traffic": None,
-            "kernel": "paged_attn call (attn_mfma_kernel + split combine)",
+            "traffic": traffic,
+            "kernel": "attn_mfma_kernel",
             "flop_per_launch": r["flops"],
-            "avg_launch_ms": round(r["attn_ms"], 5),
+            "avg_launch_ms": round(r["main_ms"], 5),
         },
         "kv": {
             "achieved_gbps": round(r["kv_gbps"], 1),
@@ -314,8 +448,11 @@ def main():
             "frac": round(r["kv_gbps"] / PEAK_HBM_GBPS, 4),
             "bytes_per_launch": r["attn_bytes"],
         },
+        "kv_bound": kvb,
         "parts": {
             "paged_write": {"ms": round(r["write_ms"], 5), "gbps": round(r["write_gbps"], 1)},
+            "split_merge_ms": round(r["merge_ms"], 5),
+            "paged_attn_call_ms": round(r["main_ms"] + r["merge_ms"], 5),
             "gather_whole_window": {"ms": round(r["gather_ms"], 5), "gbps": round(r["gather_gbps"], 1)},
             "attn_over_staged_buffer_ms": round(r["staged_attn_ms"], 5),
         },

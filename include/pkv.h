@@ -157,6 +157,30 @@ int pkv_paged_attn(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t
                    const int32_t* segment_start_loc, float softmax_scale, void* out, void* workspace,
                    size_t workspace_bytes, void* stream);
 
+/*
+ * The two halves of pkv_paged_attn, with its arguments, meaning and errors:
+ * pkv_paged_attn_main launches the attention kernel (which writes `out`
+ * directly when the key range is not split, else one partial result per
+ * split into `workspace`); pkv_paged_attn_merge then merges the partials into
+ * `out` in split order, and does nothing when the keys were not split.  Both
+ * plan the splits from the same arguments, so a caller passing identical
+ * arguments to both, in that order on one stream, gets exactly
+ * pkv_paged_attn's result.  They let a caller time or schedule the two
+ * launches separately.
+ */
+int pkv_paged_attn_main(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads,
+                        const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
+                        const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
+                        int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
+                        const int32_t* segment_start_loc, float softmax_scale, void* out, void* workspace,
+                        size_t workspace_bytes, void* stream);
+int pkv_paged_attn_merge(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads,
+                         const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
+                         const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
+                         int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
+                         const int32_t* segment_start_loc, float softmax_scale, void* out, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
 /* Workspace bytes pkv_paged_attn would like for these sizes on the current device. */
 size_t pkv_paged_attn_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t num_seqs, int32_t max_query_len,

@@ -21,6 +21,8 @@ from ._lib import (  # noqa: F401
     pkv_gather,
     pkv_last_error,
     pkv_paged_attn,
+    pkv_paged_attn_main,
+    pkv_paged_attn_merge,
     pkv_paged_attn_workspace_size,
     pkv_paged_write,
     pkv_slot_mapping,

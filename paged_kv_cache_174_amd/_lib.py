@@ -64,13 +64,14 @@ _PI32 = ctypes.POINTER(ctypes.c_int32)
 _PI64 = ctypes.POINTER(ctypes.c_int64)
 _PPOOLS = ctypes.POINTER(_Pools)
 
+_ATTN_ARGS = [_P, _I32, _I64, _I32, _PPOOLS, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _F32, _P, _P, _SZ, _P]
+
 _SIGNATURES = {
     "pkv_paged_write": (ctypes.c_int, [_P, _P, _I32, _I64, _P, _PPOOLS, _P]),
     "pkv_gather": (ctypes.c_int, [_PPOOLS, _P, _I32, _I32, _P, _P, _P]),
-    "pkv_paged_attn": (
-        ctypes.c_int,
-        [_P, _I32, _I64, _I32, _PPOOLS, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _F32, _P, _P, _SZ, _P],
-    ),
+    "pkv_paged_attn": (ctypes.c_int, _ATTN_ARGS),
+    "pkv_paged_attn_main": (ctypes.c_int, _ATTN_ARGS),
+    "pkv_paged_attn_merge": (ctypes.c_int, _ATTN_ARGS),
     "pkv_paged_attn_workspace_size": (_SZ, [_I64, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_slot_mapping": (ctypes.c_int, [_PI32, _I64, _I64, _I64, _I32, _PI64]),
     "pkv_window_table": (ctypes.c_int, [_PI32, _I64, _I64, _I64, _I64, _I64, _I32, _PI32, _I32, _PI32, _PI32]),
@@ -242,6 +243,7 @@ def pkv_paged_attn(
     out: torch.Tensor | None = None,
     workspace: torch.Tensor | None = None,
     stream=None,
+    _entry: str = "pkv_paged_attn",
 ) -> torch.Tensor:
     if q.dim() != 3 or q.shape[2] != pools.head_dim:
         raise ValueError("q must be [tokens, num_q_heads, head_dim]")
@@ -259,7 +261,7 @@ def pkv_paged_attn(
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
     ps = pools.c_struct()
     _check(
-        lib().pkv_paged_attn(
+        getattr(lib(), _entry)(
             _dev(q, "q"),
             _TORCH_DTYPE.get(q.dtype, -1),
             q.shape[0],
@@ -282,6 +284,18 @@ def pkv_paged_attn(
         )
     )
     return out
+
+
+def pkv_paged_attn_main(*args, **kwargs) -> torch.Tensor:
+    """The attention-kernel half of pkv_paged_attn (same arguments)."""
+    return pkv_paged_attn(*args, _entry="pkv_paged_attn_main", **kwargs)
+
+
+def pkv_paged_attn_merge(*args, **kwargs) -> torch.Tensor:
+    """The split-merge half of pkv_paged_attn (same arguments; `out` required)."""
+    if kwargs.get("out") is None:
+        raise ValueError("pkv_paged_attn_merge needs the `out` its pkv_paged_attn_main call wrote")
+    return pkv_paged_attn(*args, _entry="pkv_paged_attn_merge", **kwargs)
 
 
 # ----------------------------------------------------------------- host metadata

@@ -1,4 +1,9 @@
 // Device helpers shared by the attention kernels.
+//
+// Pages cited by tag and function: P1 "vllm_omni/experimental/ar_diffusion/kv_cache/paged_attention.py",
+// P2 "tests/diffusion/ar_diffusion/test_paged_attention.py",
+// P3 "vllm_omni/diffusion/attention/backends/utils/piecewise_attn.py",
+// P4 "vllm_omni/diffusion/diffusion_kv/paged_attention_adapter.py".
 #pragma once
 
 #include "pkv_internal.hpp"

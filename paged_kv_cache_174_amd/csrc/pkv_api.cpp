@@ -1,6 +1,11 @@
 // C-ABI front end of libpkv: argument validation, kernel selection and launch,
 // and the host-side metadata helpers (slot mapping, visible-window table,
 // piecewise segments, metadata validation).
+//
+// Pages cited by tag and function: P1 "vllm_omni/experimental/ar_diffusion/kv_cache/paged_attention.py",
+// P2 "tests/diffusion/ar_diffusion/test_paged_attention.py",
+// P3 "vllm_omni/diffusion/attention/backends/utils/piecewise_attn.py",
+// P4 "vllm_omni/diffusion/diffusion_kv/paged_attention_adapter.py".
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
@@ -163,12 +168,22 @@ size_t pkv_paged_attn_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, 
   return static_cast<size_t>(p.splits) * static_cast<size_t>(num_q_tokens) * num_q_heads * (head_dim + 2) * sizeof(float);
 }
 
-int pkv_paged_attn(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads,
-                   const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
-                   const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
-                   int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
-                   const int32_t* segment_start_loc, float softmax_scale, void* out, void* workspace,
-                   size_t workspace_bytes, void* stream) {
+}  // extern "C"
+
+namespace {
+
+constexpr unsigned kPhaseMain = 1u, kPhaseMerge = 2u;
+
+// Validates the arguments, plans the key splits and launches the phases asked
+// for: the attention kernel (kPhaseMain) and, when the keys are split, the
+// merge of the partial results (kPhaseMerge).  Both phases derive the same
+// plan from the same arguments.
+int paged_attn_impl(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads,
+                    const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
+                    const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
+                    const int32_t* segment_start_loc, float softmax_scale, void* out, void* workspace,
+                    size_t workspace_bytes, void* stream, unsigned phases) {
   g_error[0] = '\0';
   if (int rc = check_pools(pools)) return rc;
   if (!q || !out || !block_table || !query_start_loc || !seq_lens || !segments || !segment_start_loc)
@@ -219,8 +234,10 @@ int pkv_paged_attn(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t
     a.num_splits = 1;
     a.row_tiles = 0;
     a.split_len = 0;
-    if (hipError_t e = launch_attn_f32(a, max_query_len, st); e != hipSuccess)
-      return fail(PKV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+    if (phases & kPhaseMain) {
+      if (hipError_t e = launch_attn_f32(a, max_query_len, st); e != hipSuccess)
+        return fail(PKV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+    }
     return PKV_OK;
   }
   if (pools->head_dim != 128)
@@ -241,14 +258,38 @@ int pkv_paged_attn(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t
     a.ws_o = static_cast<float*>(workspace);
     a.ws_ml = a.ws_o + static_cast<int64_t>(p.splits) * rows * 128;
   }
-  if (hipError_t e = launch_attn_mfma(a, pools->dtype == PKV_FP8_E4M3, st); e != hipSuccess)
-    return fail(PKV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
-  if (p.splits > 1) {
+  if (phases & kPhaseMain) {
+    if (hipError_t e = launch_attn_mfma(a, pools->dtype == PKV_FP8_E4M3, st); e != hipSuccess)
+      return fail(PKV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+  }
+  if ((phases & kPhaseMerge) && p.splits > 1) {
     if (hipError_t e = launch_attn_combine(a, st); e != hipSuccess)
       return fail(PKV_EHIP, "split combine launch failed: %s", hipGetErrorString(e));
   }
   return PKV_OK;
 }
+
+}  // namespace
+
+extern "C" {
+
+#define PKV_ATTN_PARAMS                                                                                        \
+  const void *q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads, const pkv_pools *pools,          \
+      const int32_t *block_table, int32_t table_width, const int32_t *query_start_loc, const int32_t *seq_lens, \
+      int32_t num_seqs, int32_t max_query_len, int32_t max_seq_len, const int32_t *segments,                    \
+      const int32_t *segment_start_loc, float softmax_scale, void *out, void *workspace, size_t workspace_bytes, \
+      void *stream
+#define PKV_ATTN_ARGS                                                                                       \
+  q, q_dtype, num_q_tokens, num_q_heads, pools, block_table, table_width, query_start_loc, seq_lens,         \
+      num_seqs, max_query_len, max_seq_len, segments, segment_start_loc, softmax_scale, out, workspace,      \
+      workspace_bytes, stream
+
+int pkv_paged_attn(PKV_ATTN_PARAMS) { return paged_attn_impl(PKV_ATTN_ARGS, kPhaseMain | kPhaseMerge); }
+int pkv_paged_attn_main(PKV_ATTN_PARAMS) { return paged_attn_impl(PKV_ATTN_ARGS, kPhaseMain); }
+int pkv_paged_attn_merge(PKV_ATTN_PARAMS) { return paged_attn_impl(PKV_ATTN_ARGS, kPhaseMerge); }
+
+#undef PKV_ATTN_PARAMS
+#undef PKV_ATTN_ARGS
 
 // ------------------------------------------------------------------ host metadata
 

@@ -6,6 +6,10 @@ the current chunk, and the piecewise segments; it then pads the table to one
 width and uploads everything once (P1 ``ARDiffusionPagedForwardContext.prepare``
 builds the same metadata once per KV branch for all layers).  Python only
 moves arrays between the C calls and the device.
+Pages cited by tag and function: P1 "vllm_omni/experimental/ar_diffusion/kv_cache/paged_attention.py",
+P2 "tests/diffusion/ar_diffusion/test_paged_attention.py",
+P3 "vllm_omni/diffusion/attention/backends/utils/piecewise_attn.py",
+P4 "vllm_omni/diffusion/diffusion_kv/paged_attention_adapter.py".
 """
 
 from __future__ import annotations

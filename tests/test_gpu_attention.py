@@ -63,6 +63,13 @@ SMALL = [
     small_variant(CONFIGS["frame_bf16"], name="block_aligned_bf16", num_q_heads=2, num_kv_heads=2,
                   history_lens=(128,), query_lens=(64,), sink_tokens=(0,), window_tokens=(1 << 30,),
                   full_spans=(None,)),
+    # Long causal chunks: the key range is split, and early row tiles see fewer
+    # keys than one split holds (one split writes the output alone) while later
+    # ones span several splits (merged by the last split to finish).
+    small_variant(CONFIGS["piecewise_gqa_bf16"], name="causal_long_split_bf16", num_q_heads=2, num_kv_heads=2,
+                  history_lens=(0,), query_lens=(1200,), full_spans=((),)),
+    small_variant(CONFIGS["piecewise_gqa_bf16"], name="causal_hist_split_bf16", num_q_heads=4, num_kv_heads=2,
+                  history_lens=(3000, 100), query_lens=(600, 700), full_spans=((), ((100, 500),)), sink_tokens=(0, 0), window_tokens=(1 << 30,) * 2),
 ]
 
 

@@ -1,6 +1,10 @@
 """Pins of the CPU oracle to things other than itself: values the pages and the
 OCP fp8 spec fix, library routines, closed forms, brute force, and invariants
-the pages state.  No GPU."""
+the pages state.  No GPU.
+Pages cited by tag and function: P1 "vllm_omni/experimental/ar_diffusion/kv_cache/paged_attention.py",
+P2 "tests/diffusion/ar_diffusion/test_paged_attention.py",
+P3 "vllm_omni/diffusion/attention/backends/utils/piecewise_attn.py",
+P4 "vllm_omni/diffusion/diffusion_kv/paged_attention_adapter.py"."""
 
 import json
 import math

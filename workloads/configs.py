@@ -173,7 +173,28 @@ def _c5() -> Geometry:
     )
 
 
-CONFIGS = {g.name: g for g in (_c1(), _c2(), _c3(), _c4(), _c5())}
+def _c5_short_queries(layers: int = 4) -> Geometry:
+    """The 16-token-query sequences of the varlen batch on their own: the
+    KV-bound half (each visible K/V byte feeds only 16 queries x 4 heads).
+    ``layers`` independent pools are rotated through so that successive calls
+    do not find their K/V in the last-level cache."""
+    c5 = _c5()
+    keep = [b for b, q in enumerate(c5.query_lens) if q == 16]
+    pick = lambda t: tuple(t[b] for b in keep)  # noqa: E731
+    return replace(
+        c5,
+        name="varlen_fp8_q16",
+        history_lens=pick(c5.history_lens),
+        query_lens=pick(c5.query_lens),
+        sink_tokens=pick(c5.sink_tokens),
+        window_tokens=pick(c5.window_tokens),
+        full_spans=pick(c5.full_spans),
+        num_layers=layers,
+        note="the query-length-16 sequences of varlen_fp8, over several rotating pools",
+    )
+
+
+CONFIGS = {g.name: g for g in (_c1(), _c2(), _c3(), _c4(), _c5(), _c5_short_queries())}
 
 
 def small_variant(geom: Geometry, **overrides) -> Geometry:
