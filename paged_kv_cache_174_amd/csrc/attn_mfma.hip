@@ -270,6 +270,10 @@ attn_mfma_kernel(AttnArgs a) {
       qf[t] = __builtin_bit_cast(bf16x8, v);
     }
   }
+  // Q has landed before any K/V load is issued.  The compiler cannot see the
+  // direct-to-LDS loads (inline assembly); without this wait it may guard a
+  // later use of Q with a full vmcnt(0), which would drain the K/V prefetch.
+  wait_vmcnt<0>();
 
   // ---- block-table slice for this workgroup's keys
   const int32_t* table = a.block_table + static_cast<int64_t>(b) * a.table_width;
@@ -432,9 +436,15 @@ attn_mfma_kernel(AttnArgs a) {
     }
   };
 
-  // Probabilities of a tile, rounded to bf16, and their row sum.
-  auto probs = [&](const f32x16 (&sacc)[2], bf16x8 (&pb)[2][2]) {
+  // Probabilities of a tile, rounded to bf16, and their row sum.  The
+  // exponentials overwrite S in place (all 32 first, then the packs and sums),
+  // so the transcendental latency is covered without extra registers.
+  auto probs = [&](f32x16 (&sacc)[2], bf16x8 (&pb)[2][2]) {
     const float mc = (m == -INFINITY) ? 0.f : m * sl;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = __builtin_amdgcn_exp2f(fmaf(sacc[kb][r], sl, -mc));
     float ls[4] = {0.f, 0.f, 0.f, 0.f};  // four independent partial sums
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -443,9 +453,7 @@ attn_mfma_kernel(AttnArgs a) {
         u32x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          const float p0 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * k16 + 2 * e], sl, -mc));
-          const float p1 = __builtin_amdgcn_exp2f(fmaf(sacc[kb][8 * k16 + 2 * e + 1], sl, -mc));
-          pk[e] = pack_bf16_rne(p0, p1);
+          pk[e] = pack_bf16_rne(sacc[kb][8 * k16 + 2 * e], sacc[kb][8 * k16 + 2 * e + 1]);
           // The row sum takes the bf16-rounded probabilities, the very
           // weights that multiply V, so the output's weights sum to one.
           ls[e] = add_bf16_pair(pk[e], ls[e]);
