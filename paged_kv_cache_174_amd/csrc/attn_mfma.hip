@@ -39,6 +39,8 @@
 // Split keys: with num_splits > 1 each workgroup writes unnormalised partial
 // (O, max, sum) for its key range to the workspace and a combine kernel merges
 // the splits in a fixed order (deterministic, no atomics).
+#include <type_traits>
+
 #include "attn_common.hpp"
 
 namespace pkv {
@@ -177,15 +179,14 @@ __device__ __forceinline__ uint32_t pack_exact_bf16(float lo, float hi) {
   return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
 }
 
-// Eight e4m3 codes -> eight bf16 (exact: every e4m3 value is a bf16 value).
+// Eight e4m3 codes -> eight bf16 (exact: every e4m3 value is a bf16 value),
+// two codes per v_cvt_scalef32_pk_bf16_fp8 with scale 1.
 __device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 c) {
   u32x4 r;
 #pragma unroll
   for (int w = 0; w < 2; ++w) {
-    const f32x2 lo = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c[w]), false);
-    const f32x2 hi = __builtin_amdgcn_cvt_pk_f32_fp8(static_cast<int>(c[w]), true);
-    r[2 * w] = pack_exact_bf16(lo[0], lo[1]);
-    r[2 * w + 1] = pack_exact_bf16(hi[0], hi[1]);
+    r[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[w], 1.0f, false));
+    r[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[w], 1.0f, true));
   }
   return r;
 }
@@ -203,7 +204,12 @@ __device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
                                          __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
 }
 
-template <bool FP8>
+// SHORT: at most 64 rows per (sequence, KV head) (short query chunks).  The
+// eight waves then split the keys instead of the rows: wave w takes row block
+// w % 2 (32 rows) and key group w / 2, i.e. tiles 4 i + w / 2 of iteration i,
+// so every wave multiplies while the whole workgroup loads the next four tiles
+// into registers; the four key groups' partial results are merged in LDS.
+template <bool FP8, bool SHORT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2))) void
 attn_mfma_kernel(AttnArgs a) {
   int32_t* tbl = s_tbl;
@@ -243,7 +249,8 @@ attn_mfma_kernel(AttnArgs a) {
   const int k_end = min(k_begin + a.split_len, wg_kmax);
   if (k_begin >= k_end) return;
 
-  const int wr0 = r0 + kWaveRows * w;
+  const int kg = SHORT ? (w >> 1) : 0;  // key group (SHORT)
+  const int wr0 = SHORT ? kWaveRows * (w & 1) : r0 + kWaveRows * w;
   int wave_kmin = 0, wave_kmax = 0;
   if (wr0 < R) {
     wave_kmin = row_limit(a.segments, seg0, seg1, gbase + wr0 / G);
@@ -354,24 +361,26 @@ attn_mfma_kernel(AttnArgs a) {
   };
 
   // ---- MFMA operand addresses (bytes, without the buffer offset)
-  uint32_t k_rd[8];  // LDS address in buffer 0 of K row 32 kb + l32, chunk 2 t + h2
+  // (buffer 0, or the key group's own buffer for SHORT)
+  uint32_t k_rd[8];  // LDS address of K row 32 kb + l32, chunk 2 t + h2
 #pragma unroll
-  for (int t = 0; t < 8; ++t) k_rd[t] = lds_addr(s_k[0] + l32 * kRowBytes + 16 * ((2 * t + h2) ^ k_swz(l32)));
+  for (int t = 0; t < 8; ++t) k_rd[t] = lds_addr(s_k[kg] + l32 * kRowBytes + 16 * ((2 * t + h2) ^ k_swz(l32)));
   // V^T via transposing reads: in each 16-lane group g, lane 4 j + q names the
   // 8-byte piece of V row 4 (g / 2) + j holding head-dim [16 (g % 2) + 4 q, +4)
   // of head-dim block db; the instruction hands lane i of the group element
   // i % 4 of the pieces named by lanes 4 j + i / 4, i.e. V[key(j)][d(lane)].
-  uint32_t v_rd[4];  // LDS address in buffer 0
+  uint32_t v_rd[4];
   {
     const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
 #pragma unroll
     for (int db = 0; db < 4; ++db) {
       const int c = 4 * db + 2 * (g & 1) + (q >> 1);
-      v_rd[db] = lds_addr(s_v[0] + (4 * (g >> 1) + j) * kRowBytes + 16 * (c ^ v_swz(j)) + 8 * (q & 1));
+      v_rd[db] = lds_addr(s_v[kg] + (4 * (g >> 1) + j) * kRowBytes + 16 * (c ^ v_swz(j)) + 8 * (q & 1));
     }
   }
 
   const float sl = a.scale_log2;
+  float lt_merged = 0.f;  // SHORT: row sum after the key-group merge
   float m = -INFINITY;
   float l = 0.f;
   f32x16 o[4];
@@ -479,73 +488,232 @@ attn_mfma_kernel(AttnArgs a) {
         }
   };
 
-  // ---- software pipeline over tiles t = 0 .. n-1 (tile t: keys k_begin + 64 t,
-  // LDS buffer t % 4).  Iteration t: mask / max of S(t); S(t+1) = K(t+1) Q^T
-  // next to the exponentials of S(t); O += V(t) P(t); then the loads of tile
-  // t + 3 are issued (bf16) or tile t + 2 is widened into LDS and tile t + 3
-  // loaded into registers (fp8).  Buffer (t + 3) % 4 held tile t - 1, whose
-  // last reader was iteration t - 1; the barrier closing iteration t makes
-  // tile t + 2 visible to iteration t + 1.  S(t + 1) of the last tile reads a
-  // stale buffer and is never used.
-  const int ntiles = (k_end - k_begin + KT - 1) / KT;
-  auto kt_of = [&](int t) { return k_begin + t * KT; };
-  if constexpr (FP8) {
-    stage_load(kt_of(0), Buf<0>{}, stage_entry(kt_of(0)));
-    fp8_store(Buf<0>{});
-    if (ntiles > 1) { stage_load(kt_of(1), Buf<1>{}, stage_entry(kt_of(1))); fp8_store(Buf<1>{}); }
-    if (ntiles > 2) stage_load(kt_of(2), Buf<2>{}, stage_entry(kt_of(2)));
-  } else {
-    stage_load(kt_of(0), Buf<0>{}, stage_entry(kt_of(0)));
-    if (ntiles > 1) stage_load(kt_of(1), Buf<1>{}, stage_entry(kt_of(1)));
-    if (ntiles > 2) {
-      stage_load(kt_of(2), Buf<2>{}, stage_entry(kt_of(2)));
-      wait_vmcnt<4>();
+  if constexpr (SHORT) {
+    // ---- iteration i: each wave multiplies tile 4 i + kg from buffer kg
+    // while the workgroup loads tiles 4 i + 4 .. 4 i + 7 into registers; after
+    // a barrier they are written (fp8 widened) into buffers 0..3.
+    // Register staging, 16 bytes per lane per load.  bf16: lane i of wave w
+    // holds chunk i % 16 of rows 8 w + 4 st + i / 16 (st = 0, 1), at the
+    // positions stage_load uses.  fp8: one load per tile covers the wave's
+    // eight rows, lane i holding codes [16 p, 16 p + 16) (p = i % 8) of row
+    // 8 w + i / 8, i.e. chunks 2 p and 2 p + 1 once widened.
+    constexpr int kLoads = FP8 ? 1 : 2;  // loads per tile per lane, for K and for V
+    // fp8 tiles are loaded two steps ahead (two register sets); bf16 tiles,
+    // twice the bytes, one step ahead.
+    constexpr int kSets = FP8 ? 2 : 1;
+    u32x4 rk[kSets][4][kLoads], rv[kSets][4][kLoads];
+    const int f8_row = 8 * w + (lane >> 3), f8_pair = lane & 7;
+    const int f8_src = (f8_row & 15) * static_cast<int>(row_bytes) + 16 * f8_pair;
+    const int ntiles = (k_end - k_begin + KT - 1) / KT;
+    auto kt_of = [&](int t) { return k_begin + t * KT; };
+    auto load4 = [&](auto setc, int t_first) {
+      constexpr int S = decltype(setc)::value;
+      // All four block-table entries first: one LDS round trip, not four.
+      int e[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) e[j] = (t_first + j < ntiles) ? stage_entry(kt_of(t_first + j)) : 0;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int t = t_first + j;
+        if (t >= ntiles) break;
+        const int kt = kt_of(t);
+        const int64_t boff = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(e[j])) * block_bytes;
+        const u32x4 zero = {0u, 0u, 0u, 0u};
+        if constexpr (FP8) {
+          const bool ok = kt + f8_row < kv_lim;
+          rk[S][j][0] = ok ? *reinterpret_cast<const u32x4*>(kpool + boff + f8_src) : zero;
+          rv[S][j][0] = ok ? *reinterpret_cast<const u32x4*>(vpool + boff + f8_src) : zero;
+        } else {
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const bool ok = kt + st_row[st] < kv_lim;
+            rk[S][j][st] = ok ? *reinterpret_cast<const u32x4*>(kpool + boff + k_src_off[st]) : zero;
+            rv[S][j][st] = ok ? *reinterpret_cast<const u32x4*>(vpool + boff + v_src_off[st]) : zero;
+          }
+        }
+      }
+    };
+    auto store4 = [&](auto setc, int t_first) {
+      constexpr int S = decltype(setc)::value;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (t_first + j >= ntiles) break;
+        if constexpr (FP8) {
+          const int row = f8_row * kRowBytes;
+          const u32x4 klo = e4m3x8_to_bf16x8(u32x2{rk[S][j][0][0], rk[S][j][0][1]});
+          const u32x4 khi = e4m3x8_to_bf16x8(u32x2{rk[S][j][0][2], rk[S][j][0][3]});
+          const u32x4 vlo = e4m3x8_to_bf16x8(u32x2{rv[S][j][0][0], rv[S][j][0][1]});
+          const u32x4 vhi = e4m3x8_to_bf16x8(u32x2{rv[S][j][0][2], rv[S][j][0][3]});
+          *reinterpret_cast<u32x4*>(s_k[j] + row + 16 * ((2 * f8_pair) ^ k_swz(f8_row))) = klo;
+          *reinterpret_cast<u32x4*>(s_k[j] + row + 16 * ((2 * f8_pair + 1) ^ k_swz(f8_row))) = khi;
+          *reinterpret_cast<u32x4*>(s_v[j] + row + 16 * ((2 * f8_pair) ^ v_swz(f8_row))) = vlo;
+          *reinterpret_cast<u32x4*>(s_v[j] + row + 16 * ((2 * f8_pair + 1) ^ v_swz(f8_row))) = vhi;
+        } else {
+#pragma unroll
+          for (int st = 0; st < 2; ++st) {
+            const int dst = st_row[st] * kRowBytes + 16 * st_pos;
+            *reinterpret_cast<u32x4*>(s_k[j] + dst) = rk[S][j][st];
+            *reinterpret_cast<u32x4*>(s_v[j] + dst) = rv[S][j][st];
+          }
+        }
+      }
+    };
+    f32x16 sacc[2];
+    auto step = [&](auto cur, int t4) {
+      // Loads of the tiles two steps (fp8) or one step (bf16) ahead.
+      constexpr int C = decltype(cur)::value;
+      if constexpr (kSets == 2) load4(std::integral_constant<int, 1 - C>{}, t4 + 8);
+      else load4(std::integral_constant<int, 0>{}, t4 + 4);
+      const int t = t4 + kg;
+      if (t < ntiles && kt_of(t) < wave_kmax) {
+        qk(Buf<0>{}, sacc);
+        mask_and_rescale(kt_of(t), sacc);
+        bf16x8 pb[2][2];
+        probs(sacc, pb);
+        pv(Buf<0>{}, pb);
+      }
+      lds_barrier();
+      if constexpr (kSets == 2) store4(std::integral_constant<int, C>{}, t4 + 4);
+      else store4(std::integral_constant<int, 0>{}, t4 + 4);
+      lds_barrier();
+    };
+    if constexpr (kSets == 2) {
+      load4(std::integral_constant<int, 0>{}, 0);
+      store4(std::integral_constant<int, 0>{}, 0);
+      load4(std::integral_constant<int, 0>{}, 4);
+      lds_barrier();
+      // Step i keeps tiles 4 i + 4 .. + 7 in set i % 2 and loads 4 i + 8 .. into the other.
+      for (int t4 = 0; t4 < ntiles; t4 += 8) {
+        step(std::integral_constant<int, 0>{}, t4);
+        if (t4 + 4 < ntiles) step(std::integral_constant<int, 1>{}, t4 + 4);
+      }
     } else {
-      wait_vmcnt<0>();
+      load4(std::integral_constant<int, 0>{}, 0);
+      store4(std::integral_constant<int, 0>{}, 0);
+      lds_barrier();
+      for (int t4 = 0; t4 < ntiles; t4 += 4) step(std::integral_constant<int, 0>{}, t4);
     }
-  }
-  int e_next = stage_entry(kt_of(3));  // entry for the tile staged in iteration 0
-  lds_barrier();
-  f32x16 sA[2], sB[2];
-  qk(Buf<0>{}, sA);
 
-  auto iteration = [&](auto bufc, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
-    constexpr int B = decltype(bufc)::value;
-    const int kt = kt_of(t);
-    // Tile t + 3 goes into buffer (t + 3) % 4, free since the barrier that
-    // closed iteration t - 1; bf16 loads are issued first so that they
-    // overlap this iteration's math.
-    const int e_use = e_next;
-    e_next = stage_entry(kt_of(t + 4));
-    if constexpr (!FP8) {
-      if (t + 3 < ntiles) stage_load(kt_of(t + 3), Buf<(B + 3) % kBufs>{}, e_use);
-    }
-    if (kt < wave_kmax) {
-      mask_and_rescale(kt, s_cur);
-      bf16x8 pb[2][2];
-      qk(Buf<(B + 1) % kBufs>{}, s_next);
-      probs(s_cur, pb);
-      pv(bufc, pb);
-    }
-    if constexpr (FP8) {
-      if (t + 2 < ntiles) fp8_store(Buf<(B + 2) % kBufs>{});
-      if (t + 3 < ntiles) stage_load(kt_of(t + 3), Buf<(B + 3) % kBufs>{}, e_use);
-    } else {
-      // Tile t + 2 (issued one iteration ago) must have landed before the
-      // barrier after which iteration t + 1 reads it.
-      if (t + 3 < ntiles) wait_vmcnt<4>(); else wait_vmcnt<0>();
-    }
+    // ---- merge the four key groups of each row block: common max, then
+    // ((kg 0 + kg 2) + (kg 1 + kg 3)) in that order, through LDS.
+    float lt_own = sum_halves(l);
+    float* ml = reinterpret_cast<float*>(s_tbl);  // [wave][32 rows] running max
+    if (h2 == 0) ml[w * 32 + l32] = m;
     lds_barrier();
-  };
-  for (int t = 0; t < ntiles; t += kBufs) {
-    iteration(Buf<0>{}, t, sA, sB);
-    if (t + 1 < ntiles) iteration(Buf<1>{}, t + 1, sB, sA);
-    if (t + 2 < ntiles) iteration(Buf<2>{}, t + 2, sA, sB);
-    if (t + 3 < ntiles) iteration(Buf<3>{}, t + 3, sB, sA);
+    float M = -INFINITY;
+#pragma unroll
+    for (int g = 0; g < 4; ++g) M = fmaxf(M, ml[(2 * g + (w & 1)) * 32 + l32]);
+    const float f = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - M) * sl);
+    lt_own *= f;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[db][r] *= f;
+    // Region of a wave's O: 64 lanes x 64 floats, lane-interleaved f32x4.
+    auto o_slot = [&](uint8_t* region, int db, int rq) {
+      return reinterpret_cast<f32x4*>(region + ((db * 4 + rq) * 64 + lane) * 16);
+    };
+    float* lt_x = reinterpret_cast<float*>(s_tbl) + 512;  // [region][64 lanes]
+    auto put = [&](uint8_t* region, int slot) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq)
+          *o_slot(region, db, rq) = f32x4{o[db][4 * rq], o[db][4 * rq + 1], o[db][4 * rq + 2], o[db][4 * rq + 3]};
+      lt_x[slot * 64 + lane] = lt_own;
+    };
+    auto add = [&](uint8_t* region, int slot) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int rq = 0; rq < 4; ++rq) {
+          const f32x4 v = *o_slot(region, db, rq);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) o[db][4 * rq + e] += v[e];
+        }
+      lt_own += lt_x[slot * 64 + lane];
+    };
+    // level 1: kg 2, 3 hand over to kg 0, 1 (regions in the K buffers)
+    if (kg >= 2) put(s_k[w - 4], w - 4);
+    lds_barrier();
+    if (kg < 2) add(s_k[w], w);
+    lds_barrier();
+    // level 2: kg 1 hands over to kg 0 (regions in the V buffers)
+    if (kg == 1) put(s_v[w - 2], 4 + (w - 2));
+    lds_barrier();
+    if (kg == 0) add(s_v[w], 4 + w);
+    if (kg != 0) return;
+    m = M;
+    lt_merged = lt_own;
+  } else {
+    // ---- software pipeline over tiles t = 0 .. n-1 (tile t: keys k_begin + 64 t,
+    // LDS buffer t % 4).  Iteration t: mask / max of S(t); S(t+1) = K(t+1) Q^T
+    // next to the exponentials of S(t); O += V(t) P(t); then the loads of tile
+    // t + 3 are issued (bf16) or tile t + 2 is widened into LDS and tile t + 3
+    // loaded into registers (fp8).  Buffer (t + 3) % 4 held tile t - 1, whose
+    // last reader was iteration t - 1; the barrier closing iteration t makes
+    // tile t + 2 visible to iteration t + 1.  S(t + 1) of the last tile reads a
+    // stale buffer and is never used.
+    const int ntiles = (k_end - k_begin + KT - 1) / KT;
+    auto kt_of = [&](int t) { return k_begin + t * KT; };
+    if constexpr (FP8) {
+      stage_load(kt_of(0), Buf<0>{}, stage_entry(kt_of(0)));
+      fp8_store(Buf<0>{});
+      if (ntiles > 1) { stage_load(kt_of(1), Buf<1>{}, stage_entry(kt_of(1))); fp8_store(Buf<1>{}); }
+      if (ntiles > 2) stage_load(kt_of(2), Buf<2>{}, stage_entry(kt_of(2)));
+    } else {
+      stage_load(kt_of(0), Buf<0>{}, stage_entry(kt_of(0)));
+      if (ntiles > 1) stage_load(kt_of(1), Buf<1>{}, stage_entry(kt_of(1)));
+      if (ntiles > 2) {
+        stage_load(kt_of(2), Buf<2>{}, stage_entry(kt_of(2)));
+        wait_vmcnt<4>();
+      } else {
+        wait_vmcnt<0>();
+      }
+    }
+    int e_next = stage_entry(kt_of(3));  // entry for the tile staged in iteration 0
+    lds_barrier();
+    f32x16 sA[2], sB[2];
+    qk(Buf<0>{}, sA);
+
+    auto iteration = [&](auto bufc, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+      constexpr int B = decltype(bufc)::value;
+      const int kt = kt_of(t);
+      // Tile t + 3 goes into buffer (t + 3) % 4, free since the barrier that
+      // closed iteration t - 1; bf16 loads are issued first so that they
+      // overlap this iteration's math.
+      const int e_use = e_next;
+      e_next = stage_entry(kt_of(t + 4));
+      if constexpr (!FP8) {
+        if (t + 3 < ntiles) stage_load(kt_of(t + 3), Buf<(B + 3) % kBufs>{}, e_use);
+      }
+      if (kt < wave_kmax) {
+        mask_and_rescale(kt, s_cur);
+        bf16x8 pb[2][2];
+        qk(Buf<(B + 1) % kBufs>{}, s_next);
+        probs(s_cur, pb);
+        pv(bufc, pb);
+      }
+      if constexpr (FP8) {
+        if (t + 2 < ntiles) fp8_store(Buf<(B + 2) % kBufs>{});
+        if (t + 3 < ntiles) stage_load(kt_of(t + 3), Buf<(B + 3) % kBufs>{}, e_use);
+      } else {
+        // Tile t + 2 (issued one iteration ago) must have landed before the
+        // barrier after which iteration t + 1 reads it.
+        if (t + 3 < ntiles) wait_vmcnt<4>(); else wait_vmcnt<0>();
+      }
+      lds_barrier();
+    };
+    for (int t = 0; t < ntiles; t += kBufs) {
+      iteration(Buf<0>{}, t, sA, sB);
+      if (t + 1 < ntiles) iteration(Buf<1>{}, t + 1, sB, sA);
+      if (t + 2 < ntiles) iteration(Buf<2>{}, t + 2, sA, sB);
+      if (t + 3 < ntiles) iteration(Buf<3>{}, t + 3, sB, sA);
+    }
   }
 
   // ---- epilogue
-  const float lt = sum_halves(l);
+  const float lt = SHORT ? lt_merged : sum_halves(l);
   if (!valid) return;
   const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
   const int64_t orow_id = static_cast<int64_t>(t0 + tok) * a.num_q_heads + head;
@@ -622,13 +790,17 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 
 }  // namespace
 
-hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipStream_t s) {
+hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, bool short_rows, hipStream_t s) {
   const int64_t n = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.num_splits * a.row_tiles;
   if (n <= 0) return hipSuccess;
-  if (kv_fp8) {
-    hipLaunchKernelGGL(attn_mfma_kernel<true>, dim3(static_cast<unsigned>(n)), dim3(NT), 0, s, a);
+  const dim3 grid(static_cast<unsigned>(n));
+  if (short_rows) {
+    if (a.row_tiles != 1) return hipErrorInvalidValue;
+    if (kv_fp8) hipLaunchKernelGGL((attn_mfma_kernel<true, true>), grid, dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((attn_mfma_kernel<false, true>), grid, dim3(NT), 0, s, a);
   } else {
-    hipLaunchKernelGGL(attn_mfma_kernel<false>, dim3(static_cast<unsigned>(n)), dim3(NT), 0, s, a);
+    if (kv_fp8) hipLaunchKernelGGL((attn_mfma_kernel<true, false>), grid, dim3(NT), 0, s, a);
+    else hipLaunchKernelGGL((attn_mfma_kernel<false, false>), grid, dim3(NT), 0, s, a);
   }
   return hipGetLastError();
 }

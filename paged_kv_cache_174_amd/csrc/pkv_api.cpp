@@ -59,6 +59,7 @@ struct SplitPlan {
   int row_tiles;
   int splits;
   int split_len;
+  bool short_rows;  // the short-query kernel (at most kShortRows rows per KV head)
 };
 
 // Number of key splits for the MFMA kernel.  One workgroup occupies a CU, so
@@ -71,6 +72,7 @@ SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, i
                       int max_seq_len, size_t workspace_bytes, bool have_workspace) {
   SplitPlan p{};
   const int group = num_q_heads / num_kv_heads;
+  p.short_rows = static_cast<int64_t>(max_query_len) * group <= kShortRows;
   p.row_tiles = static_cast<int>((static_cast<int64_t>(max_query_len) * group + kMfmaRows - 1) / kMfmaRows);
   const int64_t base = static_cast<int64_t>(num_seqs) * num_kv_heads * p.row_tiles;
   const int cus = cu_count();
@@ -79,6 +81,7 @@ SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, i
   constexpr double kCuFlops = 4.9e12;     // sustained FLOP/s of one CU on this kernel (about half of peak)
   constexpr double kPartialBw = 5.0e12;   // B/s for writing and re-reading the partials
   constexpr double kCombineLaunch = 3e-6; // s
+  constexpr double kShortStep = 1.4e-6;   // s per four-tile step of the short-query kernel
   // A split's block-table slice is staged in LDS, which bounds its length.
   const int min_splits = static_cast<int>((static_cast<int64_t>(max_seq_len) + kMaxSplitKeys - 1) / kMaxSplitKeys);
   int best = min_splits;
@@ -86,7 +89,9 @@ SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, i
   for (int sp = min_splits; sp <= std::max(min_splits, std::min(kMaxSplits, max_by_len)); ++sp) {
     if (sp > 1 && (!have_workspace || workspace_bytes < static_cast<size_t>(per_split_bytes) * sp)) break;
     const int64_t keys = ((max_seq_len + sp - 1) / sp + kMfmaKeyTile - 1) / kMfmaKeyTile * kMfmaKeyTile;
-    const double wg_time = static_cast<double>(kMfmaRows) * keys * 128 * 4 / kCuFlops;
+    // The short-query kernel takes four key tiles per step (one per key group).
+    const double wg_time = p.short_rows ? std::ceil(keys / (4.0 * kMfmaKeyTile)) * kShortStep
+                                        : static_cast<double>(kMfmaRows) * keys * 128 * 4 / kCuFlops;
     const double rounds = std::ceil(static_cast<double>(base) * sp / cus);
     double t = rounds * wg_time;
     if (sp > 1) t += 2.0 * per_split_bytes * sp / kPartialBw + kCombineLaunch;
@@ -259,7 +264,7 @@ int paged_attn_impl(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_
     a.ws_ml = a.ws_o + static_cast<int64_t>(p.splits) * rows * 128;
   }
   if (phases & kPhaseMain) {
-    if (hipError_t e = launch_attn_mfma(a, pools->dtype == PKV_FP8_E4M3, st); e != hipSuccess)
+    if (hipError_t e = launch_attn_mfma(a, pools->dtype == PKV_FP8_E4M3, p.short_rows, st); e != hipSuccess)
       return fail(PKV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
   }
   if ((phases & kPhaseMerge) && p.splits > 1) {

@@ -81,7 +81,11 @@ constexpr int kMaxSplits = 16;
 constexpr int kTableSlice = 4096;
 constexpr int kMaxSplitKeys = (kTableSlice - 1) * 16;
 
-hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, hipStream_t s);
+// Rows (query tokens x query heads of one KV head) up to which the short-query
+// kernel runs: two 32-row blocks, the keys split four ways inside the workgroup.
+constexpr int kShortRows = 64;
+// short_rows: every sequence has at most kShortRows rows per KV head (row_tiles == 1).
+hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, bool short_rows, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int max_query_len, hipStream_t s);
 

@@ -68,6 +68,15 @@ SMALL = [
     # ones span several splits (merged by the last split to finish).
     small_variant(CONFIGS["piecewise_gqa_bf16"], name="causal_long_split_bf16", num_q_heads=2, num_kv_heads=2,
                   history_lens=(0,), query_lens=(1200,), full_spans=((),)),
+    # Short query chunks (at most 64 rows per KV head): the kernel that splits
+    # the keys four ways inside the workgroup and merges them in LDS.
+    small_variant(CONFIGS["varlen_fp8"], name="short_fp8_gqa", num_q_heads=8, num_kv_heads=2,
+                  history_lens=(3000, 700, 90, 5000), query_lens=(16, 16, 3, 16), sink_tokens=(0,) * 4,
+                  window_tokens=(1 << 30,) * 4, full_spans=(None,) * 4),
+    small_variant(CONFIGS["frame_bf16"], name="short_window_bf16", num_q_heads=4, num_kv_heads=2,
+                  history_lens=(1000, 37), query_lens=(32, 7), sink_tokens=(300, 0), window_tokens=(600, 1 << 30)),
+    small_variant(CONFIGS["piecewise_gqa_bf16"], name="short_piecewise_bf16", num_q_heads=2, num_kv_heads=2,
+                  history_lens=(200,), query_lens=(60,), full_spans=(((210, 240),),)),
     small_variant(CONFIGS["piecewise_gqa_bf16"], name="causal_hist_split_bf16", num_q_heads=4, num_kv_heads=2,
                   history_lens=(3000, 100), query_lens=(600, 700), full_spans=((), ((100, 500),)), sink_tokens=(0, 0), window_tokens=(1 << 30,) * 2),
 ]
@@ -133,6 +142,24 @@ def test_varlen_fp8_full_size_sampled_rows():
     seqs = sorted({long_q, short_q, int(np.argmin(s))})
     rows = _sample_rows(geom, np.random.default_rng(1), per_seq=12, seqs=seqs)
     heads = [0, 3, 4, 31]
+    _, _, _, ref = H.run_layer(wl, li=li, rows=rows, heads=heads, seqs=seqs)
+    _check(geom, out, ref, rows=rows, heads=heads)
+
+
+def test_varlen_fp8_short_queries_full_size():
+    """The KV-bound half of the varlen batch (query length 16, 32/8 heads, up to
+    32k keys) through the short-query kernel: every row of the longest and the
+    shortest sequence on four heads."""
+    geom = CONFIGS["varlen_fp8_q16"]
+    wl = make_workload(geom, device="cuda")
+    li = wl.layer(0)
+    G.say("attn full", geom.name)
+    plan, _, _, out = G.run(wl, li=li)
+    s = np.asarray(plan.kv_lens)
+    seqs = sorted({int(np.argmax(s)), int(np.argmin(s))})
+    qsl = np.concatenate([[0], np.cumsum(geom.query_lens)])
+    rows = [r for b in seqs for r in range(int(qsl[b]), int(qsl[b + 1]))]
+    heads = [0, 5, 17, 31]
     _, _, _, ref = H.run_layer(wl, li=li, rows=rows, heads=heads, seqs=seqs)
     _check(geom, out, ref, rows=rows, heads=heads)
 
