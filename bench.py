@@ -325,7 +325,7 @@ def run_kv_bound(args):
     gbps = abytes / (ms * 1e-3) / 1e9
     return {
         "workload": geom.name,
-        "kernel": "attn_mfma_kernel<fp8>",
+        "kernel": "attn_mfma_kernel<fp8, short rows>",
         "bound": "hbm",
         "achieved": round(gbps, 1),
         "peak": PEAK_HBM_GBPS,
@@ -438,7 +438,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(r["achieved_tflops"] / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "attn_mfma_kernel",
+            "kernel": "attn_mfma_kernel<bf16>",
             "flop_per_launch": r["flops"],
             "avg_launch_ms": round(r["main_ms"], 5),
         },
