@@ -164,10 +164,10 @@ def run_bench(args, geom):
             P.pkv_paged_write(li.k_cur, li.v_cur, plan.slot_mapping, pools)
             if ev is not None:
                 ev[4 * i + 1].record(stream)
-            P.pkv_paged_attn_main(*attn_args(li, pools), out=out, workspace=ws)
+            P.pkv_paged_attn_main(*attn_args(li, pools), out=out, workspace=ws, seq_order=plan.seq_order)
             if ev is not None:
                 ev[4 * i + 2].record(stream)
-            P.pkv_paged_attn_merge(*attn_args(li, pools), out=out, workspace=ws)
+            P.pkv_paged_attn_merge(*attn_args(li, pools), out=out, workspace=ws, seq_order=plan.seq_order)
             if ev is not None:
                 ev[4 * i + 3].record(stream)
 
@@ -221,7 +221,7 @@ def run_bench(args, geom):
     def staged_attn():
         P.pkv_paged_attn(li.q, staged, ident, plan.query_start_loc, plan.seq_lens, plan.segments,
                          plan.segment_start_loc, scale, plan.max_query_len, plan.max_seq_len, out=out,
-                         workspace=ws)
+                         workspace=ws, seq_order=plan.seq_order)
 
     if args.copy_calibration:
         copy_calibration(pools)
@@ -300,7 +300,7 @@ def run_kv_bound(args):
     def launch(li, pools, out):
         args_ = (li.q, pools, plan.block_table, plan.query_start_loc, plan.seq_lens, plan.segments,
                  plan.segment_start_loc, scale, plan.max_query_len, plan.max_seq_len)
-        P.pkv_paged_attn_main(*args_, out=out, workspace=ws)
+        P.pkv_paged_attn_main(*args_, out=out, workspace=ws, seq_order=plan.seq_order)
 
     for _ in range(max(args.warmup, 1)):
         for layer in layers:
@@ -316,7 +316,7 @@ def run_kv_bound(args):
             ev[k + 1].record(stream)
             P.pkv_paged_attn_merge(layer[0].q, layer[1], plan.block_table, plan.query_start_loc, plan.seq_lens,
                                    plan.segments, plan.segment_start_loc, scale, plan.max_query_len,
-                                   plan.max_seq_len, out=layer[2], workspace=ws)
+                                   plan.max_seq_len, out=layer[2], workspace=ws, seq_order=plan.seq_order)
             k += 2
     torch.cuda.synchronize()
     ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 2)]))

@@ -141,6 +141,10 @@ int pkv_gather(const pkv_pools* pools, const int32_t* block_ids, int32_t n_block
  *   max_seq_len       host bound on every seq_lens[b] (a capacity, P1 build_block_table)
  *   segments          device int32 [num_segments][4]
  *   segment_start_loc device int32 [num_seqs + 1] (CSR into segments)
+ *   seq_order         device int32 [num_seqs], a permutation of 0 .. num_seqs - 1, or NULL:
+ *                     the order in which the sequences' work is handed to the GPU.
+ *                     Longest first (the ForwardPlan's choice) lets short sequences fill
+ *                     in behind long ones; the result does not depend on it.
  *   out               device, same shape and dtype as q
  *   workspace         device scratch for split-key partial results, or NULL;
  *                     pkv_paged_attn_workspace_size() gives the size that lets the
@@ -154,7 +158,7 @@ int pkv_paged_attn(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t
                    const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
                    const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
                    int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
-                   const int32_t* segment_start_loc, float softmax_scale, void* out, void* workspace,
+                   const int32_t* segment_start_loc, const int32_t* seq_order, float softmax_scale, void* out, void* workspace,
                    size_t workspace_bytes, void* stream);
 
 /*
@@ -172,13 +176,13 @@ int pkv_paged_attn_main(const void* q, int32_t q_dtype, int64_t num_q_tokens, in
                         const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
                         const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
                         int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
-                        const int32_t* segment_start_loc, float softmax_scale, void* out, void* workspace,
+                        const int32_t* segment_start_loc, const int32_t* seq_order, float softmax_scale, void* out, void* workspace,
                         size_t workspace_bytes, void* stream);
 int pkv_paged_attn_merge(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads,
                          const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
                          const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
                          int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
-                         const int32_t* segment_start_loc, float softmax_scale, void* out, void* workspace,
+                         const int32_t* segment_start_loc, const int32_t* seq_order, float softmax_scale, void* out, void* workspace,
                          size_t workspace_bytes, void* stream);
 
 /* Workspace bytes pkv_paged_attn would like for these sizes on the current device. */

@@ -64,7 +64,7 @@ _PI32 = ctypes.POINTER(ctypes.c_int32)
 _PI64 = ctypes.POINTER(ctypes.c_int64)
 _PPOOLS = ctypes.POINTER(_Pools)
 
-_ATTN_ARGS = [_P, _I32, _I64, _I32, _PPOOLS, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _F32, _P, _P, _SZ, _P]
+_ATTN_ARGS = [_P, _I32, _I64, _I32, _PPOOLS, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P, _F32, _P, _P, _SZ, _P]
 
 _SIGNATURES = {
     "pkv_paged_write": (ctypes.c_int, [_P, _P, _I32, _I64, _P, _PPOOLS, _P]),
@@ -243,8 +243,12 @@ def pkv_paged_attn(
     out: torch.Tensor | None = None,
     workspace: torch.Tensor | None = None,
     stream=None,
+    seq_order: torch.Tensor | None = None,
     _entry: str = "pkv_paged_attn",
 ) -> torch.Tensor:
+    """Paged attention (see include/pkv.h).  ``seq_order`` (int32 [num_seqs], a
+    permutation) is the order the sequences' work is dispatched in, e.g.
+    ForwardPlan.seq_order (longest first); it does not change the result."""
     if q.dim() != 3 or q.shape[2] != pools.head_dim:
         raise ValueError("q must be [tokens, num_q_heads, head_dim]")
     if out is None:
@@ -256,6 +260,11 @@ def pkv_paged_attn(
     num_seqs = block_table.shape[0]
     if query_start_loc.numel() != num_seqs + 1 or seq_lens.numel() != num_seqs or segment_start_loc.numel() != num_seqs + 1:
         raise ValueError("query_start_loc, seq_lens and segment_start_loc must match block_table's rows")
+    order_ptr = None
+    if seq_order is not None:
+        if seq_order.numel() != num_seqs:
+            raise ValueError("seq_order must hold one entry per sequence")
+        order_ptr = _dev(seq_order, "seq_order", torch.int32)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
@@ -276,6 +285,7 @@ def pkv_paged_attn(
             int(max_seq_len),
             _dev(segments, "segments", torch.int32),
             _dev(segment_start_loc, "segment_start_loc", torch.int32),
+            order_ptr,
             float(softmax_scale),
             _dev(out, "out"),
             ws_ptr,

@@ -61,6 +61,8 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 typedef short v4i16 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) void* lds_ptr;
 typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
+typedef int v2i32 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) v2i32* lds_v2i32_ptr;
 
 constexpr int D = 128;
 constexpr int KT = kMfmaKeyTile;  // keys per tile
@@ -220,18 +222,23 @@ attn_mfma_kernel(AttnArgs a) {
   const int l32 = lane & 31;
   const int h2 = lane >> 5;
 
-  // ---- work item: XCD-aware remap so that workgroups sharing K/V (same
-  // sequence, KV head, key split) are dispatched to the same XCD and its L2.
-  const uint32_t n = gridDim.x;
-  const uint32_t id = blockIdx.x;
-  const uint32_t xcd = id & 7u, k8 = id >> 3, q8 = n >> 3, r8 = n & 7u;
-  const uint32_t logical = (xcd < r8) ? xcd * (q8 + 1) + k8 : r8 * (q8 + 1) + (xcd - r8) * q8 + k8;
-  const int rt = static_cast<int>(logical % static_cast<uint32_t>(a.row_tiles));
-  uint32_t rest = logical / static_cast<uint32_t>(a.row_tiles);
-  const int z = static_cast<int>(rest % static_cast<uint32_t>(a.num_splits));
-  rest /= static_cast<uint32_t>(a.num_splits);
-  const int hk = static_cast<int>(rest % static_cast<uint32_t>(a.num_kv_heads));
-  const int b = static_cast<int>(rest / static_cast<uint32_t>(a.num_kv_heads));
+  // ---- work item.  Workgroups are dealt to the 8 XCDs round-robin by id
+  // (id % 8), each XCD taking its share in id order.  A group is one
+  // (sequence, KV head); all of a group's workgroups (key splits x row tiles)
+  // go to one XCD, so they share its L2 for the group's K/V, and group g
+  // (counted in dispatch order: sequences as seq_order lists them, KV heads
+  // fastest) goes to XCD g % 8, which spreads every sequence over the XCDs
+  // and keeps their loads balanced.
+  const uint32_t xcd = blockIdx.x & 7u, pos = blockIdx.x >> 3;
+  const uint32_t per_group = static_cast<uint32_t>(a.num_splits) * static_cast<uint32_t>(a.row_tiles);
+  const uint32_t grp = xcd + 8u * (pos / per_group);
+  if (grp >= static_cast<uint32_t>(a.num_seqs) * static_cast<uint32_t>(a.num_kv_heads)) return;
+  const uint32_t item = pos % per_group;
+  const int rt = static_cast<int>(item % static_cast<uint32_t>(a.row_tiles));
+  const int z = static_cast<int>(item / static_cast<uint32_t>(a.row_tiles));
+  const int hk = static_cast<int>(grp % static_cast<uint32_t>(a.num_kv_heads));
+  const int b_pos = static_cast<int>(grp / static_cast<uint32_t>(a.num_kv_heads));
+  const int b = a.seq_order ? a.seq_order[b_pos] : b_pos;
 
   const int G = a.group;
   const int t0 = a.qsl[b];
@@ -266,14 +273,18 @@ attn_mfma_kernel(AttnArgs a) {
 
   // Q^T fragments for S^T = K Q^T: lane holds 8 consecutive head-dim values
   // [16 t + 8 h2, +8) of its query row for each of the 8 k-steps.
+  // (fp8 pools: step t takes head-dim piece 4 (t / 2) + 2 h2 + t % 2 of 8
+  // values instead, so that one 16-byte LDS read of K feeds two steps.)
+  constexpr bool kF8Lds = FP8;  // fp8 K/V tiles are kept as fp8 in LDS
   bf16x8 qf[8];
   {
     const __bf16* qr = static_cast<const __bf16*>(a.q) +
-                       (static_cast<int64_t>(t0 + tok) * a.num_q_heads + head) * D + 8 * h2;
+                       (static_cast<int64_t>(t0 + tok) * a.num_q_heads + head) * D;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
+      const int piece = kF8Lds ? 4 * (t >> 1) + 2 * h2 + (t & 1) : 2 * t + h2;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (valid) v = *reinterpret_cast<const u32x4*>(qr + 16 * t);
+      if (valid) v = *reinterpret_cast<const u32x4*>(qr + 8 * piece);
       qf[t] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -293,9 +304,9 @@ attn_mfma_kernel(AttnArgs a) {
   // and past the slice every row of the workgroup masks them anyway.
   const int kv_lim = min(s, blk_hi * 16);
 
-  // ---- staging geometry: wave w stages tile rows [8 w, 8 w + 8) of both the
-  // K and the V tile, four rows (one 1 KB direct load) per step; lane i takes
-  // row 8 w + 4 step + i / 16 and LDS chunk position i % 16.
+  // ---- staging geometry (bf16): wave w stages tile rows [8 w, 8 w + 8) of
+  // both the K and the V tile, four rows (one 1 KB direct load) per step; lane
+  // i takes row 8 w + 4 step + i / 16 and LDS chunk position i % 16.
   const int64_t row_bytes = static_cast<int64_t>(a.num_kv_heads) * D * ELSZ;
   const int64_t block_bytes = 16 * row_bytes;
   const uint8_t* kpool = static_cast<const uint8_t*>(a.kpool) + static_cast<int64_t>(hk) * D * ELSZ;
@@ -311,14 +322,12 @@ attn_mfma_kernel(AttnArgs a) {
   }
   const uint8_t* zero_row = reinterpret_cast<const uint8_t*>(g_zero_row) + 16 * st_pos;
 
-  // Issue the loads of the tile at key kt into LDS buffer buf (bf16: direct
-  // to LDS; fp8: into registers, see fp8_store).
-  u32x2 f8k[2], f8v[2];
   // Block-table entry of the 16 keys this wave stages for the tile at key kt.
   auto stage_entry = [&](int kt) {
     const int blk = (kt >> 4) + (w >> 1);
     return (blk < blk_hi) ? tbl[blk - blk_lo] : 0;
   };
+  // bf16: direct loads of the tile at key kt into LDS buffer buf.
   auto stage_load = [&](int kt, auto bufc, int e) {
     constexpr int B = decltype(bufc)::value;
     // The wave's eight rows lie in one 16-key block: its base address is
@@ -330,33 +339,13 @@ attn_mfma_kernel(AttnArgs a) {
     for (int st = 0; st < 2; ++st) {
       const int dst = (8 * w + 4 * st) * kRowBytes;
       if (kt + 8 * w + 4 * st + 4 <= kv_lim) {  // all four rows exist (uniform)
-        if constexpr (FP8) {
-          f8k[st] = *reinterpret_cast<const u32x2*>(kb + k_src_off[st]);
-          f8v[st] = *reinterpret_cast<const u32x2*>(vb + v_src_off[st]);
-        } else {
-          dma16(kb, static_cast<uint32_t>(k_src_off[st]), kbuf<B>() + dst);
-          dma16(vb, static_cast<uint32_t>(v_src_off[st]), vbuf<B>() + dst);
-        }
+        dma16(kb, static_cast<uint32_t>(k_src_off[st]), kbuf<B>() + dst);
+        dma16(vb, static_cast<uint32_t>(v_src_off[st]), vbuf<B>() + dst);
       } else {  // the tile at the end of the staged keys: rows past kv_lim read zeros
         const bool ok = kt + st_row[st] < kv_lim;
-        if constexpr (FP8) {
-          f8k[st] = ok ? *reinterpret_cast<const u32x2*>(kb + k_src_off[st]) : u32x2{0u, 0u};
-          f8v[st] = ok ? *reinterpret_cast<const u32x2*>(vb + v_src_off[st]) : u32x2{0u, 0u};
-        } else {
-          dma16(ok ? kb + k_src_off[st] : zero_row, kbuf<B>() + dst);
-          dma16(ok ? vb + v_src_off[st] : zero_row, vbuf<B>() + dst);
-        }
+        dma16(ok ? kb + k_src_off[st] : zero_row, kbuf<B>() + dst);
+        dma16(ok ? vb + v_src_off[st] : zero_row, vbuf<B>() + dst);
       }
-    }
-  };
-  // fp8 only: widen the registers of the last stage_load into LDS buffer buf.
-  auto fp8_store = [&](auto bufc) {
-    constexpr int B = decltype(bufc)::value;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int dst = st_row[st] * kRowBytes + 16 * st_pos;
-      *reinterpret_cast<u32x4*>(kbuf<B>() + dst) = e4m3x8_to_bf16x8(f8k[st]);
-      *reinterpret_cast<u32x4*>(vbuf<B>() + dst) = e4m3x8_to_bf16x8(f8v[st]);
     }
   };
 
@@ -488,26 +477,159 @@ attn_mfma_kernel(AttnArgs a) {
         }
   };
 
-  if constexpr (SHORT) {
-    // ---- iteration i: each wave multiplies tile 4 i + kg from buffer kg
-    // while the workgroup loads tiles 4 i + 4 .. 4 i + 7 into registers; after
-    // a barrier they are written (fp8 widened) into buffers 0..3.
-    // Register staging, 16 bytes per lane per load.  bf16: lane i of wave w
-    // holds chunk i % 16 of rows 8 w + 4 st + i / 16 (st = 0, 1), at the
-    // positions stage_load uses.  fp8: one load per tile covers the wave's
-    // eight rows, lane i holding codes [16 p, 16 p + 16) (p = i % 8) of row
-    // 8 w + i / 8, i.e. chunks 2 p and 2 p + 1 once widened.
-    constexpr int kLoads = FP8 ? 1 : 2;  // loads per tile per lane, for K and for V
-    // fp8 tiles are loaded two steps ahead (two register sets); bf16 tiles,
-    // twice the bytes, one step ahead.
-    constexpr int kSets = FP8 ? 2 : 1;
-    u32x4 rk[kSets][4][kLoads], rv[kSets][4][kLoads];
-    const int f8_row = 8 * w + (lane >> 3), f8_pair = lane & 7;
-    const int f8_src = (f8_row & 15) * static_cast<int>(row_bytes) + 16 * f8_pair;
-    const int ntiles = (k_end - k_begin + KT - 1) / KT;
-    auto kt_of = [&](int t) { return k_begin + t * KT; };
-    auto load4 = [&](auto setc, int t_first) {
-      constexpr int S = decltype(setc)::value;
+  // ---- fp8 pools: tiles stay fp8 in LDS (8 KB of K and 8 KB of V per tile,
+  // eight tiles in the 128 KB of tile buffers), filled by direct loads, and
+  // are widened to bf16 as the MFMA operands are read.
+  //   K: 128-byte rows, 16-byte chunk c of row r at position c ^ ((r / 2) % 8);
+  //      lane (l32, h2) reads chunk 2 m + h2 of its row, the head-dim pieces
+  //      of steps 2 m and 2 m + 1 (the order Q was loaded in).
+  //   V: 128-byte rows, chunk c of row r at c ^ 2 (((r / 2) % 2) | ((r / 4) % 2 * 2));
+  //      read with ds_read_b64_tr_b8: in each 16-lane group g, lane 8 hb + c
+  //      receives byte c of the 8-byte pieces that lanes 2 j + hb (j = 0..7)
+  //      name.  Lane 16 g + 2 j + hb names the row holding key
+  //      8 (j / 4) + 4 (g / 2) + j % 4 of the 16-key chunk (the key order of
+  //      P's MFMA operand) and head-dim piece 4 db + 2 (g % 2) + hb.
+  // Both layouts are free of bank conflicts for these reads.
+  uint8_t* const f8k_base = &s_k[0][0];
+  uint8_t* const f8v_base = &s_v[0][0];
+  constexpr int kF8Tile = 64 * D;  // bytes of one fp8 K (or V) tile
+  auto f8_swz_k = [](int r) { return (r >> 1) & 7; };
+  auto f8_swz_v = [](int r) { return 2 * (((r >> 1) & 1) | ((r >> 2) & 2)); };
+  // direct loads: wave w fills rows 8 w .. 8 w + 7 of each tile, lane i
+  // position i % 8 of row 8 w + i / 8
+  const int dl_row = 8 * w + (lane >> 3), dl_pos = lane & 7;
+  const uint32_t dl_k = static_cast<uint32_t>((dl_row & 15) * row_bytes + 16 * (dl_pos ^ f8_swz_k(dl_row)));
+  const uint32_t dl_v = static_cast<uint32_t>((dl_row & 15) * row_bytes + 16 * (dl_pos ^ f8_swz_v(dl_row)));
+  const uint8_t* f8_zero = reinterpret_cast<const uint8_t*>(g_zero_row) + 16 * dl_pos;
+  // K operand addresses (buffer offset added per tile): chunk 2 m + h2 of row l32 (+ 32 kb)
+  uint32_t k8_rd[4];
+#pragma unroll
+  for (int mm = 0; mm < 4; ++mm) k8_rd[mm] = lds_addr(f8k_base + l32 * D + 16 * ((2 * mm + h2) ^ f8_swz_k(l32)));
+  uint32_t v8_rd[4];
+  {
+    const int g = lane >> 4, mpos = lane & 15, j = mpos >> 1, hb = mpos & 1;
+    const int row = 8 * (j >> 2) + 4 * (g >> 1) + (j & 3);
+    const int sq = f8_swz_v(row) >> 1;  // swizzle in units of 4 pieces
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+      v8_rd[db] = lds_addr(f8v_base + row * D + 32 * (db ^ sq) + 8 * (2 * (g & 1) + hb));
+  }
+  // Direct loads of tile t (block-table entry e) into fp8 buffer buf: wave w
+  // fills rows 8 w .. 8 w + 7; rows past kv_lim read zeros.
+  auto issue1 = [&](int buf, int t, int e) {
+    const int kt = k_begin + t * KT;
+    const int64_t boff = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(e)) * block_bytes;
+    uint8_t* kdst = f8k_base + buf * kF8Tile + 8 * w * D;
+    uint8_t* vdst = f8v_base + buf * kF8Tile + 8 * w * D;
+    if (kt + 8 * w + 8 <= kv_lim) {  // all eight rows exist (uniform)
+      dma16(kpool + boff, dl_k, kdst);
+      dma16(vpool + boff, dl_v, vdst);
+    } else {
+      const bool ok = kt + dl_row < kv_lim;
+      dma16(ok ? kpool + boff + dl_k : f8_zero, kdst);
+      dma16(ok ? vpool + boff + dl_v : f8_zero, vdst);
+    }
+  };
+  auto qk8 = [&](int buf, f32x16 (&sacc)[2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) sacc[kb][r] = 0.f;
+#pragma unroll
+    for (int mm = 0; mm < 4; ++mm)
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        const u32x4 c = *lds_at<u32x4>(k8_rd[mm] + buf * kF8Tile + kb * 32 * D);
+        const bf16x8 k0 = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(u32x2{c[0], c[1]}));
+        const bf16x8 k1 = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(u32x2{c[2], c[3]}));
+        sacc[kb] = mfma(k0, qf[2 * mm], sacc[kb]);
+        sacc[kb] = mfma(k1, qf[2 * mm + 1], sacc[kb]);
+      }
+  };
+  auto pv8 = [&](int buf, const bf16x8 (&pb)[2][2]) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int k16 = 0; k16 < 2; ++k16)
+#pragma unroll
+        for (int db = 0; db < 4; ++db) {
+          const uint32_t addr = v8_rd[db] + buf * kF8Tile + (32 * kb + 16 * k16) * D;
+          const v2i32 c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32_ptr)(addr));
+          const bf16x8 va = __builtin_bit_cast(
+              bf16x8, e4m3x8_to_bf16x8(u32x2{static_cast<uint32_t>(c[0]), static_cast<uint32_t>(c[1])}));
+          o[db] = mfma(va, pb[kb][k16], o[db]);
+        }
+  };
+  const int ntiles = (k_end - k_begin + KT - 1) / KT;
+  auto kt_of = [&](int t) { return k_begin + t * KT; };
+
+  if constexpr (kF8Lds && SHORT) {
+    // ---- fp8 short path: four tiles per step, one per key group, loaded one
+    // step ahead into the other half of the eight fp8 buffers.
+    // Direct loads of tiles t_first + j0, t_first + j0 + 1 into buffers
+    // 4 set + j0, 4 set + j0 + 1.
+    auto issue2 = [&](int set, int t_first, int j0) {
+      int e[2];
+#pragma unroll
+      for (int j = 0; j < 2; ++j) e[j] = (t_first + j0 + j < ntiles) ? stage_entry(kt_of(t_first + j0 + j)) : 0;
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        if (t_first + j0 + j >= ntiles) break;
+        issue1(4 * set + j0 + j, t_first + j0 + j, e[j]);
+      }
+    };
+    // Step i computes from buffers 4 (i % 2) ..  The loads of step i + 2 go
+    // into the same buffers once every wave has left step i: tiles 0, 1 of it
+    // right after the barrier closing step i, tiles 2, 3 after the QK products
+    // of step i + 1 (issuing all eight loads at once would stall every wave's
+    // instruction stream on the vector-memory queue at the same moment).
+    issue2(0, 0, 0);
+    issue2(0, 0, 2);
+    issue2(1, 4, 0);
+    issue2(1, 4, 2);
+    // Step 0 has landed once at most the second group's loads (two per tile
+    // of tiles 4 .. 7) are outstanding.
+    switch (min(4, max(0, ntiles - 4))) {
+      case 4: wait_vmcnt<8>(); break;
+      case 3: wait_vmcnt<6>(); break;
+      case 2: wait_vmcnt<4>(); break;
+      case 1: wait_vmcnt<2>(); break;
+      default: wait_vmcnt<0>(); break;
+    }
+    lds_barrier();
+    f32x16 sacc[2];
+    int pend = -1;  // set whose tiles 2, 3 of step t4 / 4 + 1 are still to be issued
+    for (int t4 = 0, set = 0; t4 < ntiles; t4 += 4, set ^= 1) {
+      const int t = t4 + kg;
+      if (t < ntiles && kt_of(t) < wave_kmax) {
+        qk8(4 * set + kg, sacc);
+        if (pend >= 0) {
+          issue2(pend, t4 + 4, 2);
+          pend = -1;
+        }
+        mask_and_rescale(kt_of(t), sacc);
+        bf16x8 pb[2][2];
+        probs(sacc, pb);
+        pv8(4 * set + kg, pb);
+      }
+      if (pend >= 0) {
+        issue2(pend, t4 + 4, 2);
+        pend = -1;
+      }
+      wait_vmcnt<0>();  // this wave's share of step i + 1 has landed
+      lds_barrier();
+      if (t4 + 8 < ntiles) {
+        issue2(set, t4 + 8, 0);
+        pend = set;
+      }
+    }
+  } else if constexpr (SHORT) {
+    // ---- bf16 short path: each wave multiplies tile 4 i + kg from buffer kg
+    // while the workgroup loads tiles 4 i + 4 .. 4 i + 7 into registers (lane
+    // i of wave w: chunk i % 16 of rows 8 w + 4 st + i / 16, at the positions
+    // stage_load uses); after a barrier they are written into buffers 0..3.
+    u32x4 rk[4][2], rv[4][2];
+    auto load4 = [&](int t_first) {
       // All four block-table entries first: one LDS round trip, not four.
       int e[4];
 #pragma unroll
@@ -519,51 +641,32 @@ attn_mfma_kernel(AttnArgs a) {
         const int kt = kt_of(t);
         const int64_t boff = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(e[j])) * block_bytes;
         const u32x4 zero = {0u, 0u, 0u, 0u};
-        if constexpr (FP8) {
-          const bool ok = kt + f8_row < kv_lim;
-          rk[S][j][0] = ok ? *reinterpret_cast<const u32x4*>(kpool + boff + f8_src) : zero;
-          rv[S][j][0] = ok ? *reinterpret_cast<const u32x4*>(vpool + boff + f8_src) : zero;
-        } else {
 #pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const bool ok = kt + st_row[st] < kv_lim;
-            rk[S][j][st] = ok ? *reinterpret_cast<const u32x4*>(kpool + boff + k_src_off[st]) : zero;
-            rv[S][j][st] = ok ? *reinterpret_cast<const u32x4*>(vpool + boff + v_src_off[st]) : zero;
-          }
+        for (int st = 0; st < 2; ++st) {
+          const bool ok = kt + st_row[st] < kv_lim;
+          rk[j][st] = ok ? *reinterpret_cast<const u32x4*>(kpool + boff + k_src_off[st]) : zero;
+          rv[j][st] = ok ? *reinterpret_cast<const u32x4*>(vpool + boff + v_src_off[st]) : zero;
         }
       }
     };
-    auto store4 = [&](auto setc, int t_first) {
-      constexpr int S = decltype(setc)::value;
+    auto store4 = [&](int t_first) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         if (t_first + j >= ntiles) break;
-        if constexpr (FP8) {
-          const int row = f8_row * kRowBytes;
-          const u32x4 klo = e4m3x8_to_bf16x8(u32x2{rk[S][j][0][0], rk[S][j][0][1]});
-          const u32x4 khi = e4m3x8_to_bf16x8(u32x2{rk[S][j][0][2], rk[S][j][0][3]});
-          const u32x4 vlo = e4m3x8_to_bf16x8(u32x2{rv[S][j][0][0], rv[S][j][0][1]});
-          const u32x4 vhi = e4m3x8_to_bf16x8(u32x2{rv[S][j][0][2], rv[S][j][0][3]});
-          *reinterpret_cast<u32x4*>(s_k[j] + row + 16 * ((2 * f8_pair) ^ k_swz(f8_row))) = klo;
-          *reinterpret_cast<u32x4*>(s_k[j] + row + 16 * ((2 * f8_pair + 1) ^ k_swz(f8_row))) = khi;
-          *reinterpret_cast<u32x4*>(s_v[j] + row + 16 * ((2 * f8_pair) ^ v_swz(f8_row))) = vlo;
-          *reinterpret_cast<u32x4*>(s_v[j] + row + 16 * ((2 * f8_pair + 1) ^ v_swz(f8_row))) = vhi;
-        } else {
 #pragma unroll
-          for (int st = 0; st < 2; ++st) {
-            const int dst = st_row[st] * kRowBytes + 16 * st_pos;
-            *reinterpret_cast<u32x4*>(s_k[j] + dst) = rk[S][j][st];
-            *reinterpret_cast<u32x4*>(s_v[j] + dst) = rv[S][j][st];
-          }
+        for (int st = 0; st < 2; ++st) {
+          const int dst = st_row[st] * kRowBytes + 16 * st_pos;
+          *reinterpret_cast<u32x4*>(s_k[j] + dst) = rk[j][st];
+          *reinterpret_cast<u32x4*>(s_v[j] + dst) = rv[j][st];
         }
       }
     };
+    load4(0);
+    store4(0);
+    lds_barrier();
     f32x16 sacc[2];
-    auto step = [&](auto cur, int t4) {
-      // Loads of the tiles two steps (fp8) or one step (bf16) ahead.
-      constexpr int C = decltype(cur)::value;
-      if constexpr (kSets == 2) load4(std::integral_constant<int, 1 - C>{}, t4 + 8);
-      else load4(std::integral_constant<int, 0>{}, t4 + 4);
+    for (int t4 = 0; t4 < ntiles; t4 += 4) {
+      load4(t4 + 4);
       const int t = t4 + kg;
       if (t < ntiles && kt_of(t) < wave_kmax) {
         qk(Buf<0>{}, sacc);
@@ -573,27 +676,108 @@ attn_mfma_kernel(AttnArgs a) {
         pv(Buf<0>{}, pb);
       }
       lds_barrier();
-      if constexpr (kSets == 2) store4(std::integral_constant<int, C>{}, t4 + 4);
-      else store4(std::integral_constant<int, 0>{}, t4 + 4);
+      store4(t4 + 4);
+      lds_barrier();
+    }
+  } else if constexpr (FP8) {
+    // ---- fp8 long chunks: tile t in fp8 buffer t % 8, loaded seven tiles
+    // ahead.  Iteration t: mask / max of S(t); S(t+1) = K(t+1) Q^T next to the
+    // exponentials of S(t); O += V(t) P(t).  Tile t + 7 goes into buffer
+    // (t - 1) % 8, whose last reader (V(t - 1)) finished before the barrier
+    // closing iteration t - 1.  A wave waits for its own share of tile t + 2
+    // before the barrier after which iteration t + 1 reads it.
+    auto wait_tiles = [&](int outstanding_tiles) {  // two loads per tile and wave
+      switch (outstanding_tiles) {
+        case 5: wait_vmcnt<10>(); break;
+        case 4: wait_vmcnt<8>(); break;
+        case 3: wait_vmcnt<6>(); break;
+        case 2: wait_vmcnt<4>(); break;
+        case 1: wait_vmcnt<2>(); break;
+        default: wait_vmcnt<0>(); break;
+      }
+    };
+#pragma unroll
+    for (int j = 0; j < 7; ++j)
+      if (j < ntiles) issue1(j, j, stage_entry(kt_of(j)));
+    wait_tiles(max(0, min(ntiles, 7) - 2));  // tiles 0 and 1
+    int e_next = stage_entry(kt_of(7));
+    lds_barrier();
+    f32x16 sA[2], sB[2];
+    qk8(0, sA);
+    auto iteration = [&](auto bufc, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+      constexpr int B = decltype(bufc)::value;
+      const int e_use = e_next;
+      e_next = stage_entry(kt_of(t + 8));
+      if (t + 7 < ntiles) issue1((B + 7) % 8, t + 7, e_use);
+      if (kt_of(t) < wave_kmax) {
+        mask_and_rescale(kt_of(t), s_cur);
+        bf16x8 pb[2][2];
+        qk8((B + 1) % 8, s_next);
+        probs(s_cur, pb);
+        pv8(B, pb);
+      }
+      wait_tiles(max(0, min(t + 7, ntiles - 1) - (t + 2)));
       lds_barrier();
     };
-    if constexpr (kSets == 2) {
-      load4(std::integral_constant<int, 0>{}, 0);
-      store4(std::integral_constant<int, 0>{}, 0);
-      load4(std::integral_constant<int, 0>{}, 4);
-      lds_barrier();
-      // Step i keeps tiles 4 i + 4 .. + 7 in set i % 2 and loads 4 i + 8 .. into the other.
-      for (int t4 = 0; t4 < ntiles; t4 += 8) {
-        step(std::integral_constant<int, 0>{}, t4);
-        if (t4 + 4 < ntiles) step(std::integral_constant<int, 1>{}, t4 + 4);
-      }
-    } else {
-      load4(std::integral_constant<int, 0>{}, 0);
-      store4(std::integral_constant<int, 0>{}, 0);
-      lds_barrier();
-      for (int t4 = 0; t4 < ntiles; t4 += 4) step(std::integral_constant<int, 0>{}, t4);
+    for (int t = 0; t < ntiles; t += 8) {
+      iteration(Buf<0>{}, t, sA, sB);
+      if (t + 1 < ntiles) iteration(Buf<1>{}, t + 1, sB, sA);
+      if (t + 2 < ntiles) iteration(Buf<2>{}, t + 2, sA, sB);
+      if (t + 3 < ntiles) iteration(Buf<3>{}, t + 3, sB, sA);
+      if (t + 4 < ntiles) iteration(Buf<4>{}, t + 4, sA, sB);
+      if (t + 5 < ntiles) iteration(Buf<5>{}, t + 5, sB, sA);
+      if (t + 6 < ntiles) iteration(Buf<6>{}, t + 6, sA, sB);
+      if (t + 7 < ntiles) iteration(Buf<7>{}, t + 7, sB, sA);
     }
+  } else {
+    // ---- bf16 long chunks: software pipeline over tiles t = 0 .. n-1 (tile
+    // t: keys k_begin + 64 t, LDS buffer t % 4).  Iteration t: mask / max of
+    // S(t); S(t+1) = K(t+1) Q^T next to the exponentials of S(t);
+    // O += V(t) P(t); the direct loads of tile t + 3 are issued first, into
+    // buffer (t + 3) % 4, which held tile t - 1, whose last reader was
+    // iteration t - 1; the barrier closing iteration t makes tile t + 2
+    // visible to iteration t + 1.  S(t + 1) of the last tile reads a stale
+    // buffer and is never used.
+    stage_load(kt_of(0), Buf<0>{}, stage_entry(kt_of(0)));
+    if (ntiles > 1) stage_load(kt_of(1), Buf<1>{}, stage_entry(kt_of(1)));
+    if (ntiles > 2) {
+      stage_load(kt_of(2), Buf<2>{}, stage_entry(kt_of(2)));
+      wait_vmcnt<4>();
+    } else {
+      wait_vmcnt<0>();
+    }
+    int e_next = stage_entry(kt_of(3));  // entry for the tile staged in iteration 0
+    lds_barrier();
+    f32x16 sA[2], sB[2];
+    qk(Buf<0>{}, sA);
 
+    auto iteration = [&](auto bufc, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+      constexpr int B = decltype(bufc)::value;
+      const int kt = kt_of(t);
+      const int e_use = e_next;
+      e_next = stage_entry(kt_of(t + 4));
+      if (t + 3 < ntiles) stage_load(kt_of(t + 3), Buf<(B + 3) % kBufs>{}, e_use);
+      if (kt < wave_kmax) {
+        mask_and_rescale(kt, s_cur);
+        bf16x8 pb[2][2];
+        qk(Buf<(B + 1) % kBufs>{}, s_next);
+        probs(s_cur, pb);
+        pv(bufc, pb);
+      }
+      // Tile t + 2 (issued one iteration ago) must have landed before the
+      // barrier after which iteration t + 1 reads it.
+      if (t + 3 < ntiles) wait_vmcnt<4>(); else wait_vmcnt<0>();
+      lds_barrier();
+    };
+    for (int t = 0; t < ntiles; t += kBufs) {
+      iteration(Buf<0>{}, t, sA, sB);
+      if (t + 1 < ntiles) iteration(Buf<1>{}, t + 1, sB, sA);
+      if (t + 2 < ntiles) iteration(Buf<2>{}, t + 2, sA, sB);
+      if (t + 3 < ntiles) iteration(Buf<3>{}, t + 3, sB, sA);
+    }
+  }
+
+  if constexpr (SHORT) {
     // ---- merge the four key groups of each row block: common max, then
     // ((kg 0 + kg 2) + (kg 1 + kg 3)) in that order, through LDS.
     float lt_own = sum_halves(l);
@@ -645,71 +829,6 @@ attn_mfma_kernel(AttnArgs a) {
     if (kg != 0) return;
     m = M;
     lt_merged = lt_own;
-  } else {
-    // ---- software pipeline over tiles t = 0 .. n-1 (tile t: keys k_begin + 64 t,
-    // LDS buffer t % 4).  Iteration t: mask / max of S(t); S(t+1) = K(t+1) Q^T
-    // next to the exponentials of S(t); O += V(t) P(t); then the loads of tile
-    // t + 3 are issued (bf16) or tile t + 2 is widened into LDS and tile t + 3
-    // loaded into registers (fp8).  Buffer (t + 3) % 4 held tile t - 1, whose
-    // last reader was iteration t - 1; the barrier closing iteration t makes
-    // tile t + 2 visible to iteration t + 1.  S(t + 1) of the last tile reads a
-    // stale buffer and is never used.
-    const int ntiles = (k_end - k_begin + KT - 1) / KT;
-    auto kt_of = [&](int t) { return k_begin + t * KT; };
-    if constexpr (FP8) {
-      stage_load(kt_of(0), Buf<0>{}, stage_entry(kt_of(0)));
-      fp8_store(Buf<0>{});
-      if (ntiles > 1) { stage_load(kt_of(1), Buf<1>{}, stage_entry(kt_of(1))); fp8_store(Buf<1>{}); }
-      if (ntiles > 2) stage_load(kt_of(2), Buf<2>{}, stage_entry(kt_of(2)));
-    } else {
-      stage_load(kt_of(0), Buf<0>{}, stage_entry(kt_of(0)));
-      if (ntiles > 1) stage_load(kt_of(1), Buf<1>{}, stage_entry(kt_of(1)));
-      if (ntiles > 2) {
-        stage_load(kt_of(2), Buf<2>{}, stage_entry(kt_of(2)));
-        wait_vmcnt<4>();
-      } else {
-        wait_vmcnt<0>();
-      }
-    }
-    int e_next = stage_entry(kt_of(3));  // entry for the tile staged in iteration 0
-    lds_barrier();
-    f32x16 sA[2], sB[2];
-    qk(Buf<0>{}, sA);
-
-    auto iteration = [&](auto bufc, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
-      constexpr int B = decltype(bufc)::value;
-      const int kt = kt_of(t);
-      // Tile t + 3 goes into buffer (t + 3) % 4, free since the barrier that
-      // closed iteration t - 1; bf16 loads are issued first so that they
-      // overlap this iteration's math.
-      const int e_use = e_next;
-      e_next = stage_entry(kt_of(t + 4));
-      if constexpr (!FP8) {
-        if (t + 3 < ntiles) stage_load(kt_of(t + 3), Buf<(B + 3) % kBufs>{}, e_use);
-      }
-      if (kt < wave_kmax) {
-        mask_and_rescale(kt, s_cur);
-        bf16x8 pb[2][2];
-        qk(Buf<(B + 1) % kBufs>{}, s_next);
-        probs(s_cur, pb);
-        pv(bufc, pb);
-      }
-      if constexpr (FP8) {
-        if (t + 2 < ntiles) fp8_store(Buf<(B + 2) % kBufs>{});
-        if (t + 3 < ntiles) stage_load(kt_of(t + 3), Buf<(B + 3) % kBufs>{}, e_use);
-      } else {
-        // Tile t + 2 (issued one iteration ago) must have landed before the
-        // barrier after which iteration t + 1 reads it.
-        if (t + 3 < ntiles) wait_vmcnt<4>(); else wait_vmcnt<0>();
-      }
-      lds_barrier();
-    };
-    for (int t = 0; t < ntiles; t += kBufs) {
-      iteration(Buf<0>{}, t, sA, sB);
-      if (t + 1 < ntiles) iteration(Buf<1>{}, t + 1, sB, sA);
-      if (t + 2 < ntiles) iteration(Buf<2>{}, t + 2, sA, sB);
-      if (t + 3 < ntiles) iteration(Buf<3>{}, t + 3, sB, sA);
-    }
   }
 
   // ---- epilogue
@@ -791,8 +910,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
 }  // namespace
 
 hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, bool short_rows, hipStream_t s) {
-  const int64_t n = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads * a.num_splits * a.row_tiles;
+  // Groups (sequence, KV head) padded to a multiple of the 8 XCDs; see the
+  // work-item mapping at the top of the kernel.
+  const int64_t groups = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads;
+  const int64_t n = (groups + 7) / 8 * 8 * a.num_splits * a.row_tiles;
   if (n <= 0) return hipSuccess;
+  if (n > 0x7fffffff) return hipErrorInvalidValue;
   const dim3 grid(static_cast<unsigned>(n));
   if (short_rows) {
     if (a.row_tiles != 1) return hipErrorInvalidValue;

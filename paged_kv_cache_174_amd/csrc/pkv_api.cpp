@@ -187,8 +187,8 @@ int paged_attn_impl(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_
                     const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
                     const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
                     int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
-                    const int32_t* segment_start_loc, float softmax_scale, void* out, void* workspace,
-                    size_t workspace_bytes, void* stream, unsigned phases) {
+                    const int32_t* segment_start_loc, const int32_t* seq_order, float softmax_scale, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream, unsigned phases) {
   g_error[0] = '\0';
   if (int rc = check_pools(pools)) return rc;
   if (!q || !out || !block_table || !query_start_loc || !seq_lens || !segments || !segment_start_loc)
@@ -220,6 +220,7 @@ int paged_attn_impl(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_
   a.seq_lens = seq_lens;
   a.segments = segments;
   a.seg_loc = segment_start_loc;
+  a.seq_order = seq_order;
   a.num_q_tokens = num_q_tokens;
   a.table_width = table_width;
   a.num_seqs = num_seqs;
@@ -282,12 +283,12 @@ extern "C" {
   const void *q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads, const pkv_pools *pools,          \
       const int32_t *block_table, int32_t table_width, const int32_t *query_start_loc, const int32_t *seq_lens, \
       int32_t num_seqs, int32_t max_query_len, int32_t max_seq_len, const int32_t *segments,                    \
-      const int32_t *segment_start_loc, float softmax_scale, void *out, void *workspace, size_t workspace_bytes, \
-      void *stream
+      const int32_t *segment_start_loc, const int32_t *seq_order, float softmax_scale, void *out, void *workspace, \
+      size_t workspace_bytes, void *stream
 #define PKV_ATTN_ARGS                                                                                       \
   q, q_dtype, num_q_tokens, num_q_heads, pools, block_table, table_width, query_start_loc, seq_lens,         \
-      num_seqs, max_query_len, max_seq_len, segments, segment_start_loc, softmax_scale, out, workspace,      \
-      workspace_bytes, stream
+      num_seqs, max_query_len, max_seq_len, segments, segment_start_loc, seq_order, softmax_scale, out,      \
+      workspace, workspace_bytes, stream
 
 int pkv_paged_attn(PKV_ATTN_PARAMS) { return paged_attn_impl(PKV_ATTN_ARGS, kPhaseMain | kPhaseMerge); }
 int pkv_paged_attn_main(PKV_ATTN_PARAMS) { return paged_attn_impl(PKV_ATTN_ARGS, kPhaseMain); }

@@ -44,6 +44,7 @@ class ForwardPlan:
     seq_lens: torch.Tensor | None = None
     segments: torch.Tensor | None = None
     segment_start_loc: torch.Tensor | None = None
+    seq_order: torch.Tensor | None = None
     slot_mapping: torch.Tensor | None = None
     history_slot_mapping: torch.Tensor | None = None
 
@@ -114,11 +115,21 @@ class ForwardPlan:
         self.seq_lens = up(np.asarray(self.kv_lens, dtype=np.int32))
         self.segments = up(self.segments_host.reshape(-1))
         self.segment_start_loc = up(self.segment_start_host)
+        self.seq_order = up(self.seq_order_host)
         self.slot_mapping = up(self.cur_slots_host)
         self.history_slot_mapping = up(self.hist_slots_host)
         return self
 
+    @property
+    def seq_order_host(self) -> np.ndarray:
+        """Dispatch order for the attention kernel: longest sequence first
+        (ties in index order), so that short sequences fill in behind long ones."""
+        return np.argsort(-np.asarray(self.kv_lens, dtype=np.int64), kind="stable").astype(np.int32)
+
     def validate(self, num_blocks: int) -> None:
+        order = self.seq_order_host
+        if sorted(order.tolist()) != list(range(self.num_seqs)):
+            raise ValueError("seq_order is not a permutation of the sequences")
         L.pkv_validate_metadata_host(
             self.query_start_host,
             np.asarray(self.kv_lens, dtype=np.int32),

@@ -25,6 +25,9 @@ GEOMS = {
     "bf16": small_variant(CONFIGS["piecewise_gqa_bf16"], name="inv_bf16", num_q_heads=6, num_kv_heads=2,
                           history_lens=(200, 57), query_lens=(300, 70), sink_tokens=(0, 0),
                           window_tokens=(1 << 30,) * 2, full_spans=(((250, 330),), None)),
+    "fp8_short": small_variant(CONFIGS["varlen_fp8"], name="inv_fp8_short", num_q_heads=8, num_kv_heads=2,
+                               history_lens=(900, 2100, 250), query_lens=(16, 7, 16), sink_tokens=(0,) * 3,
+                               window_tokens=(1 << 30,) * 3, full_spans=(None,) * 3),
     "fp8": small_variant(CONFIGS["varlen_fp8"], name="inv_fp8", num_q_heads=4, num_kv_heads=2,
                          history_lens=(500, 31), query_lens=(16, 200), sink_tokens=(0, 0),
                          window_tokens=(1 << 30,) * 2, full_spans=(None, None)),
@@ -67,6 +70,27 @@ def test_one_workspace_serves_calls_of_different_shapes():
             out = G.attend(plan, pools, li, geom, workspace=ws)
             torch.cuda.synchronize()
             assert torch.equal(out.view(torch.int16), ref.view(torch.int16)), (geom.name, rep)
+
+
+@pytest.mark.parametrize("kind", ["fp8", "fp8_short", "bf16"])
+def test_dispatch_order_does_not_change_the_result(kind):
+    """The sequences' dispatch order (natural, longest first, reversed) only
+    changes which workgroup runs when: the bits are the same."""
+    import paged_kv_cache_174_amd as P
+
+    geom = GEOMS[kind]
+    wl = make_workload(geom, device="cuda")
+    li = wl.layer(0)
+    G.say("dispatch order", kind)
+    plan, pools, _, ref = G.run(wl, li=li, workspace="auto")
+    ws = G.workspace_for(plan, geom)
+    args = (li.q, pools, plan.block_table, plan.query_start_loc, plan.seq_lens, plan.segments,
+            plan.segment_start_loc, H.softmax_scale(geom.head_dim), plan.max_query_len, plan.max_seq_len)
+    rev = torch.arange(plan.num_seqs - 1, -1, -1, dtype=torch.int32, device="cuda")
+    for order in (None, plan.seq_order, rev):
+        out = P.pkv_paged_attn(*args, workspace=ws, seq_order=order)
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
 
 @pytest.mark.parametrize("kind", list(GEOMS))
