@@ -254,7 +254,20 @@ attn_mfma_kernel(AttnArgs a) {
   const int wg_kmax = row_limit(a.segments, seg0, seg1, gbase + (min(r0 + kMfmaRows, R) - 1) / G);
   const int k_begin = z * a.split_len;
   const int k_end = min(k_begin + a.split_len, wg_kmax);
-  if (k_begin >= k_end) return;
+  if (k_begin >= k_end) {
+    // No key of this split is visible to any row of the tile: its partial is
+    // empty (max -inf, sum 0), which the merge skips.
+    if (a.num_splits > 1 && threadIdx.x < kMfmaRows) {
+      const int row = r0 + static_cast<int>(threadIdx.x);
+      if (row < R) {
+        const int64_t orow = static_cast<int64_t>(t0 + row / G) * a.num_q_heads + hk * G + row % G;
+        const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
+        const f32x2 ml = {-INFINITY, 0.f};
+        *reinterpret_cast<f32x2*>(a.ws_ml + (static_cast<int64_t>(z) * total_rows + orow) * 2) = ml;
+      }
+    }
+    return;
+  }
 
   const int kg = SHORT ? (w >> 1) : 0;  // key group (SHORT)
   const int wr0 = SHORT ? kWaveRows * (w & 1) : r0 + kWaveRows * w;
@@ -865,27 +878,21 @@ attn_mfma_kernel(AttnArgs a) {
 }
 
 // Merges the key splits of a row, in split order: 32 lanes per row, four
-// head-dim values per lane, eight rows per workgroup.
+// head-dim values per lane, eight rows per workgroup.  Every split has a
+// partial for every row (an empty one has max -inf and sum 0 and is skipped),
+// so no sequence or mask metadata has to be looked up first.
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int sub = threadIdx.x & 31;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
   const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
   if (row >= total_rows) return;
-  const int64_t t = row / a.num_q_heads;
-  const int b = seq_of_token(a.qsl, a.num_seqs, t);
-  const int t0 = a.qsl[b];
-  const int q_len = a.qsl[b + 1] - t0;
-  const int g = a.seq_lens[b] - q_len + static_cast<int>(t - t0);
-  const int L = row_limit(a.segments, a.seg_loc[b], a.seg_loc[b + 1], g);
-  const int nz = min(a.num_splits, (L + a.split_len - 1) / a.split_len);
+  const int nz = a.num_splits;
   f32x2 ml[kMaxSplits];
-  f32x4 ov[kMaxSplits];
   float M = -INFINITY;
 #pragma unroll
   for (int zz = 0; zz < kMaxSplits; ++zz) {
     if (zz < nz) {
       ml[zz] = *reinterpret_cast<const f32x2*>(a.ws_ml + (zz * total_rows + row) * 2);
-      ov[zz] = *reinterpret_cast<const f32x4*>(a.ws_o + (zz * total_rows + row) * D + 4 * sub);
       M = fmaxf(M, ml[zz][0]);
     }
   }
@@ -893,11 +900,12 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int zz = 0; zz < kMaxSplits; ++zz) {
-    if (zz < nz) {
+    if (zz < nz && ml[zz][0] != -INFINITY) {  // uniform over the row's 32 lanes
+      const f32x4 ov = *reinterpret_cast<const f32x4*>(a.ws_o + (zz * total_rows + row) * D + 4 * sub);
       const float wz = __builtin_amdgcn_exp2f((ml[zz][0] - M) * a.scale_log2);
       den = fmaf(wz, ml[zz][1], den);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) num[e] = fmaf(wz, ov[zz][e], num[e]);
+      for (int e = 0; e < 4; ++e) num[e] = fmaf(wz, ov[e], num[e]);
     }
   }
   const float inv = a.v_scale / den;

@@ -37,35 +37,38 @@ __device__ __forceinline__ uint32_t f32_to_e4m3(float x) {
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 
-// One 16-byte source vector per thread per step.  blockIdx.y selects K (0) or V (1).
+// One token row per workgroup (grid-striding over rows), one 16-byte source
+// vector per thread; blockIdx.y selects K (0) or V (1).  The row's slot is a
+// wave-uniform load, and no per-element index division is needed.
 template <int MODE>
-__global__ __launch_bounds__(kThreads) void write_kernel(WriteArgs a, int64_t vecs_per_row, int64_t total_vecs) {
+__global__ __launch_bounds__(kThreads) void write_kernel(WriteArgs a, int vecs_per_row) {
   const bool is_v = blockIdx.y != 0;
-  const uint8_t* src = static_cast<const uint8_t*>(is_v ? a.value : a.key);
-  uint8_t* dst = static_cast<uint8_t*>(is_v ? a.vpool : a.kpool);
+  const uint8_t* __restrict__ src = static_cast<const uint8_t*>(is_v ? a.value : a.key);
+  uint8_t* __restrict__ dst = static_cast<uint8_t*>(is_v ? a.vpool : a.kpool);
   const float inv = is_v ? a.v_inv_scale : a.k_inv_scale;
   // bytes of one row in the source and in the pool
-  const int64_t src_row = vecs_per_row * 16;
-  const int64_t dst_row = (MODE == 2) ? vecs_per_row * 8 : src_row;
-  for (int64_t v = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; v < total_vecs;
-       v += static_cast<int64_t>(gridDim.x) * kThreads) {
-    const int64_t t = v / vecs_per_row;
-    const int64_t c = v - t * vecs_per_row;
+  const int64_t src_row = static_cast<int64_t>(vecs_per_row) * 16;
+  const int64_t dst_row = (MODE == 2) ? static_cast<int64_t>(vecs_per_row) * 8 : src_row;
+  for (int64_t t = blockIdx.x; t < a.num_tokens; t += gridDim.x) {
     const int64_t slot = a.slots[t];
-    const u32x4 x = *reinterpret_cast<const u32x4*>(src + t * src_row + c * 16);
-    if (MODE == 2) {
-      uint32_t q[8];
+    const uint8_t* srow = src + t * src_row;
+    uint8_t* drow = dst + slot * dst_row;
+    for (int c = threadIdx.x; c < vecs_per_row; c += kThreads) {
+      const u32x4 x = *reinterpret_cast<const u32x4*>(srow + 16 * c);
+      if (MODE == 2) {
+        uint32_t q[8];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        q[2 * i] = f32_to_e4m3(bf16_lo(x[i]) * inv);
-        q[2 * i + 1] = f32_to_e4m3(bf16_hi(x[i]) * inv);
+        for (int i = 0; i < 4; ++i) {
+          q[2 * i] = f32_to_e4m3(bf16_lo(x[i]) * inv);
+          q[2 * i + 1] = f32_to_e4m3(bf16_hi(x[i]) * inv);
+        }
+        u32x2 y;
+        y[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
+        y[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
+        *reinterpret_cast<u32x2*>(drow + 8 * c) = y;
+      } else {
+        *reinterpret_cast<u32x4*>(drow + 16 * c) = x;
       }
-      u32x2 y;
-      y[0] = q[0] | (q[1] << 8) | (q[2] << 16) | (q[3] << 24);
-      y[1] = q[4] | (q[5] << 8) | (q[6] << 16) | (q[7] << 24);
-      *reinterpret_cast<u32x2*>(dst + slot * dst_row + c * 8) = y;
-    } else {
-      *reinterpret_cast<u32x4*>(dst + slot * dst_row + c * 16) = x;
     }
   }
 }
@@ -89,14 +92,14 @@ hipError_t launch_write(const WriteArgs& a, int mode, hipStream_t s) {
   if (a.num_tokens == 0) return hipSuccess;
   const int64_t elem = (mode == 0) ? 4 : 2;  // source element size
   const int64_t vecs_per_row = a.row_elems * elem / 16;
-  const int64_t total = vecs_per_row * a.num_tokens;
-  int64_t blocks = (total + kThreads - 1) / kThreads;
-  if (blocks > 65535) blocks = 65535;  // grid-stride loop covers the rest
+  if (vecs_per_row <= 0 || vecs_per_row > (1 << 24)) return hipErrorInvalidValue;
+  const int64_t blocks = a.num_tokens < 65535 ? a.num_tokens : 65535;  // grid-stride over rows beyond
   dim3 grid(static_cast<unsigned>(blocks), 2);
+  const int vpr = static_cast<int>(vecs_per_row);
   switch (mode) {
-    case 0: hipLaunchKernelGGL(write_kernel<0>, grid, dim3(kThreads), 0, s, a, vecs_per_row, total); break;
-    case 1: hipLaunchKernelGGL(write_kernel<1>, grid, dim3(kThreads), 0, s, a, vecs_per_row, total); break;
-    default: hipLaunchKernelGGL(write_kernel<2>, grid, dim3(kThreads), 0, s, a, vecs_per_row, total); break;
+    case 0: hipLaunchKernelGGL(write_kernel<0>, grid, dim3(kThreads), 0, s, a, vpr); break;
+    case 1: hipLaunchKernelGGL(write_kernel<1>, grid, dim3(kThreads), 0, s, a, vpr); break;
+    default: hipLaunchKernelGGL(write_kernel<2>, grid, dim3(kThreads), 0, s, a, vpr); break;
   }
   return hipGetLastError();
 }
