@@ -185,6 +185,71 @@ int pkv_paged_attn_merge(const void* q, int32_t q_dtype, int64_t num_q_tokens, i
                          const int32_t* segment_start_loc, const int32_t* seq_order, float softmax_scale, void* out, void* workspace,
                          size_t workspace_bytes, void* stream);
 
+/*
+ * Attention metadata of one forward, shared by every layer (P1
+ * ARDiffusionPagedForwardContext.prepare builds it once per KV branch).  The
+ * fields are pkv_paged_attn's arguments of the same names.  For capture in a
+ * HIP graph keep table_width and max_seq_len fixed capacities (P1
+ * build_block_table pads the table to a constant width and passes a constant
+ * max_seq_len), so that only the device arrays' contents change between
+ * forwards.
+ */
+typedef struct {
+  const int32_t* block_table;        /* device int32 [num_seqs, table_width] */
+  const int32_t* query_start_loc;    /* device int32 [num_seqs + 1] */
+  const int32_t* seq_lens;           /* device int32 [num_seqs] */
+  const int32_t* segments;           /* device int32 [num_segments][4] */
+  const int32_t* segment_start_loc;  /* device int32 [num_seqs + 1] */
+  const int32_t* seq_order;          /* device int32 [num_seqs] or NULL */
+  int32_t table_width;
+  int32_t num_seqs;
+  int32_t max_query_len;
+  int32_t max_seq_len;
+} pkv_attn_meta;
+
+/*
+ * Caller-owned contiguous staging of one sequence's visible window
+ * (P1 _stage_window and the staged branch of ar_diffusion_paged_attention).
+ */
+typedef struct {
+  void* stage_key;          /* device, capacity_tokens rows of num_kv_heads * head_dim pool elements */
+  void* stage_value;        /* device, same size */
+  int64_t capacity_tokens;  /* rows each buffer holds */
+  int32_t first_block;      /* 0: restage the whole window; k > 0: block rows [0, k) already hold this
+                               window (same history, P1 _prepare_history_staging) and only
+                               [k, max_seq_len / block_size) are refreshed */
+} pkv_staging;
+
+/*
+ * One layer of the per-layer op (P1 _paged_write_attn_impl): enqueues, in
+ * order on `stream`,
+ *   1. the slot writes of the current video K/V (as pkv_paged_write with
+ *      key/value/kv_dtype/num_tokens/slot_mapping),
+ *   2. the slot writes of the action K/V (the same with action_key,
+ *      action_value, num_action_tokens, action_slot_mapping; skipped when
+ *      num_action_tokens == 0, and the four may then be NULL/0),
+ *   3. with staging != NULL: the gather of table row 0's blocks
+ *      [first_block, max_seq_len / block_size) into the staging buffers (as
+ *      pkv_gather), and attention over those buffers read as one contiguous
+ *      run; with staging == NULL: attention over the pools through the table,
+ *   4. the attention and split merge of pkv_paged_attn with meta's fields.
+ * The call allocates nothing, synchronises nothing and launches a fixed
+ * sequence of kernels for fixed host arguments, so it can be captured in a
+ * HIP graph and replayed with new device contents.
+ * Every argument is checked before anything is enqueued.  Errors: those of
+ * pkv_paged_write, pkv_gather and pkv_paged_attn, and PKV_EINVAL for staged
+ * calls with num_seqs != 1, a max_seq_len that is not a whole number of
+ * blocks or exceeds table_width blocks or capacity_tokens, and, when
+ * first_block > 0, a current chunk that is not a whole number of blocks or
+ * first_block + its blocks > max_seq_len / block_size (P1 asserts both).
+ */
+int pkv_paged_write_attn(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads,
+                         const void* key, const void* value, int32_t kv_dtype, int64_t num_tokens,
+                         const int64_t* slot_mapping, const void* action_key, const void* action_value,
+                         int64_t num_action_tokens, const int64_t* action_slot_mapping, const pkv_pools* pools,
+                         const pkv_attn_meta* meta, const pkv_staging* staging, float softmax_scale, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream);
+
 /* Workspace bytes pkv_paged_attn would like for these sizes on the current device. */
 size_t pkv_paged_attn_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t num_seqs, int32_t max_query_len,
@@ -219,6 +284,21 @@ int pkv_slot_mapping(const int32_t* block_ids, int64_t num_block_ids, int64_t fi
 int pkv_window_table(const int32_t* block_ids, int64_t num_block_ids, int64_t history_tokens,
                      int64_t query_tokens, int64_t sink_tokens, int64_t window_tokens, int32_t block_size,
                      int32_t* out_table, int32_t capacity, int32_t* out_count, int32_t* out_kv_len);
+
+/*
+ * Action tokens after the video window (P1 build_block_table and
+ * ensure_action_slots): appends the scratch blocks holding action_tokens
+ * action K/V rows (positions [0, action_tokens) of action_block_ids, host) to
+ * a visible-window table (host, *count entries of capacity) and grows *count
+ * by their number and *kv_len by action_tokens.  The kernel reads the table
+ * as one run, so the video run must end on a block edge: *kv_len %
+ * block_size != 0 with action tokens -> PKV_EINVAL (P1 raises ValueError).
+ * action_tokens == 0 is a no-op.  Errors: PKV_EINVAL for too few or negative
+ * ids; PKV_ERANGE if capacity is too small.
+ */
+int pkv_action_table(int32_t* table, int32_t capacity, int32_t* count, int32_t* kv_len,
+                     const int32_t* action_block_ids, int32_t num_action_block_ids, int64_t action_tokens,
+                     int32_t block_size);
 
 /*
  * Piecewise segments (P3 build_segments): full_spans (host, [num_spans][2],

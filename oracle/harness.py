@@ -39,6 +39,7 @@ class OracleMeta:
     positions: list[list[int]]
     hist_slots: list[np.ndarray]
     cur_slots: list[np.ndarray]
+    act_slots: list[np.ndarray]
     segments: list[list[O.Segment]]
     block_table: np.ndarray  # [num_seqs, width] int32, tail-padded with block 0
     query_start_loc: np.ndarray  # [num_seqs + 1] int32
@@ -48,27 +49,34 @@ class OracleMeta:
 def metadata(wl) -> OracleMeta:
     g = wl.geom
     B = g.block_size
-    tables, kv_lens, positions, hist_slots, cur_slots = [], [], [], [], []
+    tables, kv_lens, positions, hist_slots, cur_slots, act_slots = [], [], [], [], [], []
+    rows = []
     for b in range(g.num_seqs):
         h, q = g.history_lens[b], g.query_lens[b]
+        a = g.action_lens[b] if g.action_lens else 0
         win = O.visible_window(wl.block_ids[b], h + q, g.sink_tokens[b], g.window_tokens[b], B)
+        if a:
+            win = O.with_action_tokens(win, wl.action_block_ids[b], a, B)
         tables.append(win.table)
         kv_lens.append(win.kv_len)
         positions.append(win.positions)
         hist_slots.append(O.slot_mapping(wl.block_ids[b], np.arange(h), B))
         cur_slots.append(O.slot_mapping(wl.block_ids[b], np.arange(h, h + q), B))
-    segs = O.segments_for_rows(g.full_spans, g.query_lens, kv_lens, g.causal_default)
+        act_slots.append(O.slot_mapping(wl.action_block_ids[b], np.arange(a), B) if a else np.zeros(0, np.int64))
+        rows.append(q + a)  # the query: video chunk, then action tokens
+    segs = O.segments_for_rows(g.full_spans, rows, kv_lens, g.causal_default)
     width = max(len(t) for t in tables)
     bt = np.zeros((g.num_seqs, width), dtype=np.int32)  # padding block id 0, as the pages pad
     for b, t in enumerate(tables):
         bt[b, : len(t)] = t
-    qsl = np.concatenate([[0], np.cumsum(g.query_lens)]).astype(np.int32)
+    qsl = np.concatenate([[0], np.cumsum(rows)]).astype(np.int32)
     return OracleMeta(
         tables=tables,
         kv_lens=kv_lens,
         positions=positions,
         hist_slots=hist_slots,
         cur_slots=cur_slots,
+        act_slots=act_slots,
         segments=segs,
         block_table=bt,
         query_start_loc=qsl,
@@ -108,6 +116,21 @@ def write_current(geom, meta: OracleMeta, li, k_pool, v_pool, seqs=None) -> None
         O.paged_write(v_pool, vb, meta.cur_slots[b], src, geom.pool_dtype, li.v_inv_scale)
 
 
+def write_actions(geom, meta: OracleMeta, li, k_pool, v_pool, seqs=None) -> None:
+    """Writes the action K/V of the given sequences into their scratch blocks."""
+    if not geom.action_lens:
+        return
+    src = O.F32 if geom.q_dtype == O.F32 else O.BF16
+    offs = np.concatenate([[0], np.cumsum(geom.action_lens)])
+    for b in _seq_list(geom, seqs):
+        lo, hi = int(offs[b]), int(offs[b + 1])
+        if hi == lo:
+            continue
+        kb, vb = storage_bits(li.k_act[lo:hi]), storage_bits(li.v_act[lo:hi])
+        O.paged_write(k_pool, kb, meta.act_slots[b], src, geom.pool_dtype, li.k_inv_scale)
+        O.paged_write(v_pool, vb, meta.act_slots[b], src, geom.pool_dtype, li.v_inv_scale)
+
+
 def softmax_scale(head_dim: int) -> float:
     """head_dim^-0.5 computed in float64 and rounded once to fp32 (the value both
     sides receive)."""
@@ -136,7 +159,7 @@ def attention(geom, meta: OracleMeta, li, k_pool, v_pool, heads=None, rows=None)
 
 def run_layer(wl, layer: int = 0, heads=None, rows=None, li=None, seqs=None):
     """Full oracle pass for one layer: pools written (history, then the current
-    chunk) and attention over them.  Returns (meta, k_pool, v_pool, out).
+    chunk, then the action tokens) and attention over them.  Returns (meta, k_pool, v_pool, out).
 
     ``seqs`` restricts the pool writes to some sequences (sampled checks of
     large workloads); ``rows`` must then lie in those sequences."""
@@ -146,5 +169,6 @@ def run_layer(wl, layer: int = 0, heads=None, rows=None, li=None, seqs=None):
     k_pool, v_pool = empty_pool(geom), empty_pool(geom)
     write_history(geom, meta, li, k_pool, v_pool, seqs)
     write_current(geom, meta, li, k_pool, v_pool, seqs)
+    write_actions(geom, meta, li, k_pool, v_pool, seqs)
     out = attention(geom, meta, li, k_pool, v_pool, heads=heads, rows=rows)
     return meta, k_pool, v_pool, out

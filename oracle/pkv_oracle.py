@@ -32,6 +32,9 @@ __all__ = [
     "slot_mapping",
     "WindowRead",
     "visible_window",
+    "with_action_tokens",
+    "StagingState",
+    "staging_decision",
     "Segment",
     "build_segments",
     "segments_for_rows",
@@ -209,6 +212,98 @@ def visible_window(
         table.append(int(ids[i]))
         positions.extend(range(first, first + count))
     return WindowRead(table=table, kv_len=len(positions), positions=positions)
+
+
+def with_action_tokens(window: WindowRead, action_block_ids, action_len: int, block_size: int) -> WindowRead:
+    """Action K/V after the video window (P1 ``build_block_table`` with
+    ``ensure_action_slots``; P2's dense reference appends the action K/V to
+    the windowed video K/V).
+
+    The ``action_len`` action tokens occupy positions ``[0, action_len)`` of
+    their own scratch blocks.  Those blocks are listed after the video blocks
+    and the run grows by ``action_len`` tokens.  The kernel reads the list as
+    one run, so a video run that stops inside a block would have its unwritten
+    slots read as action tokens: P1 raises ``ValueError`` for it.  Action
+    tokens get the position labels ``-1, -2, ...`` in the returned window.
+    """
+    a = int(action_len)
+    if a <= 0:
+        return window
+    B = int(block_size)
+    if window.kv_len % B:
+        raise ValueError("action tokens cannot follow a partly written video block")
+    needed = (a + B - 1) // B
+    ids = [int(x) for x in action_block_ids]
+    if len(ids) < needed:
+        raise ValueError("too few action scratch blocks")
+    return WindowRead(
+        table=list(window.table) + ids[:needed],
+        kv_len=window.kv_len + a,
+        positions=list(window.positions) + [-(1 + i) for i in range(a)],
+    )
+
+
+@dataclass
+class StagingState:
+    """What the staging buffers of one KV branch last held (P1
+    ``history_staging_state``): the session and the window signature."""
+
+    session: object = None
+    signature: tuple | None = None
+
+
+def staging_decision(
+    state: StagingState,
+    session,
+    *,
+    num_seqs: int,
+    action_len: int,
+    capacity_tokens: int,
+    history_tokens: int,
+    window: WindowRead,
+    max_seq_len: int,
+    chunk_tokens: int,
+    block_size: int,
+) -> tuple[bool, bool, int]:
+    """P1 ``_prepare_history_staging``: (staging enabled, reuse the staged
+    history, first block row to gather).
+
+    * Staging covers one sequence without action tokens; otherwise it is off
+      and the state is left alone.
+    * A window longer than the buffers is an error (``RuntimeError``).
+    * The staged history is reused when the session is the same object as last
+      time, the signature (history length, the visible history's blocks,
+      ``max_seq_len``, chunk length) is unchanged, and the chunk starts on a
+      block edge and is whole blocks.  The state then records this forward.
+    * The blocks to refresh start after the visible history: the window's
+      block count minus the blocks the current chunk touches (counted from its
+      offset inside its first block).
+
+    The visible history's blocks are read off the window: a table entry is
+    history when its first position lies in a block that ends at or before
+    the chunk's first block.
+    """
+    if action_len or num_seqs != 1:
+        return False, False, 0
+    if max_seq_len > capacity_tokens:
+        raise RuntimeError("the history staging buffers are smaller than the window")
+    B = int(block_size)
+    firsts, seen = [], set()
+    for pos in window.positions:  # first position of every listed block, in order
+        blk = pos // B
+        if pos >= 0 and blk not in seen:
+            seen.add(blk)
+            firsts.append(pos)
+    chunk_first_block = int(history_tokens) // B
+    history_ids = tuple(int(window.table[n]) for n, pos in enumerate(firsts) if pos // B < chunk_first_block)
+    signature = (int(history_tokens), history_ids, int(max_seq_len), int(chunk_tokens))
+    offset = int(history_tokens) % B
+    aligned = offset == 0 and int(chunk_tokens) % B == 0
+    reuse = state.session is not None and state.session is session and state.signature == signature and aligned
+    state.session = session
+    state.signature = signature
+    touched = -(-(offset + int(chunk_tokens)) // B)
+    return True, bool(reuse), window.kv_len // B - touched
 
 
 @dataclass(frozen=True)

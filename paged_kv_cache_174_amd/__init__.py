@@ -17,6 +17,7 @@ from ._lib import (  # noqa: F401
     PkvValueError,
     Pools,
     lib,
+    pkv_action_table,
     pkv_build_segments,
     pkv_gather,
     pkv_last_error,
@@ -25,9 +26,10 @@ from ._lib import (  # noqa: F401
     pkv_paged_attn_merge,
     pkv_paged_attn_workspace_size,
     pkv_paged_write,
+    pkv_paged_write_attn,
     pkv_slot_mapping,
     pkv_validate_metadata_host,
     pkv_version,
     pkv_window_table,
 )
-from .plan import ForwardPlan  # noqa: F401
+from .plan import ForwardPlan, HistoryStaging, StagingDecision  # noqa: F401

@@ -56,6 +56,30 @@ class _Pools(ctypes.Structure):
     ]
 
 
+class _AttnMeta(ctypes.Structure):
+    _fields_ = [
+        ("block_table", ctypes.c_void_p),
+        ("query_start_loc", ctypes.c_void_p),
+        ("seq_lens", ctypes.c_void_p),
+        ("segments", ctypes.c_void_p),
+        ("segment_start_loc", ctypes.c_void_p),
+        ("seq_order", ctypes.c_void_p),
+        ("table_width", ctypes.c_int32),
+        ("num_seqs", ctypes.c_int32),
+        ("max_query_len", ctypes.c_int32),
+        ("max_seq_len", ctypes.c_int32),
+    ]
+
+
+class _Staging(ctypes.Structure):
+    _fields_ = [
+        ("stage_key", ctypes.c_void_p),
+        ("stage_value", ctypes.c_void_p),
+        ("capacity_tokens", ctypes.c_int64),
+        ("first_block", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 _P = ctypes.c_void_p
@@ -72,9 +96,15 @@ _SIGNATURES = {
     "pkv_paged_attn": (ctypes.c_int, _ATTN_ARGS),
     "pkv_paged_attn_main": (ctypes.c_int, _ATTN_ARGS),
     "pkv_paged_attn_merge": (ctypes.c_int, _ATTN_ARGS),
+    "pkv_paged_write_attn": (
+        ctypes.c_int,
+        [_P, _I32, _I64, _I32, _P, _P, _I32, _I64, _P, _P, _P, _I64, _P, _PPOOLS,
+         ctypes.POINTER(_AttnMeta), ctypes.POINTER(_Staging), _F32, _P, _P, _SZ, _P],
+    ),
     "pkv_paged_attn_workspace_size": (_SZ, [_I64, _I32, _I32, _I32, _I32, _I32, _I32]),
     "pkv_slot_mapping": (ctypes.c_int, [_PI32, _I64, _I64, _I64, _I32, _PI64]),
     "pkv_window_table": (ctypes.c_int, [_PI32, _I64, _I64, _I64, _I64, _I64, _I32, _PI32, _I32, _PI32, _PI32]),
+    "pkv_action_table": (ctypes.c_int, [_PI32, _I32, _PI32, _PI32, _PI32, _I32, _I64, _I32]),
     "pkv_build_segments": (ctypes.c_int, [_PI32, _I32, _I32, _I32, _PI32, _I32, _PI32]),
     "pkv_validate_metadata_host": (
         ctypes.c_int,
@@ -308,7 +338,126 @@ def pkv_paged_attn_merge(*args, **kwargs) -> torch.Tensor:
     return pkv_paged_attn(*args, _entry="pkv_paged_attn_merge", **kwargs)
 
 
+def _kv_rows(key, value, slot_mapping, pools, what):
+    """(key ptr, value ptr, tokens, slot ptr) of one write, or nulls for none."""
+    if key is None and value is None and slot_mapping is None:
+        return None, None, 0, None
+    if key is None or value is None or slot_mapping is None:
+        raise ValueError(f"{what}: key, value and slot_mapping go together")
+    if key.shape != value.shape or key.dtype != value.dtype:
+        raise ValueError(f"{what}: key and value must match")
+    if key.dim() != 3 or key.shape[1:] != (pools.num_kv_heads, pools.head_dim):
+        raise ValueError(f"{what}: key/value must be [tokens, num_kv_heads, head_dim] matching the pools")
+    if slot_mapping.numel() != key.shape[0]:
+        raise ValueError(f"{what}: slot_mapping needs one entry per token")
+    if key.shape[0] == 0:
+        return None, None, 0, None
+    return (_dev(key, f"{what} key"), _dev(value, f"{what} value"), key.shape[0],
+            _dev(slot_mapping, f"{what} slot_mapping", torch.int64))
+
+
+def pkv_paged_write_attn(
+    q: torch.Tensor,
+    key: torch.Tensor,
+    value: torch.Tensor,
+    slot_mapping: torch.Tensor,
+    pools: Pools,
+    meta,
+    softmax_scale: float,
+    *,
+    action_key: torch.Tensor | None = None,
+    action_value: torch.Tensor | None = None,
+    action_slot_mapping: torch.Tensor | None = None,
+    stage_key: torch.Tensor | None = None,
+    stage_value: torch.Tensor | None = None,
+    first_block: int = 0,
+    out: torch.Tensor | None = None,
+    workspace: torch.Tensor | None = None,
+    stream=None,
+) -> torch.Tensor:
+    """One layer of the fused op (see include/pkv.h): writes the current video
+    K/V and the action K/V through their slot mappings, optionally stages the
+    window into ``stage_key``/``stage_value`` from ``first_block`` on, and
+    attends.  ``meta`` is any object with the attention metadata as device
+    tensors (block_table, query_start_loc, seq_lens, segments,
+    segment_start_loc, seq_order or None) and the host ints max_query_len and
+    max_seq_len -- a ForwardPlan is one."""
+    if q.dim() != 3 or q.shape[2] != pools.head_dim:
+        raise ValueError("q must be [tokens, num_q_heads, head_dim]")
+    if out is None:
+        out = torch.empty_like(q)
+    elif out.shape != q.shape or out.dtype != q.dtype:
+        raise ValueError("out must match q")
+    kp, vp, n, sp = _kv_rows(key, value, slot_mapping, pools, "video")
+    akp, avp, an, asp = _kv_rows(action_key, action_value, action_slot_mapping, pools, "action")
+    kv_dtype = _TORCH_DTYPE.get(key.dtype, -1) if key is not None else _TORCH_DTYPE.get(q.dtype, -1)
+    if an and action_key.dtype != key.dtype:
+        raise ValueError("action K/V must have the video K/V's dtype")
+    bt = meta.block_table
+    if bt.dim() != 2:
+        raise ValueError("block_table must be [num_seqs, width]")
+    num_seqs = bt.shape[0]
+    if (meta.query_start_loc.numel() != num_seqs + 1 or meta.seq_lens.numel() != num_seqs
+            or meta.segment_start_loc.numel() != num_seqs + 1):
+        raise ValueError("query_start_loc, seq_lens and segment_start_loc must match block_table's rows")
+    order = getattr(meta, "seq_order", None)
+    if order is not None and order.numel() != num_seqs:
+        raise ValueError("seq_order must hold one entry per sequence")
+    m = _AttnMeta(
+        _dev(bt, "block_table", torch.int32),
+        _dev(meta.query_start_loc, "query_start_loc", torch.int32),
+        _dev(meta.seq_lens, "seq_lens", torch.int32),
+        _dev(meta.segments, "segments", torch.int32),
+        _dev(meta.segment_start_loc, "segment_start_loc", torch.int32),
+        None if order is None else _dev(order, "seq_order", torch.int32),
+        bt.shape[1],
+        num_seqs,
+        int(meta.max_query_len),
+        int(meta.max_seq_len),
+    )
+    st_ptr = None
+    if stage_key is not None or stage_value is not None:
+        for name, t in (("stage_key", stage_key), ("stage_value", stage_value)):
+            if t is None or t.dtype != pools.key.dtype or t.dim() != 3 or t.shape[1:] != pools.key.shape[1:]:
+                raise ValueError(f"{name} must be [capacity, num_kv_heads, head_dim] of the pool dtype")
+        if stage_key.shape[0] != stage_value.shape[0]:
+            raise ValueError("stage_key and stage_value must have the same capacity")
+        st = _Staging(_dev(stage_key, "stage_key"), _dev(stage_value, "stage_value"), stage_key.shape[0],
+                      int(first_block))
+        st_ptr = ctypes.byref(st)
+    elif first_block:
+        raise ValueError("first_block needs staging buffers")
+    ws_ptr, ws_bytes = None, 0
+    if workspace is not None:
+        ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    ps = pools.c_struct()
+    _check(
+        lib().pkv_paged_write_attn(
+            _dev(q, "q"), _TORCH_DTYPE.get(q.dtype, -1), q.shape[0], q.shape[1],
+            kp, vp, kv_dtype, n, sp, akp, avp, an, asp,
+            ctypes.byref(ps), ctypes.byref(m), st_ptr, float(softmax_scale),
+            _dev(out, "out"), ws_ptr, ws_bytes, _stream(stream),
+        )
+    )
+    return out
+
+
 # ----------------------------------------------------------------- host metadata
+
+
+def pkv_action_table(table, kv_len: int, action_block_ids, action_tokens: int, block_size: int = 16):
+    """Appends the action scratch blocks to a visible-window table (include/pkv.h).
+    Returns (table, kv_len)."""
+    t = _host_i32(table)
+    ids = _host_i32(action_block_ids)
+    cap = t.size + max(0, -(-int(action_tokens) // block_size))
+    out = np.zeros(cap, dtype=np.int32)
+    out[: t.size] = t
+    count, kl = ctypes.c_int32(t.size), ctypes.c_int32(int(kv_len))
+    _check(lib().pkv_action_table(_ptr(out, ctypes.c_int32), cap, ctypes.byref(count), ctypes.byref(kl),
+                                  _ptr(ids, ctypes.c_int32), ids.size, int(action_tokens), block_size))
+    return out[: count.value], int(kl.value)
+
 
 
 def pkv_slot_mapping(block_ids, first_position: int, num_tokens: int, block_size: int = 16) -> np.ndarray:

@@ -31,7 +31,8 @@ __global__ __launch_bounds__(64 * kWaves) void attn_f32_kernel(AttnArgs a) {
   const float* q = static_cast<const float*>(a.q) + (static_cast<int64_t>(t0 + i) * a.num_q_heads + h) * D;
   const float* kp = static_cast<const float*>(a.kpool) + static_cast<int64_t>(hk) * D;
   const float* vp = static_cast<const float*>(a.vpool) + static_cast<int64_t>(hk) * D;
-  const int32_t* table = a.block_table + static_cast<int64_t>(b) * a.table_width;
+  // No table: the K/V buffers are one contiguous run (logical block i is block i).
+  const int32_t* table = a.block_table ? a.block_table + static_cast<int64_t>(b) * a.table_width : nullptr;
   const int B = a.block_size;
 
   for (int d = lane; d < D; d += 64) qs[w][d] = q[d];
@@ -48,7 +49,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_f32_kernel(AttnArgs a) {
     float z = -INFINITY;
     int64_t slot = 0;
     if (j < L) {
-      slot = static_cast<int64_t>(table[j / B]) * B + (j % B);
+      slot = table ? static_cast<int64_t>(table[j / B]) * B + (j % B) : j;
       const float* kr = kp + slot * row_elems;
       float acc = 0.f;
       for (int d = 0; d < D; ++d) acc = fmaf(qs[w][d], kr[d], acc);

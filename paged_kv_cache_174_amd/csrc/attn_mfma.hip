@@ -306,12 +306,17 @@ attn_mfma_kernel(AttnArgs a) {
   // later use of Q with a full vmcnt(0), which would drain the K/V prefetch.
   wait_vmcnt<0>();
 
-  // ---- block-table slice for this workgroup's keys
-  const int32_t* table = a.block_table + static_cast<int64_t>(b) * a.table_width;
+  // ---- block-table slice for this workgroup's keys (no table: the K/V
+  // buffers are one contiguous run, logical block i is block i)
   const int nblk = (s + 15) >> 4;
   const int blk_lo = k_begin >> 4;
   const int blk_hi = min((k_end + 15) >> 4, nblk);
-  for (int i = threadIdx.x; i < blk_hi - blk_lo; i += NT) tbl[i] = table[blk_lo + i];
+  if (a.block_table) {
+    const int32_t* table = a.block_table + static_cast<int64_t>(b) * a.table_width;
+    for (int i = threadIdx.x; i < blk_hi - blk_lo; i += NT) tbl[i] = table[blk_lo + i];
+  } else {
+    for (int i = threadIdx.x; i < blk_hi - blk_lo; i += NT) tbl[i] = blk_lo + i;
+  }
   lds_barrier();
   // Keys at or past kv_lim are staged as zeros: past seq_len they do not exist,
   // and past the slice every row of the workgroup masks them anyway.

@@ -107,6 +107,50 @@ SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, i
   return p;
 }
 
+
+// ---- argument checks and launches shared by the separate calls and the fused one
+
+int write_setup(const void* key, const void* value, int32_t src_dtype, int64_t num_tokens, const int64_t* slot_mapping,
+                const pkv_pools* pools, WriteArgs& a, int& mode) {
+  if (int rc = check_pools(pools)) return rc;
+  if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens must be >= 0");
+  a = WriteArgs{key, value, slot_mapping, pools->key, pools->value, num_tokens,
+                static_cast<int64_t>(pools->num_kv_heads) * pools->head_dim, pools->k_inv_scale, pools->v_inv_scale};
+  if (num_tokens == 0) return PKV_OK;
+  if (!key || !value || !slot_mapping) return fail(PKV_EINVAL, "key, value and slot_mapping must not be NULL");
+  if (src_dtype == PKV_F32 && pools->dtype == PKV_F32) mode = 0;
+  else if (src_dtype == PKV_BF16 && pools->dtype == PKV_BF16) mode = 1;
+  else if (src_dtype == PKV_BF16 && pools->dtype == PKV_FP8_E4M3) mode = 2;
+  else return fail(PKV_EUNSUPPORTED, "no write from dtype %d into a dtype %d pool", src_dtype, pools->dtype);
+  return PKV_OK;
+}
+
+int write_launch(const WriteArgs& a, int mode, hipStream_t st) {
+  if (a.num_tokens == 0) return PKV_OK;
+  if (hipError_t e = launch_write(a, mode, st); e != hipSuccess)
+    return fail(PKV_EHIP, "write launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
+int gather_setup(const pkv_pools* pools, const int32_t* block_ids, int32_t n_blocks, int32_t first_block,
+                 void* stage_key, void* stage_value, GatherArgs& a) {
+  if (int rc = check_pools(pools)) return rc;
+  if (n_blocks < 0 || first_block < 0 || first_block > n_blocks)
+    return fail(PKV_EINVAL, "need 0 <= first_block <= n_blocks (got first_block %d, n_blocks %d)", first_block, n_blocks);
+  a = GatherArgs{pools->key, pools->value, block_ids, stage_key, stage_value, first_block, n_blocks,
+                 static_cast<int64_t>(pools->block_size) * pools->num_kv_heads * pools->head_dim * dtype_size(pools->dtype)};
+  if (first_block == n_blocks) return PKV_OK;
+  if (!block_ids || !stage_key || !stage_value) return fail(PKV_EINVAL, "block_ids and staging buffers must not be NULL");
+  return PKV_OK;
+}
+
+int gather_launch(const GatherArgs& a, hipStream_t st) {
+  if (a.first_block == a.n_blocks) return PKV_OK;
+  if (hipError_t e = launch_gather(a, st); e != hipSuccess)
+    return fail(PKV_EHIP, "gather launch failed: %s", hipGetErrorString(e));
+  return PKV_OK;
+}
+
 }  // namespace
 
 int fail(int code, const char* fmt, ...) {
@@ -130,35 +174,18 @@ const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
 int pkv_paged_write(const void* key, const void* value, int32_t src_dtype, int64_t num_tokens,
                     const int64_t* slot_mapping, const pkv_pools* pools, void* stream) {
   g_error[0] = '\0';
-  if (int rc = check_pools(pools)) return rc;
-  if (num_tokens < 0) return fail(PKV_EINVAL, "num_tokens must be >= 0");
-  if (num_tokens == 0) return PKV_OK;
-  if (!key || !value || !slot_mapping) return fail(PKV_EINVAL, "key, value and slot_mapping must not be NULL");
-  int mode;
-  if (src_dtype == PKV_F32 && pools->dtype == PKV_F32) mode = 0;
-  else if (src_dtype == PKV_BF16 && pools->dtype == PKV_BF16) mode = 1;
-  else if (src_dtype == PKV_BF16 && pools->dtype == PKV_FP8_E4M3) mode = 2;
-  else return fail(PKV_EUNSUPPORTED, "no write from dtype %d into a dtype %d pool", src_dtype, pools->dtype);
-  WriteArgs a{key, value, slot_mapping, pools->key, pools->value, num_tokens,
-              static_cast<int64_t>(pools->num_kv_heads) * pools->head_dim, pools->k_inv_scale, pools->v_inv_scale};
-  if (hipError_t e = launch_write(a, mode, static_cast<hipStream_t>(stream)); e != hipSuccess)
-    return fail(PKV_EHIP, "write launch failed: %s", hipGetErrorString(e));
-  return PKV_OK;
+  WriteArgs a{};
+  int mode = 0;
+  if (int rc = write_setup(key, value, src_dtype, num_tokens, slot_mapping, pools, a, mode)) return rc;
+  return write_launch(a, mode, static_cast<hipStream_t>(stream));
 }
 
 int pkv_gather(const pkv_pools* pools, const int32_t* block_ids, int32_t n_blocks, int32_t first_block,
                void* stage_key, void* stage_value, void* stream) {
   g_error[0] = '\0';
-  if (int rc = check_pools(pools)) return rc;
-  if (n_blocks < 0 || first_block < 0 || first_block > n_blocks)
-    return fail(PKV_EINVAL, "need 0 <= first_block <= n_blocks (got first_block %d, n_blocks %d)", first_block, n_blocks);
-  if (first_block == n_blocks) return PKV_OK;
-  if (!block_ids || !stage_key || !stage_value) return fail(PKV_EINVAL, "block_ids and staging buffers must not be NULL");
-  GatherArgs a{pools->key, pools->value, block_ids, stage_key, stage_value, first_block, n_blocks,
-               static_cast<int64_t>(pools->block_size) * pools->num_kv_heads * pools->head_dim * dtype_size(pools->dtype)};
-  if (hipError_t e = launch_gather(a, static_cast<hipStream_t>(stream)); e != hipSuccess)
-    return fail(PKV_EHIP, "gather launch failed: %s", hipGetErrorString(e));
-  return PKV_OK;
+  GatherArgs a{};
+  if (int rc = gather_setup(pools, block_ids, n_blocks, first_block, stage_key, stage_value, a)) return rc;
+  return gather_launch(a, static_cast<hipStream_t>(stream));
 }
 
 size_t pkv_paged_attn_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
@@ -179,30 +206,40 @@ namespace {
 
 constexpr unsigned kPhaseMain = 1u, kPhaseMerge = 2u;
 
-// Validates the arguments, plans the key splits and launches the phases asked
-// for: the attention kernel (kPhaseMain) and, when the keys are split, the
-// merge of the partial results (kPhaseMerge).  Both phases derive the same
-// plan from the same arguments.
-int paged_attn_impl(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads,
-                    const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
-                    const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
-                    int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
-                    const int32_t* segment_start_loc, const int32_t* seq_order, float softmax_scale, void* out,
-                    void* workspace, size_t workspace_bytes, void* stream, unsigned phases) {
-  g_error[0] = '\0';
+// Everything an attention launch needs beyond the kernel arguments.
+struct AttnLaunch {
+  AttnArgs a{};
+  SplitPlan p{};
+  bool f32 = false;
+  bool fp8 = false;
+  int max_query_len = 0;
+};
+
+// Validates the attention arguments and plans the key splits; enqueues nothing.
+// kpool / vpool are the K/V the kernel reads: the pools, or contiguous staging
+// buffers when block_table is null.
+int attn_setup(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads, const pkv_pools* pools,
+               const void* kpool, const void* vpool, const int32_t* block_table, int32_t table_width,
+               const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs, int32_t max_query_len,
+               int32_t max_seq_len, const int32_t* segments, const int32_t* segment_start_loc,
+               const int32_t* seq_order, float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
+               AttnLaunch& L) {
   if (int rc = check_pools(pools)) return rc;
-  if (!q || !out || !block_table || !query_start_loc || !seq_lens || !segments || !segment_start_loc)
+  if (!q || !out || !query_start_loc || !seq_lens || !segments || !segment_start_loc)
     return fail(PKV_EINVAL, "q, out and every metadata pointer must be non-NULL");
   if (num_seqs <= 0) return fail(PKV_EINVAL, "num_seqs must be positive");
   if (num_q_tokens <= 0) return fail(PKV_EINVAL, "num_q_tokens must be positive");
   if (num_q_heads <= 0 || num_q_heads % pools->num_kv_heads)
     return fail(PKV_EINVAL, "num_q_heads (%d) must be a positive multiple of num_kv_heads (%d)", num_q_heads,
                 pools->num_kv_heads);
-  if (table_width <= 0) return fail(PKV_EINVAL, "table_width must be positive");
   if (max_query_len <= 0 || max_seq_len <= 0 || max_query_len > max_seq_len)
     return fail(PKV_EINVAL, "need 0 < max_query_len <= max_seq_len (got %d, %d)", max_query_len, max_seq_len);
-  if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(table_width) * pools->block_size)
-    return fail(PKV_EINVAL, "max_seq_len %d exceeds what a %d-entry block table can address", max_seq_len, table_width);
+  if (block_table) {
+    if (table_width <= 0) return fail(PKV_EINVAL, "table_width must be positive");
+    if (static_cast<int64_t>(max_seq_len) > static_cast<int64_t>(table_width) * pools->block_size)
+      return fail(PKV_EINVAL, "max_seq_len %d exceeds what a %d-entry block table can address", max_seq_len,
+                  table_width);
+  }
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
     return fail(PKV_EINVAL, "softmax_scale must be positive and finite");
   const bool f32 = pools->dtype == PKV_F32;
@@ -210,11 +247,12 @@ int paged_attn_impl(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_
     return fail(PKV_EINVAL, "query dtype %d does not go with pool dtype %d (f32 with f32, bf16 with bf16 or fp8)",
                 q_dtype, pools->dtype);
 
-  AttnArgs a{};
+  AttnArgs& a = L.a;
+  a = AttnArgs{};
   a.q = q;
   a.out = out;
-  a.kpool = pools->key;
-  a.vpool = pools->value;
+  a.kpool = kpool;
+  a.vpool = vpool;
   a.block_table = block_table;
   a.qsl = query_start_loc;
   a.seq_lens = seq_lens;
@@ -232,7 +270,9 @@ int paged_attn_impl(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_
   const float k_scale = pools->dtype == PKV_FP8_E4M3 ? pools->k_scale : 1.f;
   a.v_scale = pools->dtype == PKV_FP8_E4M3 ? pools->v_scale : 1.f;
   a.scale_log2 = softmax_scale * k_scale * kLog2e;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  L.f32 = f32;
+  L.fp8 = pools->dtype == PKV_FP8_E4M3;
+  L.max_query_len = max_query_len;
 
   if (f32) {
     if (pools->head_dim != 64 && pools->head_dim != 128)
@@ -240,22 +280,21 @@ int paged_attn_impl(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_
     a.num_splits = 1;
     a.row_tiles = 0;
     a.split_len = 0;
-    if (phases & kPhaseMain) {
-      if (hipError_t e = launch_attn_f32(a, max_query_len, st); e != hipSuccess)
-        return fail(PKV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
-    }
+    L.p = SplitPlan{0, 1, 0, false};
     return PKV_OK;
   }
   if (pools->head_dim != 128)
     return fail(PKV_EUNSUPPORTED, "bf16/fp8 attention supports head_dim 128, not %d", pools->head_dim);
-  SplitPlan p = plan_splits(num_q_tokens, num_q_heads, pools->num_kv_heads, num_seqs, max_query_len, max_seq_len,
-                            workspace_bytes, workspace != nullptr);
+  const SplitPlan p = plan_splits(num_q_tokens, num_q_heads, pools->num_kv_heads, num_seqs, max_query_len,
+                                  max_seq_len, workspace_bytes, workspace != nullptr);
   if (p.splits > kMaxSplits)
     return fail(PKV_EUNSUPPORTED, "max_seq_len %d needs more than %d key splits", max_seq_len, kMaxSplits);
-  if (p.splits > 1 && (!workspace ||
-                       workspace_bytes < static_cast<size_t>(p.splits) * num_q_tokens * num_q_heads * (128 + 2) * sizeof(float)))
+  if (p.splits > 1 &&
+      (!workspace ||
+       workspace_bytes < static_cast<size_t>(p.splits) * num_q_tokens * num_q_heads * (128 + 2) * sizeof(float)))
     return fail(PKV_EINVAL, "max_seq_len %d needs %d key splits and a workspace of pkv_paged_attn_workspace_size() bytes",
                 max_seq_len, p.splits);
+  L.p = p;
   a.row_tiles = p.row_tiles;
   a.num_splits = p.splits;
   a.split_len = p.split_len;
@@ -264,15 +303,45 @@ int paged_attn_impl(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_
     a.ws_o = static_cast<float*>(workspace);
     a.ws_ml = a.ws_o + static_cast<int64_t>(p.splits) * rows * 128;
   }
+  return PKV_OK;
+}
+
+// Launches the phases asked for: the attention kernel (kPhaseMain) and, when
+// the keys are split, the merge of the partial results (kPhaseMerge).
+int attn_launch(const AttnLaunch& L, unsigned phases, hipStream_t st) {
+  if (L.f32) {
+    if (phases & kPhaseMain) {
+      if (hipError_t e = launch_attn_f32(L.a, L.max_query_len, st); e != hipSuccess)
+        return fail(PKV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
+    }
+    return PKV_OK;
+  }
   if (phases & kPhaseMain) {
-    if (hipError_t e = launch_attn_mfma(a, pools->dtype == PKV_FP8_E4M3, p.short_rows, st); e != hipSuccess)
+    if (hipError_t e = launch_attn_mfma(L.a, L.fp8, L.p.short_rows, st); e != hipSuccess)
       return fail(PKV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
   }
-  if ((phases & kPhaseMerge) && p.splits > 1) {
-    if (hipError_t e = launch_attn_combine(a, st); e != hipSuccess)
+  if ((phases & kPhaseMerge) && L.p.splits > 1) {
+    if (hipError_t e = launch_attn_combine(L.a, st); e != hipSuccess)
       return fail(PKV_EHIP, "split combine launch failed: %s", hipGetErrorString(e));
   }
   return PKV_OK;
+}
+
+int paged_attn_impl(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads,
+                    const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
+                    const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
+                    int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
+                    const int32_t* segment_start_loc, const int32_t* seq_order, float softmax_scale, void* out,
+                    void* workspace, size_t workspace_bytes, void* stream, unsigned phases) {
+  g_error[0] = '\0';
+  if (!block_table) return fail(PKV_EINVAL, "block_table must not be NULL");
+  if (!pools) return fail(PKV_EINVAL, "pools is NULL");
+  AttnLaunch L;
+  if (int rc = attn_setup(q, q_dtype, num_q_tokens, num_q_heads, pools, pools->key, pools->value, block_table,
+                          table_width, query_start_loc, seq_lens, num_seqs, max_query_len, max_seq_len, segments,
+                          segment_start_loc, seq_order, softmax_scale, out, workspace, workspace_bytes, L))
+    return rc;
+  return attn_launch(L, phases, static_cast<hipStream_t>(stream));
 }
 
 }  // namespace
@@ -296,6 +365,76 @@ int pkv_paged_attn_merge(PKV_ATTN_PARAMS) { return paged_attn_impl(PKV_ATTN_ARGS
 
 #undef PKV_ATTN_PARAMS
 #undef PKV_ATTN_ARGS
+
+// P1 _paged_write_attn_impl (the per-layer op: slot writes of the current
+// video and action K/V, then attention) and ar_diffusion_paged_attention's
+// staged branch (_stage_window into caller-owned buffers, then attention over
+// them as one contiguous run).
+int pkv_paged_write_attn(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads,
+                         const void* key, const void* value, int32_t kv_dtype, int64_t num_tokens,
+                         const int64_t* slot_mapping, const void* action_key, const void* action_value,
+                         int64_t num_action_tokens, const int64_t* action_slot_mapping, const pkv_pools* pools,
+                         const pkv_attn_meta* meta, const pkv_staging* staging, float softmax_scale, void* out,
+                         void* workspace, size_t workspace_bytes, void* stream) {
+  g_error[0] = '\0';
+  if (!meta) return fail(PKV_EINVAL, "meta is NULL");
+  if (!pools) return fail(PKV_EINVAL, "pools is NULL");
+  if (!meta->block_table) return fail(PKV_EINVAL, "meta->block_table must not be NULL");
+  WriteArgs wv{}, wa{};
+  int mode_v = 0, mode_a = 0;
+  if (int rc = write_setup(key, value, kv_dtype, num_tokens, slot_mapping, pools, wv, mode_v)) return rc;
+  if (int rc = write_setup(action_key, action_value, kv_dtype, num_action_tokens, action_slot_mapping, pools, wa,
+                           mode_a))
+    return rc;
+  GatherArgs ga{};
+  const void* kread = pools->key;
+  const void* vread = pools->value;
+  const int32_t* table = meta->block_table;
+  if (staging) {
+    const int B = pools->block_size;
+    if (meta->num_seqs != 1)
+      return fail(PKV_EINVAL, "staged attention covers one sequence, not %d", meta->num_seqs);
+    if (meta->max_seq_len <= 0 || meta->max_seq_len % B)
+      return fail(PKV_EINVAL, "staged attention needs a block-aligned max_seq_len, got %d", meta->max_seq_len);
+    const int32_t n_blocks = meta->max_seq_len / B;
+    if (n_blocks > meta->table_width)
+      return fail(PKV_EINVAL, "max_seq_len %d exceeds the %d-entry block table", meta->max_seq_len, meta->table_width);
+    if (staging->capacity_tokens < meta->max_seq_len)
+      return fail(PKV_EINVAL, "staging buffers hold %lld tokens but this call stages %d",
+                  static_cast<long long>(staging->capacity_tokens), meta->max_seq_len);
+    const int32_t first = staging->first_block;
+    if (first != 0) {
+      // Reuse: blocks [0, first) already hold this window; only the current
+      // chunk's whole blocks are refreshed.
+      const int64_t cur_blocks = num_tokens / B;
+      if (num_tokens <= 0 || cur_blocks * B != num_tokens)
+        return fail(PKV_EINVAL, "staged reuse needs a block-aligned current chunk, got %lld tokens",
+                    static_cast<long long>(num_tokens));
+      if (first < 0 || first + cur_blocks > n_blocks)
+        return fail(PKV_EINVAL, "first_block %d + %lld current blocks exceeds the %d-block window", first,
+                    static_cast<long long>(cur_blocks), n_blocks);
+    }
+    if (int rc = gather_setup(pools, meta->block_table, n_blocks, first, staging->stage_key, staging->stage_value, ga))
+      return rc;
+    kread = staging->stage_key;
+    vread = staging->stage_value;
+    table = nullptr;
+  }
+  AttnLaunch L;
+  if (int rc = attn_setup(q, q_dtype, num_q_tokens, num_q_heads, pools, kread, vread, table, meta->table_width,
+                          meta->query_start_loc, meta->seq_lens, meta->num_seqs, meta->max_query_len,
+                          meta->max_seq_len, meta->segments, meta->segment_start_loc, meta->seq_order, softmax_scale,
+                          out, workspace, workspace_bytes, L))
+    return rc;
+  // Everything is checked; enqueue in order on one stream.
+  const hipStream_t st = static_cast<hipStream_t>(stream);
+  if (int rc = write_launch(wv, mode_v, st)) return rc;
+  if (int rc = write_launch(wa, mode_a, st)) return rc;
+  if (staging) {
+    if (int rc = gather_launch(ga, st)) return rc;
+  }
+  return attn_launch(L, kPhaseMain | kPhaseMerge, st);
+}
 
 // ------------------------------------------------------------------ host metadata
 
@@ -366,6 +505,38 @@ int pkv_window_table(const int32_t* block_ids, int64_t num_block_ids, int64_t hi
   if (kv_len > INT32_MAX) return fail(PKV_ERANGE, "window longer than 2^31 tokens");
   *out_count = count;
   *out_kv_len = static_cast<int32_t>(kv_len);
+  return PKV_OK;
+}
+
+// P1 build_block_table: action K/V sits in scratch blocks listed after the
+// video window, and the kernel reads table and length as one run.
+int pkv_action_table(int32_t* table, int32_t capacity, int32_t* count, int32_t* kv_len,
+                     const int32_t* action_block_ids, int32_t num_action_block_ids, int64_t action_tokens,
+                     int32_t block_size) {
+  g_error[0] = '\0';
+  if (!table || !count || !kv_len) return fail(PKV_EINVAL, "NULL pointer");
+  if (block_size <= 0 || action_tokens < 0 || *count < 0 || *kv_len < 0) return fail(PKV_EINVAL, "bad sizes");
+  if (action_tokens == 0) return PKV_OK;
+  // A video run that stops inside its last block would make the kernel read
+  // that block's unwritten slots as the first action tokens.
+  if (*kv_len % block_size)
+    return fail(PKV_EINVAL,
+                "action tokens cannot follow a partly written video block: the video run ends %d slots into its "
+                "last block",
+                *kv_len % block_size);
+  const int64_t nb = (action_tokens + block_size - 1) / block_size;
+  if (!action_block_ids || num_action_block_ids < nb)
+    return fail(PKV_EINVAL, "%lld action tokens need %lld scratch blocks, got %d", static_cast<long long>(action_tokens),
+                static_cast<long long>(nb), num_action_block_ids);
+  if (*count + nb > capacity)
+    return fail(PKV_ERANGE, "table capacity %d is too small for %lld entries", capacity,
+                static_cast<long long>(*count + nb));
+  for (int64_t i = 0; i < nb; ++i) {
+    if (action_block_ids[i] < 0) return fail(PKV_EINVAL, "negative action block id");
+    table[*count + i] = action_block_ids[i];
+  }
+  *count += static_cast<int32_t>(nb);
+  *kv_len += static_cast<int32_t>(action_tokens);
   return PKV_OK;
 }
 

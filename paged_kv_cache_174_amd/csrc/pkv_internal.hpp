@@ -49,7 +49,7 @@ struct AttnArgs {
   void* out;
   const void* kpool;
   const void* vpool;
-  const int32_t* block_table;
+  const int32_t* block_table;  // null: K/V are contiguous (logical block i is block i)
   const int32_t* qsl;
   const int32_t* seq_lens;
   const int32_t* segments;

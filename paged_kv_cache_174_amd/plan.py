@@ -14,7 +14,8 @@ P4 "vllm_omni/diffusion/diffusion_kv/paged_attention_adapter.py".
 
 from __future__ import annotations
 
-from dataclasses import dataclass
+import weakref
+from dataclasses import dataclass, field
 
 import numpy as np
 import torch
@@ -38,6 +39,11 @@ class ForwardPlan:
     hist_slots_host: np.ndarray  # [sum h] int64
     max_query_len: int
     max_seq_len: int
+    # Action tokens (P1 ensure_action_slots): per sequence, rows after the
+    # current video chunk in both the query and the keys.
+    chunk_lens: list[int] = field(default_factory=list)  # current video tokens per sequence
+    action_lens: list[int] = field(default_factory=list)
+    act_slots_host: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))  # [sum a] int64
     # device copies
     block_table: torch.Tensor | None = None
     query_start_loc: torch.Tensor | None = None
@@ -47,6 +53,7 @@ class ForwardPlan:
     seq_order: torch.Tensor | None = None
     slot_mapping: torch.Tensor | None = None
     history_slot_mapping: torch.Tensor | None = None
+    action_slot_mapping: torch.Tensor | None = None
 
     @classmethod
     def build(
@@ -62,34 +69,47 @@ class ForwardPlan:
         table_width: int | None = None,
         max_seq_len: int | None = None,
         device=None,
+        action_lens=None,
+        action_block_ids=None,
     ) -> "ForwardPlan":
+        """``query_lens`` are the current video chunks.  With ``action_lens``
+        (per sequence) and ``action_block_ids`` (each sequence's scratch
+        blocks), the action K/V is listed after the window and the query of a
+        sequence is its video chunk followed by its action tokens (P1
+        build_block_table, P2 action tests)."""
         n = len(query_lens)
+        acts = [0] * n if action_lens is None else [int(a) for a in action_lens]
         tables, kv_lens, segs, seg_start = [], [], [], [0]
-        cur_slots, hist_slots = [], []
+        cur_slots, hist_slots, act_slots = [], [], []
         for b in range(n):
-            h, q = int(history_lens[b]), int(query_lens[b])
+            h, q, a = int(history_lens[b]), int(query_lens[b]), acts[b]
             table, kv_len = L.pkv_window_table(block_ids[b], h, q, sink_tokens[b], window_tokens[b], block_size)
+            if a:
+                table, kv_len = L.pkv_action_table(table, kv_len, action_block_ids[b], a, block_size)
+                act_slots.append(L.pkv_slot_mapping(action_block_ids[b], 0, a, block_size))
             tables.append(table)
             kv_lens.append(kv_len)
             hist_slots.append(L.pkv_slot_mapping(block_ids[b], 0, h, block_size))
             cur_slots.append(L.pkv_slot_mapping(block_ids[b], h, q, block_size))
+            rows = q + a  # the query is the suffix of the keys: video chunk, then actions
             spans = full_spans[b]
             if spans is None:
-                spans = [] if causal_default else [(kv_len - q, kv_len)]
-            sg = L.pkv_build_segments(list(spans), kv_len - q, q)
+                spans = [] if causal_default else [(kv_len - rows, kv_len)]
+            sg = L.pkv_build_segments(list(spans), kv_len - rows, rows)
             segs.append(sg)
             seg_start.append(seg_start[-1] + len(sg))
+        rows_per_seq = [int(q) + a for q, a in zip(query_lens, acts)]
         width = max(len(t) for t in tables) if table_width is None else int(table_width)
         bt = np.zeros((n, width), dtype=np.int32)  # tail padding with block 0, never read
         for b, t in enumerate(tables):
             if len(t) > width:
                 raise ValueError(f"sequence {b} needs {len(t)} table entries, width is {width}")
             bt[b, : len(t)] = t
-        qsl = np.concatenate([[0], np.cumsum(query_lens)]).astype(np.int32)
+        qsl = np.concatenate([[0], np.cumsum(rows_per_seq)]).astype(np.int32)
         plan = cls(
             num_seqs=n,
             block_size=block_size,
-            query_lens=[int(q) for q in query_lens],
+            query_lens=rows_per_seq,
             history_lens=[int(h) for h in history_lens],
             kv_lens=kv_lens,
             tables=tables,
@@ -99,8 +119,11 @@ class ForwardPlan:
             query_start_host=qsl,
             cur_slots_host=np.concatenate(cur_slots).astype(np.int64),
             hist_slots_host=np.concatenate(hist_slots).astype(np.int64) if hist_slots else np.zeros(0, np.int64),
-            max_query_len=int(max(query_lens)),
+            max_query_len=int(max(rows_per_seq)),
             max_seq_len=int(max(kv_lens) if max_seq_len is None else max_seq_len),
+            chunk_lens=[int(q) for q in query_lens],
+            action_lens=acts,
+            act_slots_host=np.concatenate(act_slots).astype(np.int64) if act_slots else np.zeros(0, np.int64),
         )
         if device is not None:
             plan.to(device)
@@ -118,6 +141,7 @@ class ForwardPlan:
         self.seq_order = up(self.seq_order_host)
         self.slot_mapping = up(self.cur_slots_host)
         self.history_slot_mapping = up(self.hist_slots_host)
+        self.action_slot_mapping = up(self.act_slots_host)
         return self
 
     @property
@@ -155,3 +179,58 @@ class ForwardPlan:
                 else:  # rows g in [qs, qe) see g + 1 keys
                     pairs += int((qs + 1 + qe) * (qe - qs) // 2)
         return 4.0 * head_dim * num_q_heads * pairs
+
+
+@dataclass(frozen=True)
+class StagingDecision:
+    """Whether a forward stages its window, and from which block row on."""
+
+    enabled: bool
+    reuse: bool
+    first_block: int
+
+
+class HistoryStaging:
+    """Reuse state of one KV branch's staging buffers (P1
+    ``_prepare_history_staging``).
+
+    The staged window can be kept when nothing about it moved since the last
+    forward: the same session, the same visible history (its length, its
+    blocks), the same capacity and chunk length, and a current chunk that is
+    whole blocks starting on a block edge (a chunk that shares its first block
+    with the history's tail makes the whole window restage).  Then only the
+    current chunk's blocks are gathered again: block rows from the visible
+    history's block count on.  The decision is a host value, the same for all
+    layers of a forward.  One sequence and no action tokens only.
+    """
+
+    def __init__(self, capacity_tokens: int):
+        self.capacity_tokens = int(capacity_tokens)
+        self._session = None  # weak reference to the last session
+        self._signature = None
+
+    def decide(self, session, plan: ForwardPlan) -> StagingDecision:
+        """``session`` identifies the request (compared by identity)."""
+        if plan.num_seqs != 1 or any(plan.action_lens):
+            return StagingDecision(False, False, 0)
+        if plan.max_seq_len > self.capacity_tokens:
+            raise RuntimeError(
+                f"history staging buffers hold {self.capacity_tokens} tokens but this forward stages {plan.max_seq_len}"
+            )
+        B = plan.block_size
+        h, q, kv_len = plan.history_lens[0], plan.chunk_lens[0], plan.kv_lens[0]
+        start_offset = h % B  # where the chunk starts inside its first block
+        current_blocks = -(-(start_offset + q) // B)
+        table = [int(x) for x in plan.tables[0]]
+        history_blocks = tuple(table[: len(table) - current_blocks])
+        signature = (h, history_blocks, int(plan.max_seq_len), q)
+        last = self._session() if self._session is not None else None
+        same_session = last is not None and last is session
+        block_aligned = start_offset == 0 and q % B == 0
+        reuse = same_session and self._signature == signature and block_aligned
+        try:
+            self._session = weakref.ref(session)
+        except TypeError:  # not weakly referenceable: keep it alive instead
+            self._session = (lambda s: (lambda: s))(session)
+        self._signature = signature
+        return StagingDecision(True, bool(reuse), kv_len // B - current_blocks)

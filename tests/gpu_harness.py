@@ -45,6 +45,9 @@ def poisoned_pool(geom, device="cuda"):
 
 def make_plan(wl, device="cuda", **kw):
     g = wl.geom
+    if g.action_lens:
+        kw.setdefault("action_lens", g.action_lens)
+        kw.setdefault("action_block_ids", wl.action_block_ids)
     plan = P.ForwardPlan.build(
         wl.block_ids, g.history_lens, g.query_lens, g.sink_tokens, g.window_tokens, g.full_spans,
         g.causal_default, g.block_size, device=device, **kw,
@@ -62,6 +65,20 @@ def write_layer(plan, pools, li):
     if li.k_hist.shape[0]:
         P.pkv_paged_write(li.k_hist, li.v_hist, plan.history_slot_mapping, pools)
     P.pkv_paged_write(li.k_cur, li.v_cur, plan.slot_mapping, pools)
+    if li.k_act is not None:
+        P.pkv_paged_write(li.k_act, li.v_act, plan.action_slot_mapping, pools)
+
+
+def write_attend(plan, pools, li, geom, workspace="auto", out=None, **staging):
+    """The fused per-layer call: current (and action) writes, then attention."""
+    ws = workspace_for(plan, geom) if workspace == "auto" else workspace
+    acts = {}
+    if li.k_act is not None:
+        acts = dict(action_key=li.k_act, action_value=li.v_act, action_slot_mapping=plan.action_slot_mapping)
+    return P.pkv_paged_write_attn(
+        li.q, li.k_cur, li.v_cur, plan.slot_mapping, pools, plan, softmax_scale(geom.head_dim),
+        out=out, workspace=ws, **acts, **staging,
+    )
 
 
 def workspace_for(plan, geom, device="cuda"):

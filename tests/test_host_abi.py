@@ -154,3 +154,124 @@ def test_validate_metadata_rejects_what_the_pages_reject(pkv):
     seg = plan.segments_host.copy()
     seg[1, 0] += 1  # gap in the tiling
     bad(segments=seg)
+
+
+# --------------------------------------------------------------------------- action tokens and staging reuse
+
+
+def _action_geom(pool="bf16", actions=(3, 17), name="actions"):
+    """Two sequences whose windows end on a block edge, with action tokens."""
+    base = CONFIGS["frame_bf16"] if pool == "bf16" else CONFIGS["tiny_f32"]
+    n = len(actions)
+    return small_variant(
+        base, name=name, num_q_heads=4, num_kv_heads=2 if pool == "bf16" else 4,
+        history_lens=(64, 96)[:n], query_lens=(32, 48)[:n], sink_tokens=(16, 0)[:n],
+        window_tokens=(64, 1 << 30)[:n], full_spans=(None,) * n, action_lens=tuple(actions),
+    )
+
+
+def test_action_table_matches_oracle(pkv):
+    rng = np.random.default_rng(5)
+    for _ in range(200):
+        chunk = int(rng.choice([16, 24, 32, 48]))
+        ticks = int(rng.integers(1, 6))
+        ids = rng.permutation(64)[: ticks * 4 + 4]
+        h = (ticks - 1) * chunk
+        a = int(rng.integers(0, 40))
+        act_ids = rng.permutation(np.arange(100, 110))
+        table, kv_len = pkv.pkv_window_table(ids, h, chunk, chunk, 2 * chunk, 16)
+        win = O.visible_window(ids, h + chunk, chunk, 2 * chunk, 16)
+        try:
+            want = O.with_action_tokens(win, act_ids, a, 16)
+        except ValueError:
+            with pytest.raises(ValueError, match="partly written video block"):
+                pkv.pkv_action_table(table, kv_len, act_ids, a, 16)
+            continue
+        got_table, got_len = pkv.pkv_action_table(table, kv_len, act_ids, a, 16)
+        assert list(got_table) == want.table and got_len == want.kv_len
+
+
+def test_action_table_errors(pkv):
+    with pytest.raises(ValueError):
+        pkv.pkv_action_table([1, 2], 32, [7], 20, 16)  # 20 action tokens need 2 scratch blocks
+    with pytest.raises(ValueError):
+        pkv.pkv_action_table([1, 2], 32, [-3], 2, 16)
+
+
+@pytest.mark.parametrize("actions", [(3, 17), (16, 0)])
+def test_forward_plan_with_actions_matches_oracle_metadata(pkv, actions):
+    geom = _action_geom(actions=actions)
+    wl = make_workload(geom)
+    plan = pkv.ForwardPlan.build(
+        wl.block_ids, geom.history_lens, geom.query_lens, geom.sink_tokens, geom.window_tokens,
+        geom.full_spans, geom.causal_default, geom.block_size,
+        action_lens=geom.action_lens, action_block_ids=wl.action_block_ids,
+    )
+    meta = H.metadata(wl)
+    assert np.array_equal(plan.block_table_host, meta.block_table)
+    assert plan.kv_lens == meta.kv_lens
+    assert np.array_equal(plan.query_start_host, meta.query_start_loc)
+    assert np.array_equal(plan.cur_slots_host, np.concatenate(meta.cur_slots))
+    assert np.array_equal(plan.act_slots_host, np.concatenate(meta.act_slots))
+    flat = [(g.q_start, g.q_end, g.kv_end, 1 if g.mode == "full" else 0) for segs in meta.segments for g in segs]
+    assert [tuple(r) for r in plan.segments_host.tolist()] == flat
+    plan.validate(geom.pool_blocks())
+
+
+def test_forward_plan_refuses_actions_after_a_partly_written_block(pkv):
+    with pytest.raises(ValueError, match="partly written video block"):
+        pkv.ForwardPlan.build([np.array([4, 6])], [0], [24], [0], [48], [None], action_lens=[3],
+                              action_block_ids=[np.array([9])])
+
+
+def _tick_events(seed):
+    """A random run of forwards: AR blocks of 1-3 probes, sessions that change,
+    chunk sizes that are or are not whole blocks, windows that slide."""
+    rng = np.random.default_rng(seed)
+    chunk = int(rng.choice([16, 24, 32]))
+    sink = int(rng.choice([0, chunk]))
+    window = int(rng.choice([2, 3])) * chunk
+    sessions = [object(), object()]
+    cap_blocks = -(-sink // 16) + -(-window // 16) + 2
+    ids = rng.permutation(200)
+    h = 0
+    events = []
+    for _ in range(10):
+        session = sessions[int(rng.integers(0, 2))] if rng.random() < 0.3 else sessions[0]
+        for _probe in range(int(rng.integers(1, 4))):
+            events.append((session, h, chunk, sink, window, cap_blocks * 16, ids))
+        h += chunk
+    return events
+
+
+@pytest.mark.parametrize("seed", range(8))
+def test_history_staging_decisions_match_oracle(pkv, seed):
+    product = pkv.HistoryStaging(capacity_tokens=1 << 20)
+    state = O.StagingState()
+    reused = 0
+    for session, h, chunk, sink, window, max_seq_len, ids in _tick_events(seed):
+        plan = pkv.ForwardPlan.build([ids], [h], [chunk], [sink], [window], [None], max_seq_len=max_seq_len,
+                                     table_width=max_seq_len // 16)
+        got = product.decide(session, plan)
+        win = O.visible_window(ids, h + chunk, sink, window, 16)
+        want = O.staging_decision(state, session, num_seqs=1, action_len=0, capacity_tokens=1 << 20,
+                                  history_tokens=h, window=win, max_seq_len=max_seq_len, chunk_tokens=chunk,
+                                  block_size=16)
+        assert (got.enabled, got.reuse, got.first_block) == want
+        reused += got.reuse
+    assert reused > 0 or _tick_events(seed)[0][2] % 16  # aligned runs must reuse somewhere
+
+
+def test_history_staging_is_off_for_actions_and_batches(pkv):
+    st = pkv.HistoryStaging(capacity_tokens=1024)
+    geom = _action_geom()
+    wl = make_workload(geom)
+    plan = pkv.ForwardPlan.build(wl.block_ids, geom.history_lens, geom.query_lens, geom.sink_tokens,
+                                 geom.window_tokens, geom.full_spans, action_lens=geom.action_lens,
+                                 action_block_ids=wl.action_block_ids)
+    d = st.decide(object(), plan)
+    assert (d.enabled, d.reuse, d.first_block) == (False, False, 0)
+    small = pkv.HistoryStaging(capacity_tokens=16)
+    one = pkv.ForwardPlan.build([np.arange(8)], [32], [16], [0], [48], [None])
+    with pytest.raises(RuntimeError):
+        small.decide(object(), one)

@@ -347,3 +347,128 @@ def test_unwritten_slots_never_reach_the_output():
     wl = make_workload(CONFIGS["tiny_f32"])
     _, _, _, out = H.run_layer(wl)
     assert np.isfinite(out).all()
+
+
+# --------------------------------------------------------------------------- action tokens
+
+
+def test_action_tokens_follow_the_window_like_the_pages_dense_reference():
+    """P2 ``test_paged_attention_matches_dense_reference_cpu`` with actions: the
+    paged result over video window + action scratch blocks equals dense
+    attention over the windowed video K/V with the action K/V appended, the
+    query being the chunk's rows followed by the action rows (full attention)."""
+    rng = np.random.default_rng(7)
+    B, H, D, a = 16, 2, 8, 3
+    history, chunk, window = 3 * B, B, 2 * B
+    end = history + chunk
+    video_ids = [5, 9, 2, 7]  # positions [16 i, 16 i + 16) live in block video_ids[i]
+    action_ids = [11]
+    k_vid = rng.standard_normal((end, H, D)).astype(np.float32)
+    v_vid = rng.standard_normal((end, H, D)).astype(np.float32)
+    k_act = rng.standard_normal((a, H, D)).astype(np.float32)
+    v_act = rng.standard_normal((a, H, D)).astype(np.float32)
+    q = rng.standard_normal((chunk + a, H, D)).astype(np.float32)
+    kp = np.full((16 * B, H, D), np.nan, np.float32)
+    vp = kp.copy()
+    O.paged_write(kp, k_vid, O.slot_mapping(video_ids, np.arange(end), B), O.F32, O.F32)
+    O.paged_write(vp, v_vid, O.slot_mapping(video_ids, np.arange(end), B), O.F32, O.F32)
+    O.paged_write(kp, k_act, O.slot_mapping(action_ids, np.arange(a), B), O.F32, O.F32)
+    O.paged_write(vp, v_act, O.slot_mapping(action_ids, np.arange(a), B), O.F32, O.F32)
+    win = O.with_action_tokens(O.visible_window(video_ids, end, 0, window, B), action_ids, a, B)
+    assert win.table == [2, 7, 11] and win.kv_len == window + a
+    rows = chunk + a
+    segs = O.segments_for_rows([None], [rows], [win.kv_len])
+    got = O.paged_attention(q, O.F32, kp, vp, O.F32, np.array([win.table]), [0, rows], [win.kv_len], segs,
+                            D ** -0.5, B)
+    # the dense reference, built from the source tensors without pools or tables
+    k_ref = np.concatenate([k_vid[-window:], k_act]).astype(np.float64)
+    v_ref = np.concatenate([v_vid[-window:], v_act]).astype(np.float64)
+    limits = np.full(rows, window + a)
+    ref = O.attention_bruteforce(q.astype(np.float64), k_ref, v_ref, limits, D ** -0.5)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+def test_action_tokens_after_a_partly_written_block_are_refused():
+    """P2 ``test_action_tokens_after_a_partly_written_video_block_are_refused``:
+    a 24-token chunk from an empty history ends 8 slots into its second block."""
+    win = O.visible_window([4, 6], 24, 0, 48, 16)
+    assert win.kv_len == 24
+    with pytest.raises(ValueError, match="partly written video block"):
+        O.with_action_tokens(win, [9], 3, 16)
+    assert O.with_action_tokens(win, [9], 0, 16) is win  # no actions: nothing to refuse
+
+
+def test_action_tokens_take_whole_scratch_blocks():
+    win = O.visible_window([1, 2], 32, 0, 32, 16)
+    for a, blocks in ((1, 1), (16, 1), (17, 2), (40, 3)):
+        w = O.with_action_tokens(win, [8, 9, 10], a, 16)
+        assert w.table == [1, 2] + [8, 9, 10][:blocks] and w.kv_len == 32 + a
+        assert w.positions[32:] == [-(1 + i) for i in range(a)]
+
+
+# --------------------------------------------------------------------------- staging reuse
+
+
+def _decide(state, session, history, chunk, B, sink, window, max_seq_len, ids, capacity=1 << 20, actions=0, seqs=1):
+    win = O.visible_window(ids, history + chunk, sink, window, B)
+    return O.staging_decision(state, session, num_seqs=seqs, action_len=actions, capacity_tokens=capacity,
+                              history_tokens=history, window=win, max_seq_len=max_seq_len, chunk_tokens=chunk,
+                              block_size=B)
+
+
+@pytest.mark.parametrize("history_chunks", [0, 1, 2, 3])
+def test_staged_reuse_refreshes_the_current_blocks_at_their_live_offset(history_chunks):
+    """P2 ``test_staged_reuse_refreshes_the_current_blocks_at_their_live_offset``
+    with a window of two 16-token blocks and one-block chunks: the first probe
+    of an AR block restages everything, the second reuses the history and
+    refreshes from the visible history's block count, which is not the end of
+    the padded table (capacity: 2 window blocks + 1 action-capacity block)."""
+    B = 16
+    ids = list(range(100, 100 + history_chunks + 1))
+    state, session = O.StagingState(), object()
+    max_seq_len = 3 * B
+    enabled, reuse, first = _decide(state, session, history_chunks * B, B, B, 0, 2 * B, max_seq_len, ids)
+    assert enabled and not reuse
+    enabled, reuse, first = _decide(state, session, history_chunks * B, B, B, 0, 2 * B, max_seq_len, ids)
+    assert enabled and reuse
+    assert first == min(history_chunks, 1)
+    assert max_seq_len // B - 1 != first
+
+
+def test_ragged_chunks_never_reuse_the_staged_history():
+    """P2 ``test_history_staging_holds_a_ragged_window_and_restages_it_whole``:
+    24-token chunks share a block with the history's tail, so no probe reuses."""
+    B, C = 16, 24
+    state, session = O.StagingState(), object()
+    for chunk in range(6):
+        h = chunk * C
+        ids = list(range(-(-(h + C) // B)))
+        for _probe in range(2):
+            enabled, reuse, _ = _decide(state, session, h, C, B, C, 2 * C, 8 * B, ids)
+            assert enabled and not reuse
+
+
+def test_staging_reuse_needs_the_same_session_and_history():
+    B = 16
+    ids = list(range(10))
+    state = O.StagingState()
+    s1, s2 = object(), object()
+    assert not _decide(state, s1, 64, 32, B, 0, 96, 160, ids)[1]
+    assert _decide(state, s1, 64, 32, B, 0, 96, 160, ids)[1]
+    assert not _decide(state, s2, 64, 32, B, 0, 96, 160, ids)[1]  # another request
+    assert not _decide(state, s2, 96, 32, B, 0, 96, 160, ids)[1]  # the history moved on
+    assert not _decide(state, s2, 96, 32, B, 0, 96, 176, ids)[1]  # a different capacity
+    assert _decide(state, s2, 96, 32, B, 0, 96, 176, ids)[1]
+    moved = list(ids)
+    moved[4] = 77  # the same length but another block in the visible history
+    assert not _decide(state, s2, 96, 32, B, 0, 96, 176, moved)[1]
+
+
+def test_staging_is_off_for_actions_and_batches_and_refuses_a_small_buffer():
+    B = 16
+    state, s = O.StagingState(), object()
+    assert _decide(state, s, 32, 16, B, 0, 48, 64, list(range(4)), actions=3) == (False, False, 0)
+    assert _decide(state, s, 32, 16, B, 0, 48, 64, list(range(4)), seqs=2) == (False, False, 0)
+    assert state.signature is None  # the state is left alone
+    with pytest.raises(RuntimeError):
+        _decide(state, s, 32, 16, B, 0, 48, 64, list(range(4)), capacity=48)

@@ -51,10 +51,24 @@ class Geometry:
     num_blocks: int = 0  # pool size in blocks; 0 -> ceil(1.25 * blocks needed)
     seed: int = 0
     note: str = ""
+    # Action tokens per sequence (empty: none).  They follow the video chunk
+    # in the query and sit in scratch blocks of their own after the window.
+    action_lens: tuple[int, ...] = ()
 
     @property
     def num_seqs(self) -> int:
         return len(self.query_lens)
+
+    def action_len(self, b: int) -> int:
+        return self.action_lens[b] if self.action_lens else 0
+
+    def action_blocks(self, b: int) -> int:
+        return -(-self.action_len(b) // self.block_size)
+
+    @property
+    def query_rows(self) -> tuple[int, ...]:
+        """Query rows per sequence: the video chunk, then the action tokens."""
+        return tuple(q + self.action_len(b) for b, q in enumerate(self.query_lens))
 
     @property
     def ends(self) -> tuple[int, ...]:
@@ -66,7 +80,7 @@ class Geometry:
     def pool_blocks(self) -> int:
         if self.num_blocks:
             return self.num_blocks
-        need = sum(self.logical_blocks(b) for b in range(self.num_seqs))
+        need = sum(self.logical_blocks(b) + self.action_blocks(b) for b in range(self.num_seqs))
         return int(math.ceil(1.25 * need))
 
 
@@ -219,6 +233,8 @@ class LayerInputs:
     k_inv_scale: float = 1.0
     v_scale: float = 1.0
     v_inv_scale: float = 1.0
+    k_act: torch.Tensor | None = None  # action K/V, [sum of action tokens, heads, D]
+    v_act: torch.Tensor | None = None
 
 
 @dataclass
@@ -227,6 +243,8 @@ class Workload:
     device: str
     # block_ids[b][i]: physical block holding positions [16 i, 16 i + 16) of seq b
     block_ids: list[np.ndarray] = field(default_factory=list)
+    # action_block_ids[b][i]: scratch block holding action tokens [16 i, 16 i + 16) of seq b
+    action_block_ids: list[np.ndarray] = field(default_factory=list)
 
     def layer(self, layer: int) -> LayerInputs:
         g = self.geom
@@ -240,15 +258,23 @@ class Workload:
             x = torch.randn((tokens, heads, D), generator=gen, device=self.device, dtype=torch.float32)
             return x.to(act)
 
-        q = draw(cur, Hq)
+        acts = sum(g.action_len(b) for b in range(g.num_seqs))
+        # Query rows in sequence order; each sequence's video rows come before
+        # its action rows.
+        q = draw(cur + acts, Hq)
         k_cur = draw(cur, H)
         v_cur = draw(cur, H)
         k_hist = draw(hist, H)
         v_hist = draw(hist, H)
         li = LayerInputs(k_hist=k_hist, v_hist=v_hist, k_cur=k_cur, v_cur=v_cur, q=q)
+        if acts:
+            li.k_act = draw(acts, H)
+            li.v_act = draw(acts, H)
         if g.pool_dtype == "fp8":
-            li.k_scale, li.k_inv_scale = _fp8_scale(k_hist, k_cur)
-            li.v_scale, li.v_inv_scale = _fp8_scale(v_hist, v_cur)
+            extra = (li.k_act,) if acts else ()
+            li.k_scale, li.k_inv_scale = _fp8_scale(k_hist, k_cur, *extra)
+            extra = (li.v_act,) if acts else ()
+            li.v_scale, li.v_inv_scale = _fp8_scale(v_hist, v_cur, *extra)
         return li
 
 
@@ -272,4 +298,11 @@ def make_workload(geom: Geometry, device: str = "cpu") -> Workload:
             raise ValueError(f"pool of {len(perm)} blocks is too small for {geom.name}")
         ids.append(perm[off : off + n].astype(np.int64))
         off += n
-    return Workload(geom=geom, device=device, block_ids=ids)
+    act_ids = []
+    for b in range(geom.num_seqs):  # scratch blocks for action tokens come after every video block
+        n = geom.action_blocks(b)
+        if off + n > len(perm):
+            raise ValueError(f"pool of {len(perm)} blocks is too small for {geom.name}")
+        act_ids.append(perm[off : off + n].astype(np.int64))
+        off += n
+    return Workload(geom=geom, device=device, block_ids=ids, action_block_ids=act_ids)
