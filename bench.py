@@ -1,13 +1,13 @@
 """Throughput of the paged-attention hot path on one MI355X.
 
-A step is one pass of the path over one batch: the current chunk's K/V is
-scattered into the pools through the slot mapping (pkv_paged_write), then the
-chunk's queries attend over the visible history through the block table
-(pkv_paged_attn, issued as its two halves: the attention kernel, then the
-merge of key splits).  The 40-layer workload runs that pair once per layer,
-each layer with its own pools and inputs, all sharing one metadata plan.
-Inputs, pools and metadata are resident in HBM before timing starts; the
-history is written (untimed) during setup.
+A step is one pass of the path over one batch, issued as one fused call per
+layer (pkv_paged_write_attn): the current chunk's K/V is scattered into the
+pools through the slot mapping, then the chunk's queries attend over the
+visible history through the block table (the attention kernel, then the merge
+of key splits).  The 40-layer workload runs that call once per layer, each
+layer with its own pools and inputs, all sharing one metadata plan.  Inputs,
+pools and metadata are resident in HBM before timing starts; the history is
+written (untimed) during setup.
 
 Prints one JSON line.  `value` is algorithmic attention TFLOP/s over whole
 steps (4 * D * Hq * visible query-key pairs per call).  `roofline` is for the
@@ -16,8 +16,10 @@ library launches on; its `traffic` comes from the committed rocprofv3
 FETCH_SIZE / WRITE_SIZE summary for this workload when that summary was taken
 on the current kernel sources (null otherwise).  `kv_bound` times the same
 kernel on the KV-bound half of the varlen fp8 batch (query length 16) against
-HBM bandwidth.  The merge, the write and the history-staging gather are
-reported under `parts`.
+HBM bandwidth.  `parts` reports the write, the merge and the history-staging
+gather on their own (the per-launch pass issues the three calls separately,
+with events between them), the step as three separate calls per layer, and the
+step captured once in a HIP graph and replayed.
 
     python bench.py [--steps K] [--warmup W] [--workload frame_bf16]
 """
@@ -157,7 +159,16 @@ def run_bench(args, geom):
         return (li.q, pools, plan.block_table, plan.query_start_loc, plan.seq_lens, plan.segments,
                 plan.segment_start_loc, scale, plan.max_query_len, plan.max_seq_len)
 
-    def step(ev=None):
+    def step():
+        """One pass of the path: the fused per-layer call (current K/V slot
+        writes, attention, split merge) for every layer."""
+        for li, pools, out in layers:
+            P.pkv_paged_write_attn(li.q, li.k_cur, li.v_cur, plan.slot_mapping, pools, plan, scale, out=out,
+                                   workspace=ws)
+
+    def separate_step(ev=None):
+        """The same work as three calls per layer (write, attention kernel,
+        merge), with events between the launches when `ev` is given."""
         for i, (li, pools, out) in enumerate(layers):
             if ev is not None:
                 ev[4 * i].record(stream)
@@ -171,34 +182,52 @@ def run_bench(args, geom):
             if ev is not None:
                 ev[4 * i + 3].record(stream)
 
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
+    def timed(fn):
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for _ in range(args.steps):
+            fn()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / args.steps
 
-    # whole-step timing (the number `value` is computed from)
-    t0 = torch.cuda.Event(enable_timing=True)
-    t1 = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    wall0 = time.perf_counter()
-    t0.record(stream)
-    for _ in range(args.steps):
-        step()
-    t1.record(stream)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - wall0
-    step_ms = t0.elapsed_time(t1) / args.steps
+    # Bring the GPU to its sustained state under this load before anything is
+    # measured: back-to-back steps for about a second.  (Kernels run faster
+    # for the first milliseconds of continuous load, before the power
+    # management settles the clocks, so short measurements started from idle
+    # overstate sustained throughput.)
+    settle0 = time.perf_counter()
+    while time.perf_counter() - settle0 < 1.0:
+        for _ in range(16):
+            step()
+        torch.cuda.synchronize()
 
-    # per-launch timing of the same steps, events between the launches
+    # Passes for `parts` and the roofline: the separate calls, per launch with
+    # events between them and as whole steps.
     nl = len(layers)
+    for _ in range(2):
+        separate_step()
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(4 * nl)] for _ in range(args.steps)]
     for k in range(args.steps):
-        step(evs[k])
+        separate_step(evs[k])
     torch.cuda.synchronize()
 
     def mean_gap(a, b):
         return float(np.mean([e[4 * i + a].elapsed_time(e[4 * i + b]) for e in evs for i in range(nl)]))
 
     write_ms, main_ms, merge_ms = mean_gap(0, 1), mean_gap(1, 2), mean_gap(2, 3)
+    separate_ms = timed(separate_step)
+
+    # whole-step timing (the number `value` is computed from): W warm-up
+    # steps, then exactly K timed steps
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    step_ms = timed(step)
+    wall = time.perf_counter() - wall0
 
     # the history-staging gather over the whole visible window, and the
     # contiguous path that attends over the staged buffer (identity table)
@@ -240,6 +269,23 @@ def run_bench(args, geom):
     gather_ms = np.mean([ge[3 * k].elapsed_time(ge[3 * k + 1]) for k in range(args.steps)])
     staged_ms = np.mean([ge[3 * k + 1].elapsed_time(ge[3 * k + 2]) for k in range(args.steps)])
 
+    # The step captured once in a HIP graph and replayed, last: on this
+    # software stack eager launches that follow a graph replay in the same
+    # process run measurably slower, so nothing else is timed after it.
+    side = torch.cuda.Stream()
+    side.wait_stream(stream)
+    with torch.cuda.stream(side):
+        step()
+    stream.wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    torch.cuda.synchronize()
+    graph.replay()
+    graph_ms = timed(graph.replay)
+    del graph
+
     flops = plan.attn_flops(geom.num_q_heads, geom.head_dim)
     abytes = attn_bytes(geom, plan)
     gbytes = 2 * 2 * sum(len(t) for t in plan.tables) * geom.block_size * geom.num_kv_heads * geom.head_dim * ELT[geom.pool_dtype]
@@ -259,6 +305,8 @@ def run_bench(args, geom):
         "gather_ms": gather_ms,
         "gather_gbps": gbytes / (gather_ms * 1e-3) / 1e9,
         "staged_attn_ms": staged_ms,
+        "separate_ms": separate_ms,
+        "graph_ms": graph_ms,
         "plan": plan,
         "layers": nl,
     }
@@ -302,6 +350,12 @@ def run_kv_bound(args):
                  plan.segment_start_loc, scale, plan.max_query_len, plan.max_seq_len)
         P.pkv_paged_attn_main(*args_, out=out, workspace=ws, seq_order=plan.seq_order)
 
+    # sustained state first (back-to-back launches for about half a second)
+    settle0 = time.perf_counter()
+    while time.perf_counter() - settle0 < 0.5:
+        for layer in layers:
+            launch(*layer)
+        torch.cuda.synchronize()
     for _ in range(max(args.warmup, 1)):
         for layer in layers:
             launch(*layer)
@@ -401,9 +455,11 @@ def main():
     import paged_kv_cache_174_amd as P
 
     P.lib()  # fail loudly if the HIP library is missing
+    # The KV-bound leg runs first: the main leg ends with a HIP graph replay,
+    # after which eager launches in the same process run slower.
+    kvb = None if args.no_kv_bound else run_kv_bound(args)
     r = run_bench(args, geom)
     plan = r.pop("plan")
-    kvb = None if args.no_kv_bound else run_kv_bound(args)
     cpu = None if args.no_cpu_baseline else cpu_baseline(geom, args.cpu_budget_s)
     traffic = stored_traffic(geom.name)
     line = {
@@ -455,6 +511,8 @@ def main():
             "paged_attn_call_ms": round(r["main_ms"] + r["merge_ms"], 5),
             "gather_whole_window": {"ms": round(r["gather_ms"], 5), "gbps": round(r["gather_gbps"], 1)},
             "attn_over_staged_buffer_ms": round(r["staged_attn_ms"], 5),
+            "separate_calls_step_ms": round(r["separate_ms"], 5),
+            "graph_replay_step_ms": round(r["graph_ms"], 5),
         },
         "cpu_baseline": cpu,
     }
