@@ -201,6 +201,12 @@ typedef struct {
   const int32_t* segments;           /* device int32 [num_segments][4] */
   const int32_t* segment_start_loc;  /* device int32 [num_seqs + 1] */
   const int32_t* seq_order;          /* device int32 [num_seqs] or NULL */
+  const int32_t* query_pos;          /* device int32 [num_seqs] or NULL: key position of each sequence's
+                                        first query row.  NULL places every query at the end of its keys
+                                        (seq_len - q_len, the AR chunk).  Otherwise sequence b's rows sit at
+                                        [query_pos[b], query_pos[b] + q_len) inside [0, seq_len): a local
+                                        shard of a longer query (P3 piecewise_attn query_ranges), whose
+                                        full segments may still reach past its own end (kv_end) */
   int32_t table_width;
   int32_t num_seqs;
   int32_t max_query_len;
@@ -319,14 +325,17 @@ int pkv_build_segments(const int32_t* full_spans, int32_t num_spans, int32_t que
  * enforce (P3 build_paged_piecewise_plan, P4 row and layout checks):
  * 1 <= q_len <= seq_len <= max_seq_len, q_len <= max_query_len, query_start_loc
  * starts at 0 and is non-decreasing, ceil(seq_len / block_size) <= table_width,
- * referenced table entries in [0, num_blocks), segments tile
- * [seq_len - q_len, seq_len) in order with causal kv_end == q_end and
- * full kv_end in [q_end, seq_len].  Returns PKV_OK or PKV_EINVAL with a message.
+ * referenced table entries in [0, num_blocks), the query rows
+ * [g0, g0 + q_len) inside [0, seq_len) with g0 = query_pos[b] (host, may be
+ * NULL: g0 = seq_len - q_len), segments tiling [g0, g0 + q_len) in order with
+ * causal kv_end == q_end and full kv_end in [q_end, seq_len].  Returns PKV_OK
+ * or PKV_EINVAL with a message.
  */
 int pkv_validate_metadata_host(const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
                                const int32_t* block_table, int32_t table_width, int64_t num_blocks,
                                int32_t block_size, int32_t max_query_len, int32_t max_seq_len,
-                               const int32_t* segments, const int32_t* segment_start_loc);
+                               const int32_t* segments, const int32_t* segment_start_loc,
+                               const int32_t* query_pos);
 
 /* Thread-local description of the last error returned on this thread ("" if none). */
 const char* pkv_last_error(void);

@@ -43,6 +43,7 @@ __all__ = [
     "gather",
     "kernel_view",
     "paged_attention",
+    "piecewise_attention",
     "dense_attention",
     "attention_bruteforce",
 ]
@@ -501,6 +502,52 @@ def paged_attention(
         for hi, h in enumerate(heads):
             hk = h // group
             out[dest, hi] = _softmax_attend(qf[t0 + local, h], k_all[:, hk], v_all[:, hk], limits, float(softmax_scale))
+    return out
+
+
+def piecewise_attention(q_f64: np.ndarray, k_f64: np.ndarray, v_f64: np.ndarray, full_spans, scale: float,
+                        query_ranges=None) -> np.ndarray:
+    """P3 ``piecewise_attn`` for one sequence, float64.
+
+    ``q_f64`` is the local query ``[rows, Hq, D]``; ``k_f64`` / ``v_f64`` the
+    whole key sequence ``[S, Hkv, D]``; ``full_spans`` the full-attention spans
+    in key coordinates.  ``query_ranges`` lists ``(local_start, local_end,
+    global_start)`` triples that must cover the local rows in order (P3 raises
+    ``ValueError`` otherwise); without it the query is the suffix of the keys.
+    Each range is cut into segments by ``build_segments`` at its own global
+    start, and each segment is one attention call as P3 dispatches it: a
+    causal segment ``[s, e)`` attends ``K[:e]`` with the bottom-right causal
+    mask (row at position g sees keys ``j <= g``), a full segment attends
+    ``K[:kv_end]`` unmasked -- ``kv_end`` being the unclipped span end, so a
+    shard's full rows see keys past the shard's own end.  GQA maps query head
+    h to KV head ``h // (Hq // Hkv)``.
+    """
+    rows, Hq, D = q_f64.shape
+    Hkv = k_f64.shape[1]
+    group = Hq // Hkv
+    if query_ranges is None:
+        query_ranges = [(0, rows, k_f64.shape[0] - rows)]
+    out = np.zeros((rows, Hq, D), dtype=np.float64)
+    covered = 0
+    for local_start, local_end, global_start in query_ranges:
+        n = int(local_end) - int(local_start)
+        if int(local_start) != covered or n < 0:
+            raise ValueError("query_ranges must cover local query contiguously")
+        for seg in build_segments(full_spans, int(global_start), n):
+            lo = int(local_start) + seg.q_start - int(global_start)
+            hi = int(local_start) + seg.q_end - int(global_start)
+            keys = seg.kv_end
+            for h in range(Hq):
+                z = (q_f64[lo:hi, h] @ k_f64[:keys, h // group].T) * scale
+                if seg.mode == "causal":
+                    g = np.arange(seg.q_start, seg.q_end)[:, None]
+                    z = np.where(np.arange(keys)[None, :] <= g, z, -np.inf)
+                z = z - z.max(axis=1, keepdims=True)
+                p = np.exp(z)
+                out[lo:hi, h] = (p / p.sum(axis=1, keepdims=True)) @ v_f64[:keys, h // group]
+        covered = int(local_end)
+    if covered != rows:
+        raise ValueError("query_ranges must cover the full local query")
     return out
 
 

@@ -64,6 +64,7 @@ class _AttnMeta(ctypes.Structure):
         ("segments", ctypes.c_void_p),
         ("segment_start_loc", ctypes.c_void_p),
         ("seq_order", ctypes.c_void_p),
+        ("query_pos", ctypes.c_void_p),
         ("table_width", ctypes.c_int32),
         ("num_seqs", ctypes.c_int32),
         ("max_query_len", ctypes.c_int32),
@@ -108,7 +109,7 @@ _SIGNATURES = {
     "pkv_build_segments": (ctypes.c_int, [_PI32, _I32, _I32, _I32, _PI32, _I32, _PI32]),
     "pkv_validate_metadata_host": (
         ctypes.c_int,
-        [_PI32, _PI32, _I32, _PI32, _I32, _I64, _I32, _I32, _I32, _PI32, _PI32],
+        [_PI32, _PI32, _I32, _PI32, _I32, _I64, _I32, _I32, _I32, _PI32, _PI32, _PI32],
     ),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
@@ -380,8 +381,8 @@ def pkv_paged_write_attn(
     window into ``stage_key``/``stage_value`` from ``first_block`` on, and
     attends.  ``meta`` is any object with the attention metadata as device
     tensors (block_table, query_start_loc, seq_lens, segments,
-    segment_start_loc, seq_order or None) and the host ints max_query_len and
-    max_seq_len -- a ForwardPlan is one."""
+    segment_start_loc, seq_order or None, query_pos or None) and the host ints
+    max_query_len and max_seq_len -- a ForwardPlan is one."""
     if q.dim() != 3 or q.shape[2] != pools.head_dim:
         raise ValueError("q must be [tokens, num_q_heads, head_dim]")
     if out is None:
@@ -403,6 +404,9 @@ def pkv_paged_write_attn(
     order = getattr(meta, "seq_order", None)
     if order is not None and order.numel() != num_seqs:
         raise ValueError("seq_order must hold one entry per sequence")
+    qpos = getattr(meta, "query_pos", None)
+    if qpos is not None and qpos.numel() != num_seqs:
+        raise ValueError("query_pos must hold one entry per sequence")
     m = _AttnMeta(
         _dev(bt, "block_table", torch.int32),
         _dev(meta.query_start_loc, "query_start_loc", torch.int32),
@@ -410,6 +414,7 @@ def pkv_paged_write_attn(
         _dev(meta.segments, "segments", torch.int32),
         _dev(meta.segment_start_loc, "segment_start_loc", torch.int32),
         None if order is None else _dev(order, "seq_order", torch.int32),
+        None if qpos is None else _dev(qpos, "query_pos", torch.int32),
         bt.shape[1],
         num_seqs,
         int(meta.max_query_len),
@@ -502,8 +507,12 @@ def pkv_build_segments(full_spans, query_offset: int, query_len: int) -> np.ndar
     return out[: count.value].copy()
 
 
-def pkv_validate_metadata_host(query_start_loc, seq_lens, block_table, num_blocks, block_size, max_query_len, max_seq_len, segments, segment_start_loc):
+def pkv_validate_metadata_host(query_start_loc, seq_lens, block_table, num_blocks, block_size, max_query_len, max_seq_len,
+                               segments, segment_start_loc, query_pos=None):
     qsl, sl, bt = _host_i32(query_start_loc), _host_i32(seq_lens), _host_i32(block_table)
+    qp = None if query_pos is None else _host_i32(query_pos)
+    if qp is not None and qp.size != sl.size:
+        raise ValueError("query_pos needs one entry per sequence")
     seg, sloc = _host_i32(segments).reshape(-1, 4), _host_i32(segment_start_loc)
     if bt.ndim != 2:
         raise ValueError("block_table must be 2-D")
@@ -520,6 +529,7 @@ def pkv_validate_metadata_host(query_start_loc, seq_lens, block_table, num_block
             max_seq_len,
             _ptr(seg, ctypes.c_int32),
             _ptr(sloc, ctypes.c_int32),
+            None if qp is None else _ptr(qp, ctypes.c_int32),
         )
     )
 

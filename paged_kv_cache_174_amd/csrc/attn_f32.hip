@@ -24,7 +24,7 @@ __global__ __launch_bounds__(64 * kWaves) void attn_f32_kernel(AttnArgs a) {
   const int i = blockIdx.x * kWaves + w;
   if (i >= q_len) return;  // whole wave leaves; no block-level barrier below
   const int s = a.seq_lens[b];
-  const int g = s - q_len + i;
+  const int g = (a.query_pos ? a.query_pos[b] : s - q_len) + i;  // the row's key position
   const int L = row_limit(a.segments, a.seg_loc[b], a.seg_loc[b + 1], g);
   const int hk = h / a.group;
   const int64_t row_elems = static_cast<int64_t>(a.num_kv_heads) * D;

@@ -248,7 +248,7 @@ attn_mfma_kernel(AttnArgs a) {
   const int r0 = rt * kMfmaRows;
   if (r0 >= R) return;
   const int seg0 = a.seg_loc[b], seg1 = a.seg_loc[b + 1];
-  const int gbase = s - q_len;
+  const int gbase = a.query_pos ? a.query_pos[b] : s - q_len;  // key position of the first query row
   // Row limits are non-decreasing in the row's key position, so the last row
   // bounds the workgroup's key range and the first row of a wave its mask-free prefix.
   const int wg_kmax = row_limit(a.segments, seg0, seg1, gbase + (min(r0 + kMfmaRows, R) - 1) / G);

@@ -222,8 +222,8 @@ int attn_setup(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num
                const void* kpool, const void* vpool, const int32_t* block_table, int32_t table_width,
                const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs, int32_t max_query_len,
                int32_t max_seq_len, const int32_t* segments, const int32_t* segment_start_loc,
-               const int32_t* seq_order, float softmax_scale, void* out, void* workspace, size_t workspace_bytes,
-               AttnLaunch& L) {
+               const int32_t* seq_order, const int32_t* query_pos, float softmax_scale, void* out, void* workspace,
+               size_t workspace_bytes, AttnLaunch& L) {
   if (int rc = check_pools(pools)) return rc;
   if (!q || !out || !query_start_loc || !seq_lens || !segments || !segment_start_loc)
     return fail(PKV_EINVAL, "q, out and every metadata pointer must be non-NULL");
@@ -259,6 +259,7 @@ int attn_setup(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num
   a.segments = segments;
   a.seg_loc = segment_start_loc;
   a.seq_order = seq_order;
+  a.query_pos = query_pos;
   a.num_q_tokens = num_q_tokens;
   a.table_width = table_width;
   a.num_seqs = num_seqs;
@@ -339,7 +340,7 @@ int paged_attn_impl(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_
   AttnLaunch L;
   if (int rc = attn_setup(q, q_dtype, num_q_tokens, num_q_heads, pools, pools->key, pools->value, block_table,
                           table_width, query_start_loc, seq_lens, num_seqs, max_query_len, max_seq_len, segments,
-                          segment_start_loc, seq_order, softmax_scale, out, workspace, workspace_bytes, L))
+                          segment_start_loc, seq_order, nullptr, softmax_scale, out, workspace, workspace_bytes, L))
     return rc;
   return attn_launch(L, phases, static_cast<hipStream_t>(stream));
 }
@@ -423,7 +424,8 @@ int pkv_paged_write_attn(const void* q, int32_t q_dtype, int64_t num_q_tokens, i
   AttnLaunch L;
   if (int rc = attn_setup(q, q_dtype, num_q_tokens, num_q_heads, pools, kread, vread, table, meta->table_width,
                           meta->query_start_loc, meta->seq_lens, meta->num_seqs, meta->max_query_len,
-                          meta->max_seq_len, meta->segments, meta->segment_start_loc, meta->seq_order, softmax_scale,
+                          meta->max_seq_len, meta->segments, meta->segment_start_loc, meta->seq_order,
+                          meta->query_pos, softmax_scale,
                           out, workspace, workspace_bytes, L))
     return rc;
   // Everything is checked; enqueue in order on one stream.
@@ -582,7 +584,7 @@ int pkv_build_segments(const int32_t* full_spans, int32_t num_spans, int32_t que
 int pkv_validate_metadata_host(const int32_t* qsl, const int32_t* seq_lens, int32_t num_seqs,
                                const int32_t* block_table, int32_t table_width, int64_t num_blocks,
                                int32_t block_size, int32_t max_query_len, int32_t max_seq_len,
-                               const int32_t* segments, const int32_t* seg_loc) {
+                               const int32_t* segments, const int32_t* seg_loc, const int32_t* query_pos) {
   g_error[0] = '\0';
   if (!qsl || !seq_lens || !block_table || !segments || !seg_loc) return fail(PKV_EINVAL, "NULL pointer");
   if (num_seqs <= 0 || table_width <= 0 || block_size <= 0) return fail(PKV_EINVAL, "bad sizes");
@@ -603,9 +605,14 @@ int pkv_validate_metadata_host(const int32_t* qsl, const int32_t* seq_lens, int3
       if (blk < 0 || blk >= num_blocks)
         return fail(PKV_EINVAL, "sequence %d: table entry %lld = %d outside the pool", b, static_cast<long long>(i), blk);
     }
+    // The query rows sit at key positions [g0, g0 + q): the suffix, or a shard.
+    const int32_t g0 = query_pos ? query_pos[b] : s - q;
+    if (g0 < 0 || static_cast<int64_t>(g0) + q > s)
+      return fail(PKV_EINVAL, "sequence %d: query rows [%d, %lld) lie outside its %d keys", b, g0,
+                  static_cast<long long>(g0) + q, s);
     const int32_t s0 = seg_loc[b], s1 = seg_loc[b + 1];
     if (s1 <= s0) return fail(PKV_EINVAL, "sequence %d has no segments", b);
-    int32_t cursor = s - q;
+    int32_t cursor = g0;
     for (int32_t k = s0; k < s1; ++k) {
       const int32_t qs = segments[4 * k], qe = segments[4 * k + 1], kv = segments[4 * k + 2], mode = segments[4 * k + 3];
       if (qs != cursor || qe <= qs) return fail(PKV_EINVAL, "sequence %d: segments must tile the query in order", b);
@@ -618,7 +625,8 @@ int pkv_validate_metadata_host(const int32_t* qsl, const int32_t* seq_lens, int3
       }
       cursor = qe;
     }
-    if (cursor != s) return fail(PKV_EINVAL, "sequence %d: segments end at %d, not at seq_len %d", b, cursor, s);
+    if (cursor != g0 + q)
+      return fail(PKV_EINVAL, "sequence %d: segments end at %d, not at the query's end %d", b, cursor, g0 + q);
   }
   return PKV_OK;
 }

@@ -44,6 +44,14 @@ class ForwardPlan:
     chunk_lens: list[int] = field(default_factory=list)  # current video tokens per sequence
     action_lens: list[int] = field(default_factory=list)
     act_slots_host: np.ndarray = field(default_factory=lambda: np.zeros(0, np.int64))  # [sum a] int64
+    # Full-attention spans each sequence's segments were built from (the AR
+    # default resolved), kept for shard().
+    spans: list = field(default_factory=list)
+    # Query shards (shard()): key position of each entry's first query row,
+    # and the sequence each entry reads.  None: one entry per sequence, its
+    # query at the end of its keys.
+    query_pos_host: np.ndarray | None = None
+    entry_seq: np.ndarray | None = None
     # device copies
     block_table: torch.Tensor | None = None
     query_start_loc: torch.Tensor | None = None
@@ -54,6 +62,7 @@ class ForwardPlan:
     slot_mapping: torch.Tensor | None = None
     history_slot_mapping: torch.Tensor | None = None
     action_slot_mapping: torch.Tensor | None = None
+    query_pos: torch.Tensor | None = None
 
     @classmethod
     def build(
@@ -80,7 +89,7 @@ class ForwardPlan:
         n = len(query_lens)
         acts = [0] * n if action_lens is None else [int(a) for a in action_lens]
         tables, kv_lens, segs, seg_start = [], [], [], [0]
-        cur_slots, hist_slots, act_slots = [], [], []
+        cur_slots, hist_slots, act_slots, used_spans = [], [], [], []
         for b in range(n):
             h, q, a = int(history_lens[b]), int(query_lens[b]), acts[b]
             table, kv_len = L.pkv_window_table(block_ids[b], h, q, sink_tokens[b], window_tokens[b], block_size)
@@ -95,6 +104,7 @@ class ForwardPlan:
             spans = full_spans[b]
             if spans is None:
                 spans = [] if causal_default else [(kv_len - rows, kv_len)]
+            used_spans.append([(int(a_), int(b_)) for a_, b_ in spans])
             sg = L.pkv_build_segments(list(spans), kv_len - rows, rows)
             segs.append(sg)
             seg_start.append(seg_start[-1] + len(sg))
@@ -124,6 +134,7 @@ class ForwardPlan:
             chunk_lens=[int(q) for q in query_lens],
             action_lens=acts,
             act_slots_host=np.concatenate(act_slots).astype(np.int64) if act_slots else np.zeros(0, np.int64),
+            spans=used_spans,
         )
         if device is not None:
             plan.to(device)
@@ -142,7 +153,72 @@ class ForwardPlan:
         self.slot_mapping = up(self.cur_slots_host)
         self.history_slot_mapping = up(self.hist_slots_host)
         self.action_slot_mapping = up(self.act_slots_host)
+        self.query_pos = None if self.query_pos_host is None else up(self.query_pos_host)
         return self
+
+    def shard(self, query_ranges, device=None) -> "ForwardPlan":
+        """Attention metadata for local query shards (P3 ``piecewise_attn``
+        with ``query_ranges``): ``query_ranges[b]`` lists ``(local_start,
+        local_end, global_start)`` triples covering sequence b's local query
+        rows in order from 0; each range becomes one attention entry over
+        sequence b's keys with its rows at key positions ``[global_start,
+        global_start + local_end - local_start)``, its segments cut from the
+        sequence's full spans at that start (a full segment keeps its span's
+        end, so a shard's rows attend past the shard).  The write metadata
+        (slot mappings) is the original plan's."""
+        if len(query_ranges) != self.num_seqs or self.entry_seq is not None:
+            raise ValueError("shard() takes one list of ranges per sequence of an unsharded plan")
+        tables, kv_lens, rows, qpos, entry, segs, seg_start = [], [], [], [], [], [], [0]
+        for b, ranges in enumerate(query_ranges):
+            covered = 0
+            for local_start, local_end, global_start in ranges:
+                n = int(local_end) - int(local_start)
+                if int(local_start) != covered or n < 0:
+                    raise ValueError("query_ranges must cover local query contiguously")
+                covered = int(local_end)
+                if n == 0:
+                    continue
+                if int(global_start) < 0 or int(global_start) + n > self.kv_lens[b]:
+                    raise ValueError(f"sequence {b}: rows [{global_start}, {int(global_start) + n}) lie outside "
+                                     f"its {self.kv_lens[b]} keys")
+                sg = L.pkv_build_segments(self.spans[b], int(global_start), n)
+                tables.append(self.tables[b])
+                kv_lens.append(self.kv_lens[b])
+                rows.append(n)
+                qpos.append(int(global_start))
+                entry.append(b)
+                segs.append(sg)
+                seg_start.append(seg_start[-1] + len(sg))
+        if not rows:
+            raise ValueError("the shards hold no query rows")
+        bt = np.zeros((len(rows), self.block_table_host.shape[1]), dtype=np.int32)
+        for e, b in enumerate(entry):
+            bt[e] = self.block_table_host[b]
+        out = ForwardPlan(
+            num_seqs=len(rows),
+            block_size=self.block_size,
+            query_lens=rows,
+            history_lens=self.history_lens,
+            kv_lens=kv_lens,
+            tables=tables,
+            segments_host=np.concatenate(segs).astype(np.int32),
+            segment_start_host=np.asarray(seg_start, dtype=np.int32),
+            block_table_host=bt,
+            query_start_host=np.concatenate([[0], np.cumsum(rows)]).astype(np.int32),
+            cur_slots_host=self.cur_slots_host,
+            hist_slots_host=self.hist_slots_host,
+            max_query_len=int(max(rows)),
+            max_seq_len=self.max_seq_len,
+            chunk_lens=self.chunk_lens,
+            action_lens=self.action_lens,
+            act_slots_host=self.act_slots_host,
+            spans=self.spans,
+            query_pos_host=np.asarray(qpos, dtype=np.int32),
+            entry_seq=np.asarray(entry, dtype=np.int32),
+        )
+        if device is not None:
+            out.to(device)
+        return out
 
     @property
     def seq_order_host(self) -> np.ndarray:
@@ -164,6 +240,7 @@ class ForwardPlan:
             self.max_seq_len,
             self.segments_host,
             self.segment_start_host,
+            self.query_pos_host,
         )
 
     def attn_flops(self, num_q_heads: int, head_dim: int) -> float:
@@ -171,7 +248,6 @@ class ForwardPlan:
         query-key pairs), counting each multiply-add of QK^T and PV as 2."""
         pairs = 0
         for b in range(self.num_seqs):
-            s, q = self.kv_lens[b], self.query_lens[b]
             lo, hi = self.segment_start_host[b], self.segment_start_host[b + 1]
             for qs, qe, kv, mode in self.segments_host[lo:hi]:
                 if mode == L.PKV_SEG_FULL:

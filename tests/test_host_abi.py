@@ -275,3 +275,39 @@ def test_history_staging_is_off_for_actions_and_batches(pkv):
     one = pkv.ForwardPlan.build([np.arange(8)], [32], [16], [0], [48], [None])
     with pytest.raises(RuntimeError):
         small.decide(object(), one)
+
+
+# --------------------------------------------------------------------------- query shards
+
+
+def test_sharded_plan_matches_the_oracle_segments(pkv):
+    geom = small_variant(CONFIGS["piecewise_gqa_bf16"], history_lens=(100, 40), query_lens=(300, 60),
+                         sink_tokens=(0, 0), window_tokens=(1 << 30,) * 2,
+                         full_spans=(((100, 180), (250, 400)), None))
+    wl = make_workload(geom)
+    plan = pkv.ForwardPlan.build(wl.block_ids, geom.history_lens, geom.query_lens, geom.sink_tokens,
+                                 geom.window_tokens, geom.full_spans)
+    ranges = [[(0, 90, 150), (90, 200, 240)], [(0, 0, 5), (0, 30, 70)]]
+    sh = plan.shard(ranges)
+    sh.validate(geom.pool_blocks())
+    assert sh.num_seqs == 3 and list(sh.entry_seq) == [0, 0, 1]
+    assert list(sh.query_pos_host) == [150, 240, 70] and sh.query_lens == [90, 110, 30]
+    spans = [[(100, 180), (250, 400)], [(40, 100)]]  # sequence 1: the AR default, its whole chunk
+    want = []
+    for (_, n, g0), b in zip([(0, 90, 150), (0, 110, 240), (0, 30, 70)], [0, 0, 1]):
+        want += [(s.q_start, s.q_end, s.kv_end, 1 if s.mode == "full" else 0) for s in O.build_segments(spans[b], g0, n)]
+    assert [tuple(r) for r in sh.segments_host.tolist()] == want
+    assert np.array_equal(sh.block_table_host[1], plan.block_table_host[0])
+
+
+def test_shards_are_checked_like_the_pages_check_them(pkv):
+    plan = pkv.ForwardPlan.build([np.arange(10)], [64], [32], [0], [1 << 30], [None])
+    with pytest.raises(ValueError, match="contiguously"):
+        plan.shard([[(0, 10, 64), (12, 32, 76)]])
+    with pytest.raises(ValueError, match="outside"):
+        plan.shard([[(0, 32, 80)]])
+    bad = plan.shard([[(0, 32, 64)]])
+    with pytest.raises(ValueError):  # the query rows must lie inside the keys
+        pkv.pkv_validate_metadata_host(bad.query_start_host, bad.kv_lens, bad.block_table_host, 10, 16,
+                                       bad.max_query_len, bad.max_seq_len, bad.segments_host,
+                                       bad.segment_start_host, query_pos=[70])

@@ -472,3 +472,68 @@ def test_staging_is_off_for_actions_and_batches_and_refuses_a_small_buffer():
     assert state.signature is None  # the state is left alone
     with pytest.raises(RuntimeError):
         _decide(state, s, 32, 16, B, 0, 48, 64, list(range(4)), capacity=48)
+
+
+# --------------------------------------------------------------------------- query shards
+
+
+def _shard_case(seed=3, S=40, rows=24, Hq=4, Hkv=2, D=8):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((rows, Hq, D))
+    k = rng.standard_normal((S, Hkv, D))
+    v = rng.standard_normal((S, Hkv, D))
+    return q, k, v
+
+
+@pytest.mark.parametrize("spans", [[], [(20, 30)], [(16, 28), (30, 40)], [(0, 40)], [(25, 60)]])
+def test_piecewise_attention_without_ranges_is_the_suffix_rule_by_brute_force(spans):
+    q, k, v = _shard_case()
+    S, rows = k.shape[0], q.shape[0]
+    got = O.piecewise_attention(q, k, v, spans, 0.3)
+    # limits from the rule itself: a row at g sees keys < the unclipped end of the
+    # span holding it, else keys <= g
+    limits = []
+    for i in range(rows):
+        g = S - rows + i
+        holder = [b for a, b in spans if a <= g < b]
+        limits.append(holder[0] if holder else g + 1)
+    limits = np.minimum(np.asarray(limits), S)
+    ref = O.attention_bruteforce(q, k, v, limits, 0.3)
+    np.testing.assert_allclose(got, ref, rtol=0, atol=1e-12)
+
+
+@pytest.mark.parametrize("cuts", [(8,), (5, 17), (1, 2, 23)])
+def test_query_shards_reproduce_the_rows_of_the_whole_query(cuts):
+    """P3 build_segments keeps a full span's unclipped end as kv_end so that a
+    local query shard attends past its own boundary: shards of a query give
+    exactly the rows the whole query gives."""
+    q, k, v = _shard_case(seed=11)
+    S, rows = k.shape[0], q.shape[0]
+    spans = [(18, 26), (30, 40)]
+    whole = O.piecewise_attention(q, k, v, spans, 0.25)
+    edges = [0, *cuts, rows]
+    g0 = S - rows
+    for a, b in zip(edges, edges[1:]):
+        part = O.piecewise_attention(q[a:b], k, v, spans, 0.25, query_ranges=[(0, b - a, g0 + a)])
+        np.testing.assert_allclose(part, whole[a:b], rtol=0, atol=1e-12)
+    ranges = [(a, b, g0 + a) for a, b in zip(edges, edges[1:])]
+    np.testing.assert_allclose(O.piecewise_attention(q, k, v, spans, 0.25, query_ranges=ranges), whole,
+                               rtol=0, atol=1e-12)
+
+
+def test_a_shard_in_the_middle_of_the_keys():
+    """A shard whose rows are not at the end of the keys: causal rows see keys up
+    to themselves, full rows up to their span's end, beyond the shard."""
+    q, k, v = _shard_case(seed=5, S=50, rows=10)
+    spans = [(22, 35)]
+    got = O.piecewise_attention(q, k, v, spans, 0.4, query_ranges=[(0, 10, 18)])  # rows at 18..27
+    limits = np.array([g + 1 if g < 22 else 35 for g in range(18, 28)])
+    np.testing.assert_allclose(got, O.attention_bruteforce(q, k, v, limits, 0.4), rtol=0, atol=1e-12)
+
+
+def test_query_ranges_must_cover_the_local_query_in_order():
+    q, k, v = _shard_case()
+    with pytest.raises(ValueError, match="contiguously"):
+        O.piecewise_attention(q, k, v, [], 0.3, query_ranges=[(0, 10, 16), (12, 24, 28)])
+    with pytest.raises(ValueError, match="full local query"):
+        O.piecewise_attention(q, k, v, [], 0.3, query_ranges=[(0, 10, 16)])
