@@ -337,6 +337,99 @@ int pkv_validate_metadata_host(const int32_t* query_start_loc, const int32_t* se
                                const int32_t* segments, const int32_t* segment_start_loc,
                                const int32_t* query_pos);
 
+/* ------------------------------------------------------------------ window manager */
+
+/*
+ * Host-side block manager behind the pools of one KV branch (P1
+ * ARDiffusionPagedForwardContext with its cache manager; P2's eviction,
+ * compaction, reset and table-shape tests).  Not thread-safe: one manager per
+ * thread, or a lock around it.  Physical block 0 is the null block and is
+ * never handed out, so tables padded with 0 never point at live data.
+ *
+ * Model positions count every token of a request from its start; storage
+ * positions are what the block table indexes.  They agree on the sink's
+ * blocks; past them a storage position is its model position minus the
+ * tokens dropped by compaction, always a whole number of chunks and blocks.
+ *
+ * After a committing forward ends at model position E, the tokens in
+ * [S, E - W) snapped down to a chunk boundary are dead (S = sink tokens, W =
+ * the recent window's tokens); with reset_at_boundary the commit that
+ * completes an AR block of chunks_per_block chunks kills every token past the
+ * sink.  A block is freed once all its written tokens are dead, except a
+ * partly written last block, which the next chunk continues.  Compaction
+ * drops whole multiples of lcm(block_size, chunk_size) tokens of evicted
+ * blocks right after the sink's blocks.
+ */
+typedef struct pkv_window_manager pkv_window_manager;
+
+typedef struct {
+  int64_t num_blocks;         /* physical blocks of the pools; block 0 is the null block */
+  int32_t block_size;
+  int32_t chunk_size;         /* tokens per chunk (one latent frame): the eviction unit */
+  int32_t sink_chunks;        /* leading chunks the window always keeps */
+  int32_t window_chunks;      /* most recent chunks kept, the current one included */
+  int32_t chunks_per_block;   /* chunks per AR block: where reset_at_boundary acts */
+  int32_t reset_at_boundary;  /* nonzero: an AR block's last commit keeps only the sink */
+  int32_t scratch_blocks;     /* blocks reserved per request for uncommitted chunks and action tokens */
+  int32_t compact;            /* nonzero: drop evicted gaps from the tables */
+} pkv_window_config;
+
+/* Most blocks a visible window spans (P1 max_video_blocks): the sink's blocks
+   plus the recent range's, which starts on a chunk boundary at most
+   block_size - gcd(chunk_size, block_size) tokens past a block edge.  The
+   constant table width of the configuration (add the action capacity).
+   -1 for a bad configuration. */
+int32_t pkv_wm_max_video_blocks(const pkv_window_config* cfg);
+
+/* Creates a manager (host memory only).  PKV_EINVAL for a bad configuration. */
+int pkv_wm_create(const pkv_window_config* cfg, pkv_window_manager** out);
+void pkv_wm_destroy(pkv_window_manager* wm);
+
+/* Starts a request (one sequence of one KV branch) and reserves its scratch
+   blocks; *out_request is its id.  PKV_ERANGE when the pool is short. */
+int pkv_wm_begin_request(pkv_window_manager* wm, int32_t* out_request);
+/* Returns every block of the request to the pool. */
+int pkv_wm_end_request(pkv_window_manager* wm, int32_t request);
+
+/*
+ * Prepares a forward of `tokens` video tokens continuing the request's
+ * history, plus `action_tokens` action tokens (P1 ensure_video_slots and
+ * ensure_action_slots).  commit != 0: the tokens go to pool blocks after the
+ * history (continuing its partly written last block) and pkv_wm_commit makes
+ * them history.  commit == 0: they start in the free slots of the history's
+ * last block and continue in scratch blocks, and the request is left as it
+ * was.  Action tokens take scratch blocks after the chunk's.  Writes the
+ * slots (host int64) of the video tokens to out_slots[tokens] and of the
+ * action tokens to out_action_slots[action_tokens].  PKV_ERANGE when the pool
+ * or the scratch blocks are short (nothing changes then).
+ */
+int pkv_wm_prepare(pkv_window_manager* wm, int32_t request, int64_t tokens, int32_t commit, int64_t action_tokens,
+                   int64_t* out_slots, int64_t* out_action_slots);
+
+/*
+ * The visible-window block table of the prepared forward (P1
+ * video_block_table then build_block_table): as pkv_window_table over the
+ * request's storage positions, followed by the action blocks as
+ * pkv_action_table appends them.  Writes the table (host) to out_table,
+ * its length to *out_count, the tokens it holds to *out_kv_len, and the
+ * number of table entries looked up to *out_reads (may be NULL), which
+ * never exceeds pkv_wm_max_video_blocks.
+ */
+int pkv_wm_window_table(const pkv_window_manager* wm, int32_t request, int32_t* out_table, int32_t capacity,
+                        int32_t* out_count, int32_t* out_kv_len, int32_t* out_reads);
+
+/* Ends the prepared forward: a committing one becomes history, then eviction
+   and compaction run; an uncommitted one is dropped. */
+int pkv_wm_commit(pkv_window_manager* wm, int32_t request);
+
+/* out[6] = {committed tokens (storage), committed tokens (model), compacted
+   tokens, table entries, free pool blocks, evicted entries still in the table}. */
+int pkv_wm_info(const pkv_window_manager* wm, int32_t request, int64_t* out);
+
+/* The request's storage block table (host), -1 for an evicted block. */
+int pkv_wm_block_table(const pkv_window_manager* wm, int32_t request, int32_t* out, int32_t capacity,
+                       int32_t* out_count);
+
 /* Thread-local description of the last error returned on this thread ("" if none). */
 const char* pkv_last_error(void);
 

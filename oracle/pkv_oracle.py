@@ -33,6 +33,7 @@ __all__ = [
     "WindowRead",
     "visible_window",
     "with_action_tokens",
+    "WindowModel",
     "StagingState",
     "staging_decision",
     "Segment",
@@ -242,6 +243,64 @@ def with_action_tokens(window: WindowRead, action_block_ids, action_len: int, bl
         kv_len=window.kv_len + a,
         positions=list(window.positions) + [-(1 + i) for i in range(a)],
     )
+
+
+class WindowModel:
+    """Which tokens a request keeps, in model positions only (no physical
+    blocks, no compaction): the rules the pages' eviction and reset tests
+    state (P2 ``test_attention_after_eviction_reads_every_kept_token_and_nothing_unwritten``,
+    ``test_compaction_does_not_change_which_tokens_stay_resident``; P1
+    ``video_block_table``), taken as this model:
+
+    * the sink is the first ``sink_chunks`` chunks, the recent window the last
+      ``window_chunks`` chunks including the current one;
+    * after a commit that ends at E, no later window starts before E - W, so
+      the whole chunks before that point, past the sink, are dead; with
+      ``reset_at_boundary``, a commit completing ``chunks_per_block`` chunks
+      kills everything past the sink;
+    * a block stays while any token written in it is alive, and a partly
+      written last block stays in any case (the next chunk continues it);
+    * a forward reads the visible window (``visible_window``) over the blocks
+      that stay plus the blocks its own tokens occupy.
+    """
+
+    def __init__(self, block_size: int, chunk_size: int, sink_chunks: int, window_chunks: int,
+                 reset_at_boundary: bool = False, chunks_per_block: int = 1):
+        self.B, self.C = int(block_size), int(chunk_size)
+        self.S = int(sink_chunks) * self.C
+        self.W = int(window_chunks) * self.C
+        self.reset = bool(reset_at_boundary)
+        self.per_block = int(chunks_per_block)
+        self.end = 0  # committed tokens
+        self.chunks = 0
+        self.kept = set()  # model block indices that stay
+
+    def window(self, tokens: int, action_tokens: int = 0) -> WindowRead:
+        """Positions a forward of ``tokens`` tokens after the history reads,
+        then its action tokens (labelled -1, -2, ...)."""
+        B = self.B
+        end = self.end + int(tokens)
+        ids = [k if (k in self.kept or (k + 1) * B > self.end) else -1 for k in range(-(-end // B))]
+        win = visible_window(ids, end, self.S, self.W, B)
+        if action_tokens:
+            win = with_action_tokens(win, list(range(10**6, 10**6 + -(-int(action_tokens) // B))), action_tokens, B)
+        return win
+
+    def commit(self, tokens: int) -> None:
+        B, C = self.B, self.C
+        start = self.end
+        self.end += int(tokens)
+        self.chunks += int(tokens) // C
+        self.kept |= set(range(start // B, -(-self.end // B)))
+        if self.reset and self.chunks % self.per_block == 0:
+            dead_end = self.end
+        else:
+            dead_end = max(self.end - self.W, 0) // C * C
+        tail = (self.end - 1) // B if self.end % B else None
+        for k in sorted(self.kept):
+            first, last = k * B, min((k + 1) * B, self.end)
+            if first >= self.S and last <= dead_end and k != tail:
+                self.kept.discard(k)
 
 
 @dataclass

@@ -33,3 +33,4 @@ from ._lib import (  # noqa: F401
     pkv_window_table,
 )
 from .plan import ForwardPlan, HistoryStaging, StagingDecision  # noqa: F401
+from .window import WindowConfig, WindowManager  # noqa: F401

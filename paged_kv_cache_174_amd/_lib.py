@@ -72,6 +72,20 @@ class _AttnMeta(ctypes.Structure):
     ]
 
 
+class _WindowConfig(ctypes.Structure):
+    _fields_ = [
+        ("num_blocks", ctypes.c_int64),
+        ("block_size", ctypes.c_int32),
+        ("chunk_size", ctypes.c_int32),
+        ("sink_chunks", ctypes.c_int32),
+        ("window_chunks", ctypes.c_int32),
+        ("chunks_per_block", ctypes.c_int32),
+        ("reset_at_boundary", ctypes.c_int32),
+        ("scratch_blocks", ctypes.c_int32),
+        ("compact", ctypes.c_int32),
+    ]
+
+
 class _Staging(ctypes.Structure):
     _fields_ = [
         ("stage_key", ctypes.c_void_p),
@@ -111,6 +125,16 @@ _SIGNATURES = {
         ctypes.c_int,
         [_PI32, _PI32, _I32, _PI32, _I32, _I64, _I32, _I32, _I32, _PI32, _PI32, _PI32],
     ),
+    "pkv_wm_max_video_blocks": (ctypes.c_int32, [ctypes.POINTER(_WindowConfig)]),
+    "pkv_wm_create": (ctypes.c_int, [ctypes.POINTER(_WindowConfig), ctypes.POINTER(ctypes.c_void_p)]),
+    "pkv_wm_destroy": (None, [_P]),
+    "pkv_wm_begin_request": (ctypes.c_int, [_P, _PI32]),
+    "pkv_wm_end_request": (ctypes.c_int, [_P, _I32]),
+    "pkv_wm_prepare": (ctypes.c_int, [_P, _I32, _I64, _I32, _I64, _PI64, _PI64]),
+    "pkv_wm_window_table": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32, _PI32, _PI32]),
+    "pkv_wm_commit": (ctypes.c_int, [_P, _I32]),
+    "pkv_wm_info": (ctypes.c_int, [_P, _I32, _PI64]),
+    "pkv_wm_block_table": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }

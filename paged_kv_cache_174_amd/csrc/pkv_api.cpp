@@ -161,6 +161,54 @@ int fail(int code, const char* fmt, ...) {
   return code;
 }
 
+// P1 video_block_table: index ranges that can hold a kept token are the
+// sink's blocks and every block from the one holding the recent window's
+// first position to the last written one; a block is read whole, so its
+// length is min(B, end - first_position), and only the last block read may be
+// partly written.
+int window_read(BlockAt block_at, const void* ctx, int64_t history_tokens, int64_t query_tokens,
+                int64_t sink_tokens, int64_t window_tokens, int32_t block_size, int32_t* out_table,
+                int32_t capacity, int32_t* out_count, int32_t* out_kv_len, int64_t* reads) {
+  if (!out_table || !out_count || !out_kv_len) return fail(PKV_EINVAL, "NULL pointer");
+  if (block_size <= 0 || history_tokens < 0 || query_tokens <= 0 || sink_tokens < 0)
+    return fail(PKV_EINVAL, "bad sizes");
+  if (window_tokens < query_tokens)
+    return fail(PKV_EINVAL, "the recent window (%lld) must hold the current chunk (%lld)",
+                static_cast<long long>(window_tokens), static_cast<long long>(query_tokens));
+  const int64_t B = block_size;
+  const int64_t end = history_tokens + query_tokens;
+  const int64_t need_blocks = (end + B - 1) / B;
+  const int64_t sink_end = std::min(sink_tokens, end);
+  const int64_t sink_blocks = (sink_end + B - 1) / B;
+  const int64_t recent_start = std::max<int64_t>(end - window_tokens, 0);
+  const int64_t recent_first = std::max(recent_start / B, sink_blocks);
+  int32_t count = 0;
+  int64_t kv_len = 0;
+  int64_t prev_len = B;
+  auto take = [&](int64_t i) -> int {
+    const int32_t blk = block_at(ctx, i);
+    ++*reads;
+    if (blk < 0) return PKV_OK;  // evicted: nothing of it is read
+    if (prev_len != B)
+      return fail(PKV_EWINDOW, "block %d is partly written but block %d follows it", out_table[count - 1], blk);
+    if (count >= capacity) return fail(PKV_ERANGE, "table capacity %d too small", capacity);
+    const int64_t len = std::min<int64_t>(B, end - i * B);
+    out_table[count++] = blk;
+    kv_len += len;
+    prev_len = len;
+    return PKV_OK;
+  };
+  for (int64_t i = 0; i < sink_blocks; ++i)
+    if (int rc = take(i)) return rc;
+  for (int64_t i = recent_first; i < need_blocks; ++i)
+    if (int rc = take(i)) return rc;
+  if (count == 0) return fail(PKV_EINVAL, "the window holds no resident block");
+  if (kv_len > INT32_MAX) return fail(PKV_ERANGE, "window longer than 2^31 tokens");
+  *out_count = count;
+  *out_kv_len = static_cast<int32_t>(kv_len);
+  return PKV_OK;
+}
+
 }  // namespace pkv
 
 using namespace pkv;
@@ -465,49 +513,15 @@ int pkv_window_table(const int32_t* block_ids, int64_t num_block_ids, int64_t hi
                      int32_t capacity, int32_t* out_count, int32_t* out_kv_len) {
   g_error[0] = '\0';
   if (!block_ids || !out_table || !out_count || !out_kv_len) return fail(PKV_EINVAL, "NULL pointer");
-  if (block_size <= 0 || history_tokens < 0 || query_tokens <= 0 || sink_tokens < 0)
-    return fail(PKV_EINVAL, "bad sizes");
-  if (window_tokens < query_tokens)
-    return fail(PKV_EINVAL, "the recent window (%lld) must hold the current chunk (%lld)",
-                static_cast<long long>(window_tokens), static_cast<long long>(query_tokens));
-  const int64_t B = block_size;
-  const int64_t end = history_tokens + query_tokens;
-  const int64_t need_blocks = (end + B - 1) / B;
+  if (block_size <= 0 || history_tokens < 0 || query_tokens <= 0) return fail(PKV_EINVAL, "bad sizes");
+  const int64_t need_blocks = (history_tokens + query_tokens + block_size - 1) / block_size;
   if (num_block_ids < need_blocks)
     return fail(PKV_EINVAL, "%lld block ids given, %lld needed", static_cast<long long>(num_block_ids),
                 static_cast<long long>(need_blocks));
-  // Index ranges that can hold a kept token (P1 video_block_table): the sink's
-  // blocks, then every block from the one holding the recent window's first
-  // position to the last written one.  A block is read whole, so its length
-  // is min(B, end - first_position).
-  const int64_t sink_end = std::min(sink_tokens, end);
-  const int64_t sink_blocks = (sink_end + B - 1) / B;
-  const int64_t recent_start = std::max<int64_t>(end - window_tokens, 0);
-  const int64_t recent_first = std::max(recent_start / B, sink_blocks);
-  int32_t count = 0;
-  int64_t kv_len = 0;
-  int64_t prev_len = B;
-  auto take = [&](int64_t i) -> int {
-    const int32_t blk = block_ids[i];
-    if (blk < 0) return PKV_OK;  // evicted: nothing of it is read
-    if (prev_len != B)
-      return fail(PKV_EWINDOW, "block %d is partly written but block %d follows it", out_table[count - 1], blk);
-    if (count >= capacity) return fail(PKV_ERANGE, "table capacity %d too small", capacity);
-    const int64_t len = std::min<int64_t>(B, end - i * B);
-    out_table[count++] = blk;
-    kv_len += len;
-    prev_len = len;
-    return PKV_OK;
-  };
-  for (int64_t i = 0; i < sink_blocks; ++i)
-    if (int rc = take(i)) return rc;
-  for (int64_t i = recent_first; i < need_blocks; ++i)
-    if (int rc = take(i)) return rc;
-  if (count == 0) return fail(PKV_EINVAL, "the window holds no resident block");
-  if (kv_len > INT32_MAX) return fail(PKV_ERANGE, "window longer than 2^31 tokens");
-  *out_count = count;
-  *out_kv_len = static_cast<int32_t>(kv_len);
-  return PKV_OK;
+  int64_t reads = 0;
+  return window_read([](const void* ctx, int64_t i) { return static_cast<const int32_t*>(ctx)[i]; }, block_ids,
+                     history_tokens, query_tokens, sink_tokens, window_tokens, block_size, out_table, capacity,
+                     out_count, out_kv_len, &reads);
 }
 
 // P1 build_block_table: action K/V sits in scratch blocks listed after the

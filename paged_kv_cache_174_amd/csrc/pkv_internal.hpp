@@ -14,6 +14,20 @@ namespace pkv {
 // Records a printf-style message as the thread's last error and returns `code`.
 int fail(int code, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 
+// ----------------------------------------------------------------- host metadata
+
+// Physical block at storage block index i of a sequence, negative when it is
+// not resident.
+typedef int32_t (*BlockAt)(const void* ctx, int64_t i);
+
+// The visible-window read (pkv_window_table): the resident blocks holding a
+// sink or recent-window position, in position order, and the tokens they hold.
+// Only the sink's block indices and those from the recent window's start on
+// are looked up; *reads counts the lookups.
+int window_read(BlockAt block_at, const void* ctx, int64_t history_tokens, int64_t query_tokens,
+                int64_t sink_tokens, int64_t window_tokens, int32_t block_size, int32_t* out_table,
+                int32_t capacity, int32_t* out_count, int32_t* out_kv_len, int64_t* reads);
+
 // ----------------------------------------------------------------- write / gather
 
 struct WriteArgs {

@@ -537,3 +537,68 @@ def test_query_ranges_must_cover_the_local_query_in_order():
         O.piecewise_attention(q, k, v, [], 0.3, query_ranges=[(0, 10, 16), (12, 24, 28)])
     with pytest.raises(ValueError, match="full local query"):
         O.piecewise_attention(q, k, v, [], 0.3, query_ranges=[(0, 10, 16)])
+
+
+# --------------------------------------------------------------------------- window residency model
+
+
+def _kept_positions(end, sink, window):
+    return set(range(min(sink, end))) | set(range(max(end - window, 0), end))
+
+
+@pytest.mark.parametrize("sink_chunks,window_chunks,reset", [(1, 2, False), (0, 2, False), (1, 3, False),
+                                                              (2, 2, True), (0, 2, True)])
+def test_window_model_reads_every_kept_token_and_nothing_unwritten(sink_chunks, window_chunks, reset):
+    """P2 ``test_attention_after_eviction_reads_every_kept_token_and_nothing_unwritten``
+    with 24-token chunks against 16-token blocks: every token the window keeps
+    (when it is still resident) is read, every token read was written, and
+    eviction happens."""
+    C, B = 24, 16
+    m = O.WindowModel(B, C, sink_chunks, window_chunks, reset, chunks_per_block=2)
+    evicted = False
+    for _ in range(10):
+        win = m.window(C)
+        end = m.end + C
+        read = [p for p in win.positions]
+        assert all(0 <= p < end for p in read) and len(set(read)) == len(read) and read == sorted(read)
+        resident = {p for p in range(end) if p // B in m.kept or p >= m.end}
+        want = _kept_positions(end, m.S, m.W) & resident
+        assert want <= set(read)
+        # whole blocks: what is read beyond the kept tokens shares a block with one
+        assert {p // B for p in read} <= {p // B for p in want}
+        m.commit(C)
+        evicted = evicted or len(m.kept) < -(-m.end // B)
+    assert evicted
+
+
+def test_window_model_reset_keeps_only_the_sink_across_a_boundary():
+    """P2: the reset case keeps only the sink across a boundary, so the recent
+    window reaches back over blocks that are no longer resident."""
+    C, B = 32, 16  # chunks are whole blocks: no partly written tail survives the reset
+    m = O.WindowModel(B, C, 1, 3, reset_at_boundary=True, chunks_per_block=2)
+    m.commit(C)
+    m.commit(C)  # completes an AR block
+    assert m.kept == {0, 1}  # the sink's blocks
+    win = m.window(C)
+    assert win.positions == list(range(C)) + list(range(2 * C, 3 * C))
+
+
+def test_window_model_shipped_geometry():
+    """P2 ``test_the_shipped_geometry_reads_exactly_the_window_on_every_tick``:
+    1560-token frames, 16-token blocks, a 9-frame sink and window, three
+    frames per tick: every kept token is read, and the window stays within
+    the width bound (whole blocks add at most B - 1 tokens at each of its two
+    boundaries)."""
+    C, B = 1560, 16
+    m = O.WindowModel(B, C, 9, 9)
+    filled = False
+    for _ in range(12):
+        win = m.window(3 * C)
+        end = m.end + 3 * C
+        assert _kept_positions(end, m.S, m.W) <= set(win.positions)
+        assert win.kv_len <= m.S + m.W + 2 * (B - 1)
+        filled = filled or end > m.S + m.W
+        m.commit(3 * C)
+    assert filled
+    # residency is bounded by the window, not by the history
+    assert len(m.kept) <= -(-m.S // B) + -(-(m.W + 3 * C) // B) + 1
