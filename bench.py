@@ -175,10 +175,12 @@ def run_bench(args, geom):
             P.pkv_paged_write(li.k_cur, li.v_cur, plan.slot_mapping, pools)
             if ev is not None:
                 ev[4 * i + 1].record(stream)
-            P.pkv_paged_attn_main(*attn_args(li, pools), out=out, workspace=ws, seq_order=plan.seq_order)
+            P.pkv_paged_attn_main(*attn_args(li, pools), out=out, workspace=ws, seq_order=plan.seq_order,
+                                  host_seq_lens=plan.kv_lens)
             if ev is not None:
                 ev[4 * i + 2].record(stream)
-            P.pkv_paged_attn_merge(*attn_args(li, pools), out=out, workspace=ws, seq_order=plan.seq_order)
+            P.pkv_paged_attn_merge(*attn_args(li, pools), out=out, workspace=ws, seq_order=plan.seq_order,
+                                   host_seq_lens=plan.kv_lens)
             if ev is not None:
                 ev[4 * i + 3].record(stream)
 
@@ -250,7 +252,7 @@ def run_bench(args, geom):
     def staged_attn():
         P.pkv_paged_attn(li.q, staged, ident, plan.query_start_loc, plan.seq_lens, plan.segments,
                          plan.segment_start_loc, scale, plan.max_query_len, plan.max_seq_len, out=out,
-                         workspace=ws, seq_order=plan.seq_order)
+                         workspace=ws, seq_order=plan.seq_order, host_seq_lens=plan.kv_lens)
 
     if args.copy_calibration:
         copy_calibration(pools)
@@ -348,7 +350,8 @@ def run_kv_bound(args):
     def launch(li, pools, out):
         args_ = (li.q, pools, plan.block_table, plan.query_start_loc, plan.seq_lens, plan.segments,
                  plan.segment_start_loc, scale, plan.max_query_len, plan.max_seq_len)
-        P.pkv_paged_attn_main(*args_, out=out, workspace=ws, seq_order=plan.seq_order)
+        P.pkv_paged_attn_main(*args_, out=out, workspace=ws, seq_order=plan.seq_order,
+                              host_seq_lens=plan.kv_lens)
 
     # sustained state first (back-to-back launches for about half a second)
     settle0 = time.perf_counter()
@@ -370,7 +373,8 @@ def run_kv_bound(args):
             ev[k + 1].record(stream)
             P.pkv_paged_attn_merge(layer[0].q, layer[1], plan.block_table, plan.query_start_loc, plan.seq_lens,
                                    plan.segments, plan.segment_start_loc, scale, plan.max_query_len,
-                                   plan.max_seq_len, out=layer[2], workspace=ws, seq_order=plan.seq_order)
+                                   plan.max_seq_len, out=layer[2], workspace=ws, seq_order=plan.seq_order,
+                                   host_seq_lens=plan.kv_lens)
             k += 2
     torch.cuda.synchronize()
     ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 2)]))

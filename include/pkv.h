@@ -145,6 +145,12 @@ int pkv_gather(const pkv_pools* pools, const int32_t* block_ids, int32_t n_block
  *                     the order in which the sequences' work is handed to the GPU.
  *                     Longest first (the ForwardPlan's choice) lets short sequences fill
  *                     in behind long ones; the result does not depend on it.
+ *   host_seq_lens     host int32 [num_seqs] or NULL: the seq_lens values, as a planning
+ *                     hint.  With short query chunks (at most 64 rows per KV head) the
+ *                     library then cuts each sequence into key ranges by its own length and
+ *                     hands the non-empty ranges out first, so they cover the CUs evenly.
+ *                     The result is the same up to rounding whatever the hint (stale
+ *                     hints, e.g. in a replayed graph, only cost speed).
  *   out               device, same shape and dtype as q
  *   workspace         device scratch for split-key partial results, or NULL;
  *                     pkv_paged_attn_workspace_size() gives the size that lets the
@@ -158,8 +164,8 @@ int pkv_paged_attn(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t
                    const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
                    const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
                    int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
-                   const int32_t* segment_start_loc, const int32_t* seq_order, float softmax_scale, void* out, void* workspace,
-                   size_t workspace_bytes, void* stream);
+                   const int32_t* segment_start_loc, const int32_t* seq_order, const int32_t* host_seq_lens,
+                   float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * The two halves of pkv_paged_attn, with its arguments, meaning and errors:
@@ -176,14 +182,14 @@ int pkv_paged_attn_main(const void* q, int32_t q_dtype, int64_t num_q_tokens, in
                         const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
                         const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
                         int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
-                        const int32_t* segment_start_loc, const int32_t* seq_order, float softmax_scale, void* out, void* workspace,
-                        size_t workspace_bytes, void* stream);
+                        const int32_t* segment_start_loc, const int32_t* seq_order, const int32_t* host_seq_lens,
+                        float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream);
 int pkv_paged_attn_merge(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads,
                          const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
                          const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
                          int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
-                         const int32_t* segment_start_loc, const int32_t* seq_order, float softmax_scale, void* out, void* workspace,
-                         size_t workspace_bytes, void* stream);
+                         const int32_t* segment_start_loc, const int32_t* seq_order, const int32_t* host_seq_lens,
+                         float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
  * Attention metadata of one forward, shared by every layer (P1
@@ -201,6 +207,7 @@ typedef struct {
   const int32_t* segments;           /* device int32 [num_segments][4] */
   const int32_t* segment_start_loc;  /* device int32 [num_seqs + 1] */
   const int32_t* seq_order;          /* device int32 [num_seqs] or NULL */
+  const int32_t* host_seq_lens;      /* host int32 [num_seqs] or NULL: planning hint, as for pkv_paged_attn */
   const int32_t* query_pos;          /* device int32 [num_seqs] or NULL: key position of each sequence's
                                         first query row.  NULL places every query at the end of its keys
                                         (seq_len - q_len, the AR chunk).  Otherwise sequence b's rows sit at

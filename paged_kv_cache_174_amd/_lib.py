@@ -64,6 +64,7 @@ class _AttnMeta(ctypes.Structure):
         ("segments", ctypes.c_void_p),
         ("segment_start_loc", ctypes.c_void_p),
         ("seq_order", ctypes.c_void_p),
+        ("host_seq_lens", ctypes.c_void_p),
         ("query_pos", ctypes.c_void_p),
         ("table_width", ctypes.c_int32),
         ("num_seqs", ctypes.c_int32),
@@ -103,7 +104,7 @@ _PI32 = ctypes.POINTER(ctypes.c_int32)
 _PI64 = ctypes.POINTER(ctypes.c_int64)
 _PPOOLS = ctypes.POINTER(_Pools)
 
-_ATTN_ARGS = [_P, _I32, _I64, _I32, _PPOOLS, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P, _F32, _P, _P, _SZ, _P]
+_ATTN_ARGS = [_P, _I32, _I64, _I32, _PPOOLS, _P, _I32, _P, _P, _I32, _I32, _I32, _P, _P, _P, _P, _F32, _P, _P, _SZ, _P]
 
 _SIGNATURES = {
     "pkv_paged_write": (ctypes.c_int, [_P, _P, _I32, _I64, _P, _PPOOLS, _P]),
@@ -299,11 +300,14 @@ def pkv_paged_attn(
     workspace: torch.Tensor | None = None,
     stream=None,
     seq_order: torch.Tensor | None = None,
+    host_seq_lens=None,
     _entry: str = "pkv_paged_attn",
 ) -> torch.Tensor:
     """Paged attention (see include/pkv.h).  ``seq_order`` (int32 [num_seqs], a
     permutation) is the order the sequences' work is dispatched in, e.g.
-    ForwardPlan.seq_order (longest first); it does not change the result."""
+    ForwardPlan.seq_order (longest first); ``host_seq_lens`` (host ints, e.g.
+    ForwardPlan.kv_lens) lets the library plan the work split from the
+    sequences' own lengths.  Neither changes the result beyond rounding."""
     if q.dim() != 3 or q.shape[2] != pools.head_dim:
         raise ValueError("q must be [tokens, num_q_heads, head_dim]")
     if out is None:
@@ -320,6 +324,7 @@ def pkv_paged_attn(
         if seq_order.numel() != num_seqs:
             raise ValueError("seq_order must hold one entry per sequence")
         order_ptr = _dev(seq_order, "seq_order", torch.int32)
+    hl = _host_lens(host_seq_lens, num_seqs)
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
@@ -341,6 +346,7 @@ def pkv_paged_attn(
             _dev(segments, "segments", torch.int32),
             _dev(segment_start_loc, "segment_start_loc", torch.int32),
             order_ptr,
+            None if hl is None else _ptr(hl, ctypes.c_int32),
             float(softmax_scale),
             _dev(out, "out"),
             ws_ptr,
@@ -361,6 +367,15 @@ def pkv_paged_attn_merge(*args, **kwargs) -> torch.Tensor:
     if kwargs.get("out") is None:
         raise ValueError("pkv_paged_attn_merge needs the `out` its pkv_paged_attn_main call wrote")
     return pkv_paged_attn(*args, _entry="pkv_paged_attn_merge", **kwargs)
+
+
+def _host_lens(lens, num_seqs):
+    if lens is None:
+        return None
+    a = _host_i32(lens)
+    if a.size != num_seqs:
+        raise ValueError("host_seq_lens needs one entry per sequence")
+    return a
 
 
 def _kv_rows(key, value, slot_mapping, pools, what):
@@ -405,8 +420,9 @@ def pkv_paged_write_attn(
     window into ``stage_key``/``stage_value`` from ``first_block`` on, and
     attends.  ``meta`` is any object with the attention metadata as device
     tensors (block_table, query_start_loc, seq_lens, segments,
-    segment_start_loc, seq_order or None, query_pos or None) and the host ints
-    max_query_len and max_seq_len -- a ForwardPlan is one."""
+    segment_start_loc, seq_order or None, query_pos or None), the host ints
+    max_query_len and max_seq_len, and optionally kv_lens (host sequence
+    lengths, a planning hint) -- a ForwardPlan is one."""
     if q.dim() != 3 or q.shape[2] != pools.head_dim:
         raise ValueError("q must be [tokens, num_q_heads, head_dim]")
     if out is None:
@@ -431,6 +447,7 @@ def pkv_paged_write_attn(
     qpos = getattr(meta, "query_pos", None)
     if qpos is not None and qpos.numel() != num_seqs:
         raise ValueError("query_pos must hold one entry per sequence")
+    hl = _host_lens(getattr(meta, "kv_lens", None), num_seqs)
     m = _AttnMeta(
         _dev(bt, "block_table", torch.int32),
         _dev(meta.query_start_loc, "query_start_loc", torch.int32),
@@ -438,6 +455,7 @@ def pkv_paged_write_attn(
         _dev(meta.segments, "segments", torch.int32),
         _dev(meta.segment_start_loc, "segment_start_loc", torch.int32),
         None if order is None else _dev(order, "seq_order", torch.int32),
+        None if hl is None else hl.ctypes.data,
         None if qpos is None else _dev(qpos, "query_pos", torch.int32),
         bt.shape[1],
         num_seqs,

@@ -229,16 +229,57 @@ attn_mfma_kernel(AttnArgs a) {
   // (counted in dispatch order: sequences as seq_order lists them, KV heads
   // fastest) goes to XCD g % 8, which spreads every sequence over the XCDs
   // and keeps their loads balanced.
-  const uint32_t xcd = blockIdx.x & 7u, pos = blockIdx.x >> 3;
-  const uint32_t per_group = static_cast<uint32_t>(a.num_splits) * static_cast<uint32_t>(a.row_tiles);
-  const uint32_t grp = xcd + 8u * (pos / per_group);
-  if (grp >= static_cast<uint32_t>(a.num_seqs) * static_cast<uint32_t>(a.num_kv_heads)) return;
-  const uint32_t item = pos % per_group;
-  const int rt = static_cast<int>(item % static_cast<uint32_t>(a.row_tiles));
-  const int z = static_cast<int>(item / static_cast<uint32_t>(a.row_tiles));
-  const int hk = static_cast<int>(grp % static_cast<uint32_t>(a.num_kv_heads));
-  const int b_pos = static_cast<int>(grp / static_cast<uint32_t>(a.num_kv_heads));
-  const int b = a.seq_order ? a.seq_order[b_pos] : b_pos;
+  int rt, z, hk, b;
+  if (SHORT && a.packed) {
+    // Short query chunks planned from the sequences' lengths (one row tile):
+    // the key ranges (sequence in seq_order, split z < ceil(seq_len /
+    // split_len), KV head fastest) come first, then the empty ranges of every
+    // sequence, which only record empty partials.  Each workgroup finds its
+    // own item by walking the sequences (few: the host caps their number).
+    const int H = a.num_kv_heads;
+    int i = static_cast<int>(blockIdx.x);
+    if (i >= a.num_seqs * H * a.num_splits) return;
+    int found = -1, loc = 0;
+    for (int bp = 0; bp < a.num_seqs && found < 0; ++bp) {
+      const int bb = a.seq_order ? a.seq_order[bp] : bp;
+      const int n = min(a.num_splits, (max(a.seq_lens[bb], 1) + a.split_len - 1) / a.split_len);
+      if (i < n * H) {
+        found = bb;
+        loc = i;
+      } else {
+        i -= n * H;
+      }
+    }
+    if (found < 0) {  // an empty range
+      for (int bp = 0; bp < a.num_seqs && found < 0; ++bp) {
+        const int bb = a.seq_order ? a.seq_order[bp] : bp;
+        const int n = min(a.num_splits, (max(a.seq_lens[bb], 1) + a.split_len - 1) / a.split_len);
+        const int empties = (a.num_splits - n) * H;
+        if (i < empties) {
+          found = bb;
+          loc = n * H + i;
+        } else {
+          i -= empties;
+        }
+      }
+      if (found < 0) return;
+    }
+    b = found;
+    rt = 0;
+    z = loc / H;
+    hk = loc % H;
+  } else {
+    const uint32_t xcd = blockIdx.x & 7u, pos = blockIdx.x >> 3;
+    const uint32_t per_group = static_cast<uint32_t>(a.num_splits) * static_cast<uint32_t>(a.row_tiles);
+    const uint32_t grp = xcd + 8u * (pos / per_group);
+    if (grp >= static_cast<uint32_t>(a.num_seqs) * static_cast<uint32_t>(a.num_kv_heads)) return;
+    const uint32_t item = pos % per_group;
+    rt = static_cast<int>(item % static_cast<uint32_t>(a.row_tiles));
+    z = static_cast<int>(item / static_cast<uint32_t>(a.row_tiles));
+    hk = static_cast<int>(grp % static_cast<uint32_t>(a.num_kv_heads));
+    const int b_pos = static_cast<int>(grp / static_cast<uint32_t>(a.num_kv_heads));
+    b = a.seq_order ? a.seq_order[b_pos] : b_pos;
+  }
 
   const int G = a.group;
   const int t0 = a.qsl[b];
@@ -582,64 +623,134 @@ attn_mfma_kernel(AttnArgs a) {
   auto kt_of = [&](int t) { return k_begin + t * KT; };
 
   if constexpr (kF8Lds && SHORT) {
-    // ---- fp8 short path: four tiles per step, one per key group, loaded one
-    // step ahead into the other half of the eight fp8 buffers.
-    // Direct loads of tiles t_first + j0, t_first + j0 + 1 into buffers
-    // 4 set + j0, 4 set + j0 + 1.
-    auto issue2 = [&](int set, int t_first, int j0) {
-      int e[2];
+    // ---- fp8 short path: 32-key tiles, four per step (one per key group),
+    // in a ring of four steps of buffers, so three steps (96 KB per CU) are
+    // in flight while one is multiplied.  Step i uses set i % 4; after the
+    // barrier closing step i - 1, the loads of step i + 3 go into that step's
+    // set.  Wave w loads half of tile w / 2 of each step (one 16-key block of
+    // K and of V, two direct loads each), the very tile its key group
+    // multiplies.
+    constexpr int KT32 = 32;
+    constexpr int kTile32 = KT32 * D;  // bytes of one fp8 K (or V) tile
+    const int ntiles32 = (k_end - k_begin + KT32 - 1) / KT32;
+    const int nsteps = (ntiles32 + 3) / 4;
+    const int ld_part = w & 1;  // which 16-key block of the tile this wave loads
+    // lane: row (ld_part * 16 + 8 * sub + lane / 8) of the tile, global chunk
+    // (lane % 8) ^ swizzle of that row at LDS slot lane % 8
+    const int ld_r8 = lane >> 3;
+    uint32_t ld_k[2], ld_v[2];
 #pragma unroll
-      for (int j = 0; j < 2; ++j) e[j] = (t_first + j0 + j < ntiles) ? stage_entry(kt_of(t_first + j0 + j)) : 0;
+    for (int sub = 0; sub < 2; ++sub) {
+      const int r = 16 * ld_part + 8 * sub + ld_r8;
+      ld_k[sub] = static_cast<uint32_t>((r & 15) * row_bytes + 16 * (dl_pos ^ f8_swz_k(r)));
+      ld_v[sub] = static_cast<uint32_t>((r & 15) * row_bytes + 16 * (dl_pos ^ f8_swz_v(r)));
+    }
+    auto tile_exists = [&](int step) { return 4 * step + kg < ntiles32; };  // kg == w / 2
+    auto issue_step = [&](int step) {
+      if (!tile_exists(step)) return;
+      const int set = step & 3;
+      const int kt = k_begin + KT32 * (4 * step + kg);
+      const int blk = (kt >> 4) + ld_part;
+      const int e = (blk < blk_hi) ? tbl[blk - blk_lo] : 0;
+      const int64_t boff = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(e)) * block_bytes;
+      const int row0 = kt + 16 * ld_part;  // key of the first row this wave loads
+      uint8_t* kdst = f8k_base + (4 * set + kg) * kTile32 + 16 * ld_part * D;
+      uint8_t* vdst = f8v_base + (4 * set + kg) * kTile32 + 16 * ld_part * D;
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        if (t_first + j0 + j >= ntiles) break;
-        issue1(4 * set + j0 + j, t_first + j0 + j, e[j]);
+      for (int sub = 0; sub < 2; ++sub) {
+        if (row0 + 8 * sub + 8 <= kv_lim) {  // all eight rows exist (uniform)
+          dma16(kpool + boff, ld_k[sub], kdst + 8 * sub * D);
+          dma16(vpool + boff, ld_v[sub], vdst + 8 * sub * D);
+        } else {  // rows past kv_lim read zeros
+          const bool ok = row0 + 8 * sub + ld_r8 < kv_lim;
+          dma16(ok ? kpool + boff + ld_k[sub] : f8_zero, kdst + 8 * sub * D);
+          dma16(ok ? vpool + boff + ld_v[sub] : f8_zero, vdst + 8 * sub * D);
+        }
       }
     };
-    // Step i computes from buffers 4 (i % 2) ..  The loads of step i + 2 go
-    // into the same buffers once every wave has left step i: tiles 0, 1 of it
-    // right after the barrier closing step i, tiles 2, 3 after the QK products
-    // of step i + 1 (issuing all eight loads at once would stall every wave's
-    // instruction stream on the vector-memory queue at the same moment).
-    issue2(0, 0, 0);
-    issue2(0, 0, 2);
-    issue2(1, 4, 0);
-    issue2(1, 4, 2);
-    // Step 0 has landed once at most the second group's loads (two per tile
-    // of tiles 4 .. 7) are outstanding.
-    switch (min(4, max(0, ntiles - 4))) {
-      case 4: wait_vmcnt<8>(); break;
-      case 3: wait_vmcnt<6>(); break;
-      case 2: wait_vmcnt<4>(); break;
-      case 1: wait_vmcnt<2>(); break;
-      default: wait_vmcnt<0>(); break;
-    }
+    // Waits until this wave's loads of step `step` have landed, given which
+    // later steps it has issued (four loads per step and wave).
+    auto wait_step = [&](int step, int issued_upto) {
+      const int later = (issued_upto >= step + 1 && tile_exists(step + 1)) + (issued_upto >= step + 2 && tile_exists(step + 2));
+      switch (later) {
+        case 2: wait_vmcnt<8>(); break;
+        case 1: wait_vmcnt<4>(); break;
+        default: wait_vmcnt<0>(); break;
+      }
+    };
+    issue_step(0);
+    issue_step(1);
+    issue_step(2);
+    wait_step(0, 2);
     lds_barrier();
-    f32x16 sacc[2];
-    int pend = -1;  // set whose tiles 2, 3 of step t4 / 4 + 1 are still to be issued
-    for (int t4 = 0, set = 0; t4 < ntiles; t4 += 4, set ^= 1) {
-      const int t = t4 + kg;
-      if (t < ntiles && kt_of(t) < wave_kmax) {
-        qk8(4 * set + kg, sacc);
-        if (pend >= 0) {
-          issue2(pend, t4 + 4, 2);
-          pend = -1;
+    for (int step = 0; step < nsteps; ++step) {
+      issue_step(step + 3);  // into the set of step - 1, which every wave has left
+      const int set = step & 3;
+      const int kt = k_begin + KT32 * (4 * step + kg);
+      if (tile_exists(step) && kt < wave_kmax) {
+        const int buf = 4 * set + kg;
+        f32x16 sc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = 0.f;
+#pragma unroll
+        for (int mm = 0; mm < 4; ++mm) {
+          const u32x4 c = *lds_at<u32x4>(k8_rd[mm] + buf * kTile32);
+          const bf16x8 k0 = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(u32x2{c[0], c[1]}));
+          const bf16x8 k1 = __builtin_bit_cast(bf16x8, e4m3x8_to_bf16x8(u32x2{c[2], c[3]}));
+          sc = mfma(k0, qf[2 * mm], sc);
+          sc = mfma(k1, qf[2 * mm + 1], sc);
         }
-        mask_and_rescale(kt_of(t), sacc);
-        bf16x8 pb[2][2];
-        probs(sacc, pb);
-        pv8(4 * set + kg, pb);
+        if (kt + KT32 > wave_kmin) {
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int j = kt + 8 * (r >> 2) + 4 * h2 + (r & 3);
+            if (j >= Lrow) sc[r] = -INFINITY;
+          }
+        }
+        float c4[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) c4[i] = fmaxf(fmaxf(fmaxf(sc[i], sc[i + 4]), sc[i + 8]), sc[i + 12]);
+        const float mx = max_halves(fmaxf(fmaxf(fmaxf(c4[0], c4[1]), c4[2]), c4[3]));
+        const bool grow = (mx - m) * sl > kRescaleLog2;  // false for NaN (-inf - -inf)
+        if (__builtin_amdgcn_ballot_w64(grow)) {
+          const float m_new = fmaxf(m, mx);
+          const float alpha = (m == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m - m_new) * sl);
+          l *= alpha;
+#pragma unroll
+          for (int db = 0; db < 4; ++db)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) o[db][r] *= alpha;
+          m = m_new;
+        }
+        const float mc = (m == -INFINITY) ? 0.f : m * sl;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) sc[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], sl, -mc));
+        float ls[4] = {0.f, 0.f, 0.f, 0.f};
+        bf16x8 pb[2];
+#pragma unroll
+        for (int k16 = 0; k16 < 2; ++k16) {
+          u32x4 pk;
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            pk[e] = pack_bf16_rne(sc[8 * k16 + 2 * e], sc[8 * k16 + 2 * e + 1]);
+            ls[e] = add_bf16_pair(pk[e], ls[e]);
+          }
+          pb[k16] = __builtin_bit_cast(bf16x8, pk);
+        }
+        l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
+#pragma unroll
+        for (int k16 = 0; k16 < 2; ++k16)
+#pragma unroll
+          for (int db = 0; db < 4; ++db) {
+            const uint32_t addr = v8_rd[db] + buf * kTile32 + 16 * k16 * D;
+            const v2i32 c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32_ptr)(addr));
+            const bf16x8 va = __builtin_bit_cast(
+                bf16x8, e4m3x8_to_bf16x8(u32x2{static_cast<uint32_t>(c[0]), static_cast<uint32_t>(c[1])}));
+            o[db] = mfma(va, pb[k16], o[db]);
+          }
       }
-      if (pend >= 0) {
-        issue2(pend, t4 + 4, 2);
-        pend = -1;
-      }
-      wait_vmcnt<0>();  // this wave's share of step i + 1 has landed
+      wait_step(step + 1, step + 3);  // this wave's share of step + 1 has landed
       lds_barrier();
-      if (t4 + 8 < ntiles) {
-        issue2(set, t4 + 8, 0);
-        pend = set;
-      }
     }
   } else if constexpr (SHORT) {
     // ---- bf16 short path: each wave multiplies tile 4 i + kg from buffer kg

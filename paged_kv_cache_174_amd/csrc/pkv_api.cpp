@@ -60,6 +60,7 @@ struct SplitPlan {
   int splits;
   int split_len;
   bool short_rows;  // the short-query kernel (at most kShortRows rows per KV head)
+  bool packed;      // short rows: the launch hands out real work first (see plan_short_packed)
 };
 
 // Number of key splits for the MFMA kernel.  One workgroup occupies a CU, so
@@ -68,12 +69,64 @@ struct SplitPlan {
 // partial results' round trip through memory and a combine launch.  Pick the
 // split count with the smallest modelled time, never cutting the key range
 // below 512 keys and never needing more workspace than the caller gave.
+// Short query chunks with the sequences' lengths known on the host: every
+// (sequence, KV head) is cut into ceil(len / L) key ranges of L keys, and the
+// launch hands these ranges out first, ahead of the empty ones, so that they
+// spread over all CUs.  L (a multiple of the short kernel's 128-key step) is
+// the one with the smallest modelled time: rounds of one workgroup per CU,
+// each streaming its L keys at a measured per-CU rate after a fixed start-up
+// cost, plus the partials' round trip.
+constexpr int kMaxPackedSeqs = 64;  // the kernel finds its work by scanning the sequences
+bool plan_short_packed(SplitPlan& p, int64_t num_q_tokens, int num_q_heads, int num_kv_heads, int num_seqs,
+                       int max_seq_len, const int32_t* host_lens, size_t workspace_bytes, bool have_workspace,
+                       int kv_elem_bytes) {
+  if (!host_lens || num_seqs > kMaxPackedSeqs || !have_workspace) return false;
+  const int cus = cu_count();
+  const int64_t per_split_bytes = num_q_tokens * num_q_heads * (128 + 2) * static_cast<int64_t>(sizeof(float));
+  constexpr double kCuBytesPerS = 20e9;  // K+V streamed by one short-kernel workgroup
+  constexpr double kWgStart = 4e-6;      // s: start-up and epilogue of one workgroup
+  constexpr double kPartialBw = 5.0e12;
+  constexpr double kCombineLaunch = 3e-6;
+  constexpr int kStep = 128;
+  const double key_bytes = 2.0 * 128 * kv_elem_bytes;
+  const int l_min = std::max(kStep, (max_seq_len + kMaxSplits - 1) / kMaxSplits);
+  double best_t = 1e30;
+  int best_l = 0;
+  for (int L = (l_min + kStep - 1) / kStep * kStep; L <= kMaxSplitKeys - kStep; L += kStep) {
+    const int splits = (max_seq_len + L - 1) / L;
+    if (splits > 1 && workspace_bytes < static_cast<size_t>(per_split_bytes) * splits) {
+      if (L >= max_seq_len) break;
+      continue;
+    }
+    int64_t items = 0;
+    for (int b = 0; b < num_seqs; ++b) items += (std::max(host_lens[b], 1) + L - 1) / L;
+    items *= num_kv_heads;
+    const double rounds = std::ceil(static_cast<double>(items) / cus);
+    double t = rounds * (L * key_bytes / kCuBytesPerS + kWgStart);
+    if (splits > 1) t += 2.0 * per_split_bytes * splits / kPartialBw + kCombineLaunch;
+    if (t < best_t * 0.98) {
+      best_t = t;
+      best_l = L;
+    }
+    if (L >= max_seq_len) break;
+  }
+  if (best_l == 0) return false;
+  p.split_len = best_l;
+  p.splits = (max_seq_len + best_l - 1) / best_l;
+  p.packed = p.splits > 1;
+  return true;
+}
+
 SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, int num_seqs, int max_query_len,
-                      int max_seq_len, size_t workspace_bytes, bool have_workspace) {
+                      int max_seq_len, size_t workspace_bytes, bool have_workspace, const int32_t* host_lens = nullptr,
+                      int kv_elem_bytes = 2) {
   SplitPlan p{};
   const int group = num_q_heads / num_kv_heads;
   p.short_rows = static_cast<int64_t>(max_query_len) * group <= kShortRows;
   p.row_tiles = static_cast<int>((static_cast<int64_t>(max_query_len) * group + kMfmaRows - 1) / kMfmaRows);
+  if (p.short_rows && plan_short_packed(p, num_q_tokens, num_q_heads, num_kv_heads, num_seqs, max_seq_len, host_lens,
+                                        workspace_bytes, have_workspace, kv_elem_bytes))
+    return p;
   const int64_t base = static_cast<int64_t>(num_seqs) * num_kv_heads * p.row_tiles;
   const int cus = cu_count();
   const int max_by_len = std::max(1, max_seq_len / 512);
@@ -244,8 +297,11 @@ size_t pkv_paged_attn_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, 
     return 0;
   SplitPlan p = plan_splits(num_q_tokens, num_q_heads, num_kv_heads, num_seqs, max_query_len, max_seq_len,
                             static_cast<size_t>(-1), true);
-  if (p.splits <= 1) return 0;
-  return static_cast<size_t>(p.splits) * static_cast<size_t>(num_q_tokens) * num_q_heads * (head_dim + 2) * sizeof(float);
+  // Short query chunks may be planned from the sequences' own lengths, with
+  // up to kMaxSplits splits (their rows are few).
+  const int splits = p.short_rows ? std::max(p.splits, std::min(kMaxSplits, (max_seq_len + 127) / 128)) : p.splits;
+  if (splits <= 1) return 0;
+  return static_cast<size_t>(splits) * static_cast<size_t>(num_q_tokens) * num_q_heads * (head_dim + 2) * sizeof(float);
 }
 
 }  // extern "C"
@@ -270,8 +326,8 @@ int attn_setup(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num
                const void* kpool, const void* vpool, const int32_t* block_table, int32_t table_width,
                const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs, int32_t max_query_len,
                int32_t max_seq_len, const int32_t* segments, const int32_t* segment_start_loc,
-               const int32_t* seq_order, const int32_t* query_pos, float softmax_scale, void* out, void* workspace,
-               size_t workspace_bytes, AttnLaunch& L) {
+               const int32_t* seq_order, const int32_t* query_pos, const int32_t* host_lens, float softmax_scale,
+               void* out, void* workspace, size_t workspace_bytes, AttnLaunch& L) {
   if (int rc = check_pools(pools)) return rc;
   if (!q || !out || !query_start_loc || !seq_lens || !segments || !segment_start_loc)
     return fail(PKV_EINVAL, "q, out and every metadata pointer must be non-NULL");
@@ -335,7 +391,8 @@ int attn_setup(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num
   if (pools->head_dim != 128)
     return fail(PKV_EUNSUPPORTED, "bf16/fp8 attention supports head_dim 128, not %d", pools->head_dim);
   const SplitPlan p = plan_splits(num_q_tokens, num_q_heads, pools->num_kv_heads, num_seqs, max_query_len,
-                                  max_seq_len, workspace_bytes, workspace != nullptr);
+                                  max_seq_len, workspace_bytes, workspace != nullptr, host_lens,
+                                  pools->dtype == PKV_FP8_E4M3 ? 1 : 2);
   if (p.splits > kMaxSplits)
     return fail(PKV_EUNSUPPORTED, "max_seq_len %d needs more than %d key splits", max_seq_len, kMaxSplits);
   if (p.splits > 1 &&
@@ -347,6 +404,7 @@ int attn_setup(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num
   a.row_tiles = p.row_tiles;
   a.num_splits = p.splits;
   a.split_len = p.split_len;
+  a.packed = p.packed ? 1 : 0;
   if (p.splits > 1) {
     const int64_t rows = num_q_tokens * num_q_heads;
     a.ws_o = static_cast<float*>(workspace);
@@ -380,15 +438,17 @@ int paged_attn_impl(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_
                     const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
                     const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
                     int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
-                    const int32_t* segment_start_loc, const int32_t* seq_order, float softmax_scale, void* out,
-                    void* workspace, size_t workspace_bytes, void* stream, unsigned phases) {
+                    const int32_t* segment_start_loc, const int32_t* seq_order, const int32_t* host_seq_lens,
+                    float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream,
+                    unsigned phases) {
   g_error[0] = '\0';
   if (!block_table) return fail(PKV_EINVAL, "block_table must not be NULL");
   if (!pools) return fail(PKV_EINVAL, "pools is NULL");
   AttnLaunch L;
   if (int rc = attn_setup(q, q_dtype, num_q_tokens, num_q_heads, pools, pools->key, pools->value, block_table,
                           table_width, query_start_loc, seq_lens, num_seqs, max_query_len, max_seq_len, segments,
-                          segment_start_loc, seq_order, nullptr, softmax_scale, out, workspace, workspace_bytes, L))
+                          segment_start_loc, seq_order, nullptr, host_seq_lens, softmax_scale, out, workspace,
+                          workspace_bytes, L))
     return rc;
   return attn_launch(L, phases, static_cast<hipStream_t>(stream));
 }
@@ -401,12 +461,12 @@ extern "C" {
   const void *q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads, const pkv_pools *pools,          \
       const int32_t *block_table, int32_t table_width, const int32_t *query_start_loc, const int32_t *seq_lens, \
       int32_t num_seqs, int32_t max_query_len, int32_t max_seq_len, const int32_t *segments,                    \
-      const int32_t *segment_start_loc, const int32_t *seq_order, float softmax_scale, void *out, void *workspace, \
-      size_t workspace_bytes, void *stream
+      const int32_t *segment_start_loc, const int32_t *seq_order, const int32_t *host_seq_lens, float softmax_scale, \
+      void *out, void *workspace, size_t workspace_bytes, void *stream
 #define PKV_ATTN_ARGS                                                                                       \
   q, q_dtype, num_q_tokens, num_q_heads, pools, block_table, table_width, query_start_loc, seq_lens,         \
-      num_seqs, max_query_len, max_seq_len, segments, segment_start_loc, seq_order, softmax_scale, out,      \
-      workspace, workspace_bytes, stream
+      num_seqs, max_query_len, max_seq_len, segments, segment_start_loc, seq_order, host_seq_lens, softmax_scale, \
+      out, workspace, workspace_bytes, stream
 
 int pkv_paged_attn(PKV_ATTN_PARAMS) { return paged_attn_impl(PKV_ATTN_ARGS, kPhaseMain | kPhaseMerge); }
 int pkv_paged_attn_main(PKV_ATTN_PARAMS) { return paged_attn_impl(PKV_ATTN_ARGS, kPhaseMain); }
@@ -473,7 +533,7 @@ int pkv_paged_write_attn(const void* q, int32_t q_dtype, int64_t num_q_tokens, i
   if (int rc = attn_setup(q, q_dtype, num_q_tokens, num_q_heads, pools, kread, vread, table, meta->table_width,
                           meta->query_start_loc, meta->seq_lens, meta->num_seqs, meta->max_query_len,
                           meta->max_seq_len, meta->segments, meta->segment_start_loc, meta->seq_order,
-                          meta->query_pos, softmax_scale,
+                          meta->query_pos, meta->host_seq_lens, softmax_scale,
                           out, workspace, workspace_bytes, L))
     return rc;
   // Everything is checked; enqueue in order on one stream.

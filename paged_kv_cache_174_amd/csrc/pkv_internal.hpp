@@ -83,6 +83,7 @@ struct AttnArgs {
   int32_t row_tiles;  // query-row tiles per (sequence, KV head)
   int32_t num_splits;
   int32_t split_len;  // keys per split, a multiple of the key tile
+  int32_t packed;     // short rows: workgroups take the non-empty key ranges first
   float scale_log2;   // softmax_scale * k_scale * log2(e)
   float v_scale;
 };

@@ -94,7 +94,7 @@ def attend(plan, pools, li, geom, workspace="auto", out=None):
     return P.pkv_paged_attn(
         li.q, pools, plan.block_table, plan.query_start_loc, plan.seq_lens, plan.segments,
         plan.segment_start_loc, softmax_scale(geom.head_dim), plan.max_query_len, plan.max_seq_len,
-        out=out, workspace=ws, seq_order=plan.seq_order,
+        out=out, workspace=ws, seq_order=plan.seq_order, host_seq_lens=plan.kv_lens,
     )
 
 

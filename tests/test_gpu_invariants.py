@@ -75,7 +75,8 @@ def test_one_workspace_serves_calls_of_different_shapes():
 @pytest.mark.parametrize("kind", ["fp8", "fp8_short", "bf16"])
 def test_dispatch_order_does_not_change_the_result(kind):
     """The sequences' dispatch order (natural, longest first, reversed) only
-    changes which workgroup runs when: the bits are the same."""
+    changes which workgroup runs when: with the same work split (the same
+    length hint), the bits are the same."""
     import paged_kv_cache_174_amd as P
 
     geom = GEOMS[kind]
@@ -88,7 +89,7 @@ def test_dispatch_order_does_not_change_the_result(kind):
             plan.segment_start_loc, H.softmax_scale(geom.head_dim), plan.max_query_len, plan.max_seq_len)
     rev = torch.arange(plan.num_seqs - 1, -1, -1, dtype=torch.int32, device="cuda")
     for order in (None, plan.seq_order, rev):
-        out = P.pkv_paged_attn(*args, workspace=ws, seq_order=order)
+        out = P.pkv_paged_attn(*args, workspace=ws, seq_order=order, host_seq_lens=plan.kv_lens)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), ref.view(torch.int16))
 
@@ -108,9 +109,10 @@ def test_main_then_merge_equals_one_call(kind):
         args = (li.q, pools, plan.block_table, plan.query_start_loc, plan.seq_lens, plan.segments,
                 plan.segment_start_loc, H.softmax_scale(geom.head_dim), plan.max_query_len, plan.max_seq_len)
         out = torch.empty_like(li.q)
-        P.pkv_paged_attn_main(*args, out=out, workspace=ws)
-        P.pkv_paged_attn_merge(*args, out=out, workspace=ws)
-        one = P.pkv_paged_attn(*args, workspace=ws)
+        kw = dict(workspace=ws, seq_order=plan.seq_order, host_seq_lens=plan.kv_lens)  # the harness's plan
+        P.pkv_paged_attn_main(*args, out=out, **kw)
+        P.pkv_paged_attn_merge(*args, out=out, **kw)
+        one = P.pkv_paged_attn(*args, **kw)
         torch.cuda.synchronize()
         assert torch.equal(out.view(torch.int16), one.view(torch.int16))
         if ws is not None:
@@ -247,3 +249,29 @@ def test_nothing_past_seq_len_is_read():
     out2 = G.attend(plan, pools, li, geom)
     torch.cuda.synchronize()
     assert torch.equal(out1.view(torch.int16), out2.view(torch.int16))
+
+
+def test_length_hint_changes_only_the_work_split():
+    """The host length hint re-plans the short-query work split; with it,
+    without it, and with a stale one the output matches the oracle and the
+    three agree within rounding."""
+    geom = small_variant(CONFIGS["varlen_fp8"], name="hint_fp8", num_q_heads=8, num_kv_heads=2,
+                         history_lens=(6000, 700, 90, 3100), query_lens=(16, 16, 3, 16), sink_tokens=(0,) * 4,
+                         window_tokens=(1 << 30,) * 4, full_spans=(None,) * 4)
+    wl = make_workload(geom, device="cuda")
+    li = wl.layer(0)
+    plan = G.make_plan(wl)
+    pools = G.make_pools(geom, li)
+    G.write_layer(plan, pools, li)
+    ws = G.workspace_for(plan, geom)
+    args = (li.q, pools, plan.block_table, plan.query_start_loc, plan.seq_lens, plan.segments,
+            plan.segment_start_loc, H.softmax_scale(geom.head_dim), plan.max_query_len, plan.max_seq_len)
+    G.say("length hint", geom.name)
+    outs = [G.P.pkv_paged_attn(*args, workspace=ws, seq_order=plan.seq_order, host_seq_lens=hint)
+            for hint in (plan.kv_lens, None, [plan.max_seq_len] * plan.num_seqs, [1] * plan.num_seqs)]
+    torch.cuda.synchronize()
+    _, _, _, ref = H.run_layer(wl, li=li)
+    for o in outs:
+        got = G.as_f64(o)
+        assert np.isfinite(got).all() and np.max(np.abs(got - ref)) <= 6e-2
+        assert np.max(np.abs(got - G.as_f64(outs[0]))) <= 2e-2
