@@ -1003,25 +1003,32 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
   if (row >= total_rows) return;
   const int nz = a.num_splits;
+  // Every split's (max, sum) and numerator slice are loaded at once (one
+  // round trip); an empty split (max -inf) wrote no numerator, so whatever
+  // its slot holds is dropped by a select, never multiplied.
   f32x2 ml[kMaxSplits];
-  float M = -INFINITY;
+  f32x4 ov[kMaxSplits];
 #pragma unroll
   for (int zz = 0; zz < kMaxSplits; ++zz) {
     if (zz < nz) {
       ml[zz] = *reinterpret_cast<const f32x2*>(a.ws_ml + (zz * total_rows + row) * 2);
-      M = fmaxf(M, ml[zz][0]);
+      ov[zz] = *reinterpret_cast<const f32x4*>(a.ws_o + (zz * total_rows + row) * D + 4 * sub);
     }
   }
+  float M = -INFINITY;
+#pragma unroll
+  for (int zz = 0; zz < kMaxSplits; ++zz)
+    if (zz < nz) M = fmaxf(M, ml[zz][0]);
   float den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int zz = 0; zz < kMaxSplits; ++zz) {
-    if (zz < nz && ml[zz][0] != -INFINITY) {  // uniform over the row's 32 lanes
-      const f32x4 ov = *reinterpret_cast<const f32x4*>(a.ws_o + (zz * total_rows + row) * D + 4 * sub);
-      const float wz = __builtin_amdgcn_exp2f((ml[zz][0] - M) * a.scale_log2);
-      den = fmaf(wz, ml[zz][1], den);
+    if (zz < nz) {
+      const bool live = ml[zz][0] != -INFINITY;
+      const float wz = live ? __builtin_amdgcn_exp2f((ml[zz][0] - M) * a.scale_log2) : 0.f;
+      den = live ? fmaf(wz, ml[zz][1], den) : den;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) num[e] = fmaf(wz, ov[e], num[e]);
+      for (int e = 0; e < 4; ++e) num[e] = live ? fmaf(wz, ov[zz][e], num[e]) : num[e];
     }
   }
   const float inv = a.v_scale / den;
