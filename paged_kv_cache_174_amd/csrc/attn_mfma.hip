@@ -200,12 +200,6 @@ __device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
 }
 
-// acc + lo + hi of a packed bf16 pair, accumulated in fp32.
-__device__ __forceinline__ float add_bf16_pair(uint32_t pair, float acc) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, pair),
-                                         __builtin_bit_cast(bf16x2, 0x3F803F80u), acc, false);
-}
-
 // SHORT: at most 64 rows per (sequence, KV head) (short query chunks).  The
 // eight waves then split the keys instead of the rows: wave w takes row block
 // w % 2 (32 rows) and key group w / 2, i.e. tiles 4 i + w / 2 of iteration i,
@@ -510,10 +504,12 @@ attn_mfma_kernel(AttnArgs a) {
         u32x4 pk;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-          pk[e] = pack_bf16_rne(sacc[kb][8 * k16 + 2 * e], sacc[kb][8 * k16 + 2 * e + 1]);
-          // The row sum takes the bf16-rounded probabilities, the very
-          // weights that multiply V, so the output's weights sum to one.
-          ls[e] = add_bf16_pair(pk[e], ls[e]);
+          const float p0 = sacc[kb][8 * k16 + 2 * e], p1 = sacc[kb][8 * k16 + 2 * e + 1];
+          pk[e] = pack_bf16_rne(p0, p1);
+          // The row sum adds the fp32 probabilities with plain adds.  (A bf16
+          // dot instruction could add the rounded pair in one step, but it
+          // issues to the matrix pipe and stalls the SIMD partner's MFMAs.)
+          ls[e] = (ls[e] + p0) + p1;
         }
         pb[kb][k16] = __builtin_bit_cast(bf16x8, pk);
       }
@@ -733,7 +729,7 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e) {
             pk[e] = pack_bf16_rne(sc[8 * k16 + 2 * e], sc[8 * k16 + 2 * e + 1]);
-            ls[e] = add_bf16_pair(pk[e], ls[e]);
+            ls[e] = (ls[e] + sc[8 * k16 + 2 * e]) + sc[8 * k16 + 2 * e + 1];
           }
           pb[k16] = __builtin_bit_cast(bf16x8, pk);
         }
