@@ -336,11 +336,6 @@ attn_mfma_kernel(AttnArgs a) {
       qf[t] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  // Q has landed before any K/V load is issued.  The compiler cannot see the
-  // direct-to-LDS loads (inline assembly); without this wait it may guard a
-  // later use of Q with a full vmcnt(0), which would drain the K/V prefetch.
-  wait_vmcnt<0>();
-
   // ---- block-table slice for this workgroup's keys (no table: the K/V
   // buffers are one contiguous run, logical block i is block i)
   const int nblk = (s + 15) >> 4;
@@ -352,6 +347,11 @@ attn_mfma_kernel(AttnArgs a) {
   } else {
     for (int i = threadIdx.x; i < blk_hi - blk_lo; i += NT) tbl[i] = blk_lo + i;
   }
+  // Q and the table slice (loaded together, so their latencies overlap) have
+  // landed before any K/V load is issued.  The compiler cannot see the
+  // direct-to-LDS loads (inline assembly); without this wait it may guard a
+  // later use of Q with a full vmcnt(0), which would drain the K/V prefetch.
+  wait_vmcnt<0>();
   lds_barrier();
   // Keys at or past kv_lim are staged as zeros: past seq_len they do not exist,
   // and past the slice every row of the workgroup masks them anyway.
