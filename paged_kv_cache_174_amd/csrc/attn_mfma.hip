@@ -375,27 +375,31 @@ attn_mfma_kernel(AttnArgs a) {
   }
   const uint8_t* zero_row = reinterpret_cast<const uint8_t*>(g_zero_row) + 16 * st_pos;
 
-  // Block-table entry of the 16 keys this wave stages for the tile at key kt.
-  auto stage_entry = [&](int kt) {
-    const int blk = (kt >> 4) + (w >> 1);
+  // Block-table entry of the 16 keys whose rows wave ws stages for the tile
+  // at key kt (rows 8 ws .. 8 ws + 7 lie in block ws / 2 of the tile).
+  auto stage_entry = [&](int kt, int ws) {
+    const int blk = (kt >> 4) + (ws >> 1);
     return (blk < blk_hi) ? tbl[blk - blk_lo] : 0;
   };
   // bf16: direct loads of the tile at key kt into LDS buffer buf.
-  auto stage_load = [&](int kt, auto bufc, int e) {
+  // Rows 8 ws .. 8 ws + 7 of the K and V tiles (ws = w, or w + 4 when waves
+  // 0..3 stage for all eight: the rows of wave w + 4 sit 32 rows, two blocks,
+  // further on, at the same offsets inside their block).
+  auto stage_load = [&](int kt, auto bufc, int e, int ws) {
     constexpr int B = decltype(bufc)::value;
-    // The wave's eight rows lie in one 16-key block: its base address is
+    // The eight rows lie in one 16-key block: its base address is
     // wave-uniform and lives in SGPRs.
     const int64_t boff = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(e)) * block_bytes;
     const uint8_t* kb = kpool + boff;
     const uint8_t* vb = vpool + boff;
 #pragma unroll
     for (int st = 0; st < 2; ++st) {
-      const int dst = (8 * w + 4 * st) * kRowBytes;
-      if (kt + 8 * w + 4 * st + 4 <= kv_lim) {  // all four rows exist (uniform)
+      const int dst = (8 * ws + 4 * st) * kRowBytes;
+      if (kt + 8 * ws + 4 * st + 4 <= kv_lim) {  // all four rows exist (uniform)
         dma16(kb, static_cast<uint32_t>(k_src_off[st]), kbuf<B>() + dst);
         dma16(vb, static_cast<uint32_t>(v_src_off[st]), vbuf<B>() + dst);
       } else {  // the tile at the end of the staged keys: rows past kv_lim read zeros
-        const bool ok = kt + st_row[st] < kv_lim;
+        const bool ok = kt + st_row[st] + 8 * (ws - w) < kv_lim;
         dma16(ok ? kb + k_src_off[st] : zero_row, kbuf<B>() + dst);
         dma16(ok ? vb + v_src_off[st] : zero_row, vbuf<B>() + dst);
       }
@@ -758,7 +762,7 @@ attn_mfma_kernel(AttnArgs a) {
       // All four block-table entries first: one LDS round trip, not four.
       int e[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) e[j] = (t_first + j < ntiles) ? stage_entry(kt_of(t_first + j)) : 0;
+      for (int j = 0; j < 4; ++j) e[j] = (t_first + j < ntiles) ? stage_entry(kt_of(t_first + j), w) : 0;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int t = t_first + j;
@@ -823,16 +827,16 @@ attn_mfma_kernel(AttnArgs a) {
     };
 #pragma unroll
     for (int j = 0; j < 7; ++j)
-      if (j < ntiles) issue1(j, j, stage_entry(kt_of(j)));
+      if (j < ntiles) issue1(j, j, stage_entry(kt_of(j), w));
     wait_tiles(max(0, min(ntiles, 7) - 2));  // tiles 0 and 1
-    int e_next = stage_entry(kt_of(7));
+    int e_next = stage_entry(kt_of(7), w);
     lds_barrier();
     f32x16 sA[2], sB[2];
     qk8(0, sA);
     auto iteration = [&](auto bufc, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
       constexpr int B = decltype(bufc)::value;
       const int e_use = e_next;
-      e_next = stage_entry(kt_of(t + 8));
+      e_next = stage_entry(kt_of(t + 8), w);
       if (t + 7 < ntiles) issue1((B + 7) % 8, t + 7, e_use);
       if (kt_of(t) < wave_kmax) {
         mask_and_rescale(kt_of(t), s_cur);
@@ -858,20 +862,30 @@ attn_mfma_kernel(AttnArgs a) {
     // ---- bf16 long chunks: software pipeline over tiles t = 0 .. n-1 (tile
     // t: keys k_begin + 64 t, LDS buffer t % 4).  Iteration t: mask / max of
     // S(t); S(t+1) = K(t+1) Q^T next to the exponentials of S(t);
-    // O += V(t) P(t); the direct loads of tile t + 3 are issued first, into
-    // buffer (t + 3) % 4, which held tile t - 1, whose last reader was
-    // iteration t - 1; the barrier closing iteration t makes tile t + 2
-    // visible to iteration t + 1.  S(t + 1) of the last tile reads a stale
+    // O += V(t) P(t); then waves 0..3 stage tile t + 3 into buffer
+    // (t + 3) % 4, which held tile t - 1, last read in iteration t - 1.  The
+    // barrier closing iteration t follows their wait for tile t + 2 (staged in
+    // iteration t - 1), which iteration t + 1 reads.  Waves 0..3 stage all
+    // eight waves' rows: they run ahead of their SIMD partners (older waves
+    // issue first) and would otherwise wait for them at the barrier, while a
+    // direct load stalls the wave that issues it for as long as the CU's
+    // earlier loads are queued.  S(t + 1) of the last tile reads a stale
     // buffer and is never used.
-    stage_load(kt_of(0), Buf<0>{}, stage_entry(kt_of(0)));
-    if (ntiles > 1) stage_load(kt_of(1), Buf<1>{}, stage_entry(kt_of(1)));
-    if (ntiles > 2) {
-      stage_load(kt_of(2), Buf<2>{}, stage_entry(kt_of(2)));
-      wait_vmcnt<4>();
-    } else {
-      wait_vmcnt<0>();
+    const bool stager = w < 4;
+    auto stage_tile = [&](int t, auto bufc) {
+      stage_load(kt_of(t), bufc, stage_entry(kt_of(t), w), w);
+      stage_load(kt_of(t), bufc, stage_entry(kt_of(t), w + 4), w + 4);
+    };
+    if (stager) {
+      stage_tile(0, Buf<0>{});
+      if (ntiles > 1) stage_tile(1, Buf<1>{});
+      if (ntiles > 2) {
+        stage_tile(2, Buf<2>{});
+        wait_vmcnt<8>();
+      } else {
+        wait_vmcnt<0>();
+      }
     }
-    int e_next = stage_entry(kt_of(3));  // entry for the tile staged in iteration 0
     lds_barrier();
     f32x16 sA[2], sB[2];
     qk(Buf<0>{}, sA);
@@ -879,9 +893,6 @@ attn_mfma_kernel(AttnArgs a) {
     auto iteration = [&](auto bufc, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
       constexpr int B = decltype(bufc)::value;
       const int kt = kt_of(t);
-      const int e_use = e_next;
-      e_next = stage_entry(kt_of(t + 4));
-      if (t + 3 < ntiles) stage_load(kt_of(t + 3), Buf<(B + 3) % kBufs>{}, e_use);
       if (kt < wave_kmax) {
         mask_and_rescale(kt, s_cur);
         bf16x8 pb[2][2];
@@ -889,9 +900,14 @@ attn_mfma_kernel(AttnArgs a) {
         probs(s_cur, pb);
         pv(bufc, pb);
       }
-      // Tile t + 2 (issued one iteration ago) must have landed before the
-      // barrier after which iteration t + 1 reads it.
-      if (t + 3 < ntiles) wait_vmcnt<4>(); else wait_vmcnt<0>();
+      if (stager) {
+        if (t + 3 < ntiles) {
+          stage_tile(t + 3, Buf<(B + 3) % kBufs>{});
+          wait_vmcnt<8>();
+        } else {
+          wait_vmcnt<0>();
+        }
+      }
       lds_barrier();
     };
     for (int t = 0; t < ntiles; t += kBufs) {
