@@ -575,16 +575,18 @@ attn_mfma_kernel(AttnArgs a) {
   }
   // Direct loads of tile t (block-table entry e) into fp8 buffer buf: wave w
   // fills rows 8 w .. 8 w + 7; rows past kv_lim read zeros.
-  auto issue1 = [&](int buf, int t, int e) {
+  // (ws = w, or w + 4 when waves 0..3 load for all eight: those rows sit 32
+  // rows, two blocks, further on, at the same offsets inside their block)
+  auto issue1 = [&](int buf, int t, int e, int ws) {
     const int kt = k_begin + t * KT;
     const int64_t boff = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(e)) * block_bytes;
-    uint8_t* kdst = f8k_base + buf * kF8Tile + 8 * w * D;
-    uint8_t* vdst = f8v_base + buf * kF8Tile + 8 * w * D;
-    if (kt + 8 * w + 8 <= kv_lim) {  // all eight rows exist (uniform)
+    uint8_t* kdst = f8k_base + buf * kF8Tile + 8 * ws * D;
+    uint8_t* vdst = f8v_base + buf * kF8Tile + 8 * ws * D;
+    if (kt + 8 * ws + 8 <= kv_lim) {  // all eight rows exist (uniform)
       dma16(kpool + boff, dl_k, kdst);
       dma16(vpool + boff, dl_v, vdst);
     } else {
-      const bool ok = kt + dl_row < kv_lim;
+      const bool ok = kt + dl_row + 8 * (ws - w) < kv_lim;
       dma16(ok ? kpool + boff + dl_k : f8_zero, kdst);
       dma16(ok ? vpool + boff + dl_v : f8_zero, vdst);
     }
@@ -811,33 +813,37 @@ attn_mfma_kernel(AttnArgs a) {
   } else if constexpr (FP8) {
     // ---- fp8 long chunks: tile t in fp8 buffer t % 8, loaded seven tiles
     // ahead.  Iteration t: mask / max of S(t); S(t+1) = K(t+1) Q^T next to the
-    // exponentials of S(t); O += V(t) P(t).  Tile t + 7 goes into buffer
-    // (t - 1) % 8, whose last reader (V(t - 1)) finished before the barrier
-    // closing iteration t - 1.  A wave waits for its own share of tile t + 2
-    // before the barrier after which iteration t + 1 reads it.
-    auto wait_tiles = [&](int outstanding_tiles) {  // two loads per tile and wave
+    // exponentials of S(t); O += V(t) P(t); then waves 0..3 load tile t + 7
+    // (all eight waves' rows, as in the bf16 loop) into buffer (t - 1) % 8,
+    // whose last reader (V(t - 1)) finished before the barrier closing
+    // iteration t - 1, and wait for tile t + 2, which iteration t + 1 reads
+    // after the barrier.
+    const bool stager = w < 4;
+    auto wait_tiles = [&](int outstanding_tiles) {  // four loads per tile and loading wave
       switch (outstanding_tiles) {
-        case 5: wait_vmcnt<10>(); break;
-        case 4: wait_vmcnt<8>(); break;
-        case 3: wait_vmcnt<6>(); break;
-        case 2: wait_vmcnt<4>(); break;
-        case 1: wait_vmcnt<2>(); break;
+        case 5: wait_vmcnt<20>(); break;
+        case 4: wait_vmcnt<16>(); break;
+        case 3: wait_vmcnt<12>(); break;
+        case 2: wait_vmcnt<8>(); break;
+        case 1: wait_vmcnt<4>(); break;
         default: wait_vmcnt<0>(); break;
       }
     };
+    auto load_tile = [&](int buf, int t) {
+      issue1(buf, t, stage_entry(kt_of(t), w), w);
+      issue1(buf, t, stage_entry(kt_of(t), w + 4), w + 4);
+    };
+    if (stager) {
 #pragma unroll
-    for (int j = 0; j < 7; ++j)
-      if (j < ntiles) issue1(j, j, stage_entry(kt_of(j), w));
-    wait_tiles(max(0, min(ntiles, 7) - 2));  // tiles 0 and 1
-    int e_next = stage_entry(kt_of(7), w);
+      for (int j = 0; j < 7; ++j)
+        if (j < ntiles) load_tile(j, j);
+      wait_tiles(max(0, min(ntiles, 7) - 2));  // tiles 0 and 1
+    }
     lds_barrier();
     f32x16 sA[2], sB[2];
     qk8(0, sA);
     auto iteration = [&](auto bufc, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
       constexpr int B = decltype(bufc)::value;
-      const int e_use = e_next;
-      e_next = stage_entry(kt_of(t + 8), w);
-      if (t + 7 < ntiles) issue1((B + 7) % 8, t + 7, e_use);
       if (kt_of(t) < wave_kmax) {
         mask_and_rescale(kt_of(t), s_cur);
         bf16x8 pb[2][2];
@@ -845,7 +851,10 @@ attn_mfma_kernel(AttnArgs a) {
         probs(s_cur, pb);
         pv8(B, pb);
       }
-      wait_tiles(max(0, min(t + 7, ntiles - 1) - (t + 2)));
+      if (stager) {
+        if (t + 7 < ntiles) load_tile((B + 7) % 8, t + 7);
+        wait_tiles(max(0, min(t + 7, ntiles - 1) - (t + 2)));
+      }
       lds_barrier();
     };
     for (int t = 0; t < ntiles; t += 8) {
