@@ -626,12 +626,11 @@ attn_mfma_kernel(AttnArgs a) {
 
   if constexpr (kF8Lds && SHORT) {
     // ---- fp8 short path: 32-key tiles, four per step (one per key group),
-    // in a ring of four steps of buffers, so three steps (96 KB per CU) are
-    // in flight while one is multiplied.  Step i uses set i % 4; after the
-    // barrier closing step i - 1, the loads of step i + 3 go into that step's
-    // set.  Wave w loads half of tile w / 2 of each step (one 16-key block of
-    // K and of V, two direct loads each), the very tile its key group
-    // multiplies.
+    // in a ring of four steps of buffers.  Step i uses set i % 4; during step
+    // i (after the barrier closing step i - 1) the loads of step i + 3 go into
+    // the set of step i - 1.  Half a tile is one 16-key block of K and of V,
+    // two direct loads each; waves w and w + 4 (w < 4) load the same half of
+    // the tiles of key groups w / 2 and w / 2 + 2, and wave w issues both.
     constexpr int KT32 = 32;
     constexpr int kTile32 = KT32 * D;  // bytes of one fp8 K (or V) tile
     const int ntiles32 = (k_end - k_begin + KT32 - 1) / KT32;
@@ -648,16 +647,17 @@ attn_mfma_kernel(AttnArgs a) {
       ld_v[sub] = static_cast<uint32_t>((r & 15) * row_bytes + 16 * (dl_pos ^ f8_swz_v(r)));
     }
     auto tile_exists = [&](int step) { return 4 * step + kg < ntiles32; };  // kg == w / 2
-    auto issue_step = [&](int step) {
-      if (!tile_exists(step)) return;
+    // Loads of step `step` for key group kgs (its tile, this wave's half).
+    auto issue_step = [&](int step, int kgs) {
+      if (!(4 * step + kgs < ntiles32)) return;
       const int set = step & 3;
-      const int kt = k_begin + KT32 * (4 * step + kg);
+      const int kt = k_begin + KT32 * (4 * step + kgs);
       const int blk = (kt >> 4) + ld_part;
       const int e = (blk < blk_hi) ? tbl[blk - blk_lo] : 0;
       const int64_t boff = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(e)) * block_bytes;
       const int row0 = kt + 16 * ld_part;  // key of the first row this wave loads
-      uint8_t* kdst = f8k_base + (4 * set + kg) * kTile32 + 16 * ld_part * D;
-      uint8_t* vdst = f8v_base + (4 * set + kg) * kTile32 + 16 * ld_part * D;
+      uint8_t* kdst = f8k_base + (4 * set + kgs) * kTile32 + 16 * ld_part * D;
+      uint8_t* vdst = f8v_base + (4 * set + kgs) * kTile32 + 16 * ld_part * D;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
         if (row0 + 8 * sub + 8 <= kv_lim) {  // all eight rows exist (uniform)
@@ -670,23 +670,35 @@ attn_mfma_kernel(AttnArgs a) {
         }
       }
     };
-    // Waits until this wave's loads of step `step` have landed, given which
-    // later steps it has issued (four loads per step and wave).
+    // Waves 0..3 load for all eight: their own key group's tile and that of
+    // wave w + 4 (key group kg + 2, the same half), at the end of their step,
+    // where they would otherwise wait for their SIMD partners (a direct load
+    // stalls the wave that issues it while the CU's earlier loads queue).
+    const bool stager = w < 4;
+    auto nloads = [&](int step) { return 4 * (4 * step + kg < ntiles32) + 4 * (4 * step + kg + 2 < ntiles32); };
+    // Waits until a loading wave's loads of step `step` have landed, given
+    // which later steps it has issued.
     auto wait_step = [&](int step, int issued_upto) {
-      const int later = (issued_upto >= step + 1 && tile_exists(step + 1)) + (issued_upto >= step + 2 && tile_exists(step + 2));
+      int later = 0;
+      if (issued_upto >= step + 1) later += nloads(step + 1);
+      if (issued_upto >= step + 2) later += nloads(step + 2);
       switch (later) {
-        case 2: wait_vmcnt<8>(); break;
-        case 1: wait_vmcnt<4>(); break;
+        case 16: wait_vmcnt<16>(); break;
+        case 12: wait_vmcnt<12>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 4: wait_vmcnt<4>(); break;
         default: wait_vmcnt<0>(); break;
       }
     };
-    issue_step(0);
-    issue_step(1);
-    issue_step(2);
-    wait_step(0, 2);
+    if (stager) {
+      for (int st0 = 0; st0 < 3; ++st0) {
+        issue_step(st0, kg);
+        issue_step(st0, kg + 2);
+      }
+      wait_step(0, 2);
+    }
     lds_barrier();
     for (int step = 0; step < nsteps; ++step) {
-      issue_step(step + 3);  // into the set of step - 1, which every wave has left
       const int set = step & 3;
       const int kt = k_begin + KT32 * (4 * step + kg);
       if (tile_exists(step) && kt < wave_kmax) {
@@ -751,7 +763,12 @@ attn_mfma_kernel(AttnArgs a) {
             o[db] = mfma(va, pb[k16], o[db]);
           }
       }
-      wait_step(step + 1, step + 3);  // this wave's share of step + 1 has landed
+      if (stager) {
+        // step + 3 goes into the set of step - 1, which every wave has left
+        issue_step(step + 3, kg);
+        issue_step(step + 3, kg + 2);
+        wait_step(step + 1, step + 3);  // step + 1 has landed
+      }
       lds_barrier();
     }
   } else if constexpr (SHORT) {
