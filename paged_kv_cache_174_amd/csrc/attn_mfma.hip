@@ -435,7 +435,7 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
     for (int r = 0; r < 16; ++r) o[db][r] = 0.f;
 
-  auto qk = [&](auto bufc, f32x16 (&sacc)[2]) {
+  auto qk = [&](auto bufc, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
     constexpr int B = decltype(bufc)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -452,7 +452,7 @@ attn_mfma_kernel(AttnArgs a) {
   };
 
   // Mask, running max (lazily moved) for tile kt.
-  auto mask_and_rescale = [&](int kt, f32x16 (&sacc)[2]) {
+  auto mask_and_rescale = [&](int kt, f32x16 (&sacc)[2]) __attribute__((always_inline)) {
     if (kt + KT > wave_kmin) {
 #pragma unroll
       for (int kb = 0; kb < 2; ++kb)
@@ -494,7 +494,7 @@ attn_mfma_kernel(AttnArgs a) {
   // Probabilities of a tile, rounded to bf16, and their row sum.  The
   // exponentials overwrite S in place (all 32 first, then the packs and sums),
   // so the transcendental latency is covered without extra registers.
-  auto probs = [&](f32x16 (&sacc)[2], bf16x8 (&pb)[2][2]) {
+  auto probs = [&](f32x16 (&sacc)[2], bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
     const float mc = (m == -INFINITY) ? 0.f : m * sl;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -520,7 +520,7 @@ attn_mfma_kernel(AttnArgs a) {
     l += (ls[0] + ls[1]) + (ls[2] + ls[3]);
   };
 
-  auto pv = [&](auto bufc, const bf16x8 (&pb)[2][2]) {
+  auto pv = [&](auto bufc, const bf16x8 (&pb)[2][2]) __attribute__((always_inline)) {
     constexpr int B = decltype(bufc)::value;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb)
@@ -916,17 +916,28 @@ attn_mfma_kernel(AttnArgs a) {
     f32x16 sA[2], sB[2];
     qk(Buf<0>{}, sA);
 
-    auto iteration = [&](auto bufc, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2]) {
+    // Waves 4..7 start an iteration with QK(t+1) and then take the mask and
+    // maximum of S(t), so their MFMAs run while waves 0..3 compute theirs;
+    // the two orders are two loops, each straight-line code for the
+    // register allocator.
+    auto iteration = [&](auto bufc, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2], auto late_c)
+                         __attribute__((always_inline)) {
       constexpr int B = decltype(bufc)::value;
+      constexpr bool late = decltype(late_c)::value;
       const int kt = kt_of(t);
       if (kt < wave_kmax) {
-        mask_and_rescale(kt, s_cur);
         bf16x8 pb[2][2];
-        qk(Buf<(B + 1) % kBufs>{}, s_next);
+        if constexpr (late) {
+          qk(Buf<(B + 1) % kBufs>{}, s_next);
+          mask_and_rescale(kt, s_cur);
+        } else {
+          mask_and_rescale(kt, s_cur);
+          qk(Buf<(B + 1) % kBufs>{}, s_next);
+        }
         probs(s_cur, pb);
         pv(bufc, pb);
       }
-      if (stager) {
+      if constexpr (!late) {
         if (t + 3 < ntiles) {
           stage_tile(t + 3, Buf<(B + 3) % kBufs>{});
           wait_vmcnt<8>();
@@ -936,12 +947,16 @@ attn_mfma_kernel(AttnArgs a) {
       }
       lds_barrier();
     };
-    for (int t = 0; t < ntiles; t += kBufs) {
-      iteration(Buf<0>{}, t, sA, sB);
-      if (t + 1 < ntiles) iteration(Buf<1>{}, t + 1, sB, sA);
-      if (t + 2 < ntiles) iteration(Buf<2>{}, t + 2, sA, sB);
-      if (t + 3 < ntiles) iteration(Buf<3>{}, t + 3, sB, sA);
-    }
+    auto loop = [&](auto late_c) __attribute__((always_inline)) {
+      for (int t = 0; t < ntiles; t += kBufs) {
+        iteration(Buf<0>{}, t, sA, sB, late_c);
+        if (t + 1 < ntiles) iteration(Buf<1>{}, t + 1, sB, sA, late_c);
+        if (t + 2 < ntiles) iteration(Buf<2>{}, t + 2, sA, sB, late_c);
+        if (t + 3 < ntiles) iteration(Buf<3>{}, t + 3, sB, sA, late_c);
+      }
+    };
+    if (stager) loop(std::false_type{});
+    else loop(std::true_type{});
   }
 
   if constexpr (SHORT) {
