@@ -34,11 +34,12 @@
 //     the value dtype before the product.
 //   The loop is software-pipelined over four LDS buffers: iteration t runs
 //   QK for tile t + 1 next to the exponentials of tile t, then PV of tile t,
-//   while tile t + 3 streams into LDS.
+//   while tile t + 3 streams into LDS (staged by waves 0..3 for all eight).
 //
-// Split keys: with num_splits > 1 each workgroup writes unnormalised partial
-// (O, max, sum) for its key range to the workspace and a combine kernel merges
-// the splits in a fixed order (deterministic, no atomics).
+// Split keys: with num_splits > 1 each workgroup writes a partial for its
+// key range to the workspace -- its normalised output O / l in bf16 and
+// (max, sum) in fp32 -- and a combine kernel merges the splits in a fixed
+// order (deterministic, no atomics).
 #include <type_traits>
 
 #include "attn_common.hpp"
@@ -1019,13 +1020,19 @@ attn_mfma_kernel(AttnArgs a) {
   const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
   const int64_t orow_id = static_cast<int64_t>(t0 + tok) * a.num_q_heads + head;
   if (a.num_splits > 1) {
-    float* wo = a.ws_o + (static_cast<int64_t>(z) * total_rows + orow_id) * D;
+    // The split's partial: its normalised output O / l (a weighted average of
+    // V rows) rounded to bf16, and (max, sum) in fp32.  A row none of whose
+    // keys lies in this split has max -inf and its O / l is never read.
+    __bf16* wo = reinterpret_cast<__bf16*>(a.ws_o) + (static_cast<int64_t>(z) * total_rows + orow_id) * D;
+    const float inv = 1.0f / lt;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
       for (int rq = 0; rq < 4; ++rq) {
-        f32x4 v = {o[db][4 * rq], o[db][4 * rq + 1], o[db][4 * rq + 2], o[db][4 * rq + 3]};
-        *reinterpret_cast<f32x4*>(wo + 32 * db + 8 * rq + 4 * h2) = v;
+        u32x2 v;
+        v[0] = pack_bf16_rne(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
+        v[1] = pack_bf16_rne(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
+        *reinterpret_cast<u32x2*>(wo + 32 * db + 8 * rq + 4 * h2) = v;
       }
     if (h2 == 0) {
       f32x2 ml = {m, lt};
@@ -1050,6 +1057,7 @@ attn_mfma_kernel(AttnArgs a) {
 // head-dim values per lane, eight rows per workgroup.  Every split has a
 // partial for every row (an empty one has max -inf and sum 0 and is skipped),
 // so no sequence or mask metadata has to be looked up first.
+template <int NZ>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int sub = threadIdx.x & 31;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
@@ -1059,27 +1067,31 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   // Every split's (max, sum) and numerator slice are loaded at once (one
   // round trip); an empty split (max -inf) wrote no numerator, so whatever
   // its slot holds is dropped by a select, never multiplied.
-  f32x2 ml[kMaxSplits];
-  f32x4 ov[kMaxSplits];
+  f32x2 ml[NZ];
+  f32x4 ov[NZ];
+  const __bf16* wo = reinterpret_cast<const __bf16*>(a.ws_o);
 #pragma unroll
-  for (int zz = 0; zz < kMaxSplits; ++zz) {
+  for (int zz = 0; zz < NZ; ++zz) {
     if (zz < nz) {
       ml[zz] = *reinterpret_cast<const f32x2*>(a.ws_ml + (zz * total_rows + row) * 2);
-      ov[zz] = *reinterpret_cast<const f32x4*>(a.ws_o + (zz * total_rows + row) * D + 4 * sub);
+      const u32x2 pv = *reinterpret_cast<const u32x2*>(wo + (zz * total_rows + row) * D + 4 * sub);
+      ov[zz] = f32x4{__uint_as_float(pv[0] << 16), __uint_as_float(pv[0] & 0xFFFF0000u),
+                     __uint_as_float(pv[1] << 16), __uint_as_float(pv[1] & 0xFFFF0000u)};
     }
   }
   float M = -INFINITY;
 #pragma unroll
-  for (int zz = 0; zz < kMaxSplits; ++zz)
+  for (int zz = 0; zz < NZ; ++zz)
     if (zz < nz) M = fmaxf(M, ml[zz][0]);
   float den = 0.f;
   f32x4 num = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int zz = 0; zz < kMaxSplits; ++zz) {
+  for (int zz = 0; zz < NZ; ++zz) {
     if (zz < nz) {
       const bool live = ml[zz][0] != -INFINITY;
-      const float wz = live ? __builtin_amdgcn_exp2f((ml[zz][0] - M) * a.scale_log2) : 0.f;
-      den = live ? fmaf(wz, ml[zz][1], den) : den;
+      // weight of split zz: its sum of probabilities at the common max
+      const float wz = live ? __builtin_amdgcn_exp2f((ml[zz][0] - M) * a.scale_log2) * ml[zz][1] : 0.f;
+      den = live ? den + wz : den;
 #pragma unroll
       for (int e = 0; e < 4; ++e) num[e] = live ? fmaf(wz, ov[zz][e], num[e]) : num[e];
     }
@@ -1115,7 +1127,12 @@ hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, bool short_rows, hip
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s) {
   const int64_t rows = a.num_q_tokens * a.num_q_heads;
   if (rows <= 0) return hipSuccess;
-  hipLaunchKernelGGL(attn_combine_kernel, dim3(static_cast<unsigned>((rows + 7) / 8)), dim3(256), 0, s, a);
+  // (one instantiation per bound on the split count: registers for unused
+  // splits would lower the occupancy this latency-bound kernel relies on)
+  const dim3 grid(static_cast<unsigned>((rows + 7) / 8));
+  if (a.num_splits <= 4) hipLaunchKernelGGL(attn_combine_kernel<4>, grid, dim3(256), 0, s, a);
+  else if (a.num_splits <= 8) hipLaunchKernelGGL(attn_combine_kernel<8>, grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(attn_combine_kernel<kMaxSplits>, grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
