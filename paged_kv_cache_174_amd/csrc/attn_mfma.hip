@@ -77,6 +77,7 @@ constexpr float kRescaleLog2 = 8.0f;  // stale-max slack before O and l are resc
 constexpr int kBufs = 4;             // LDS K/V tile buffers: tiles t, t + 1 read while t + 2, t + 3 arrive
 constexpr int kLdsBytes = 2 * kBufs * kTileBytes + kTableSlice * 4;
 static_assert(kLdsBytes <= 160 * 1024, "LDS budget of a gfx950 CU");
+static_assert(NW * kWaveRows * kRowBytes <= kBufs * kTileBytes, "the epilogue stages every wave's rows in the K buffers");
 
 // K and V tile buffers.  The direct-to-LDS loads that fill them are inline
 // assembly the compiler does not see as LDS writes, so it adds no waits for
@@ -1016,8 +1017,54 @@ attn_mfma_kernel(AttnArgs a) {
 
   // ---- epilogue
   const float lt = SHORT ? lt_merged : sum_halves(l);
-  if (!valid) return;
   const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
+  if constexpr (!SHORT && !FP8) {
+    // Lane (l32, h2) holds head-dim [32 db + 8 rq + 4 h2, +4) of row l32; a
+    // direct store would write 16 bytes of 32 rows per instruction.  The
+    // rows go through this wave's own 8 KB of the K tile buffers instead
+    // (idle: every wave passed the loop's last barrier, all tiles landed) and
+    // leave as whole 256-byte rows, four rows per store instruction.  LDS
+    // chunk c of row r sits at position c ^ (r mod 16).
+    const bool split = a.num_splits > 1;
+    const float inv = split ? 1.0f / lt : a.v_scale / lt;
+    uint8_t* const reg = &s_k[0][0] + w * (kWaveRows * kRowBytes);
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        u32x2 v;
+        v[0] = pack_bf16_rne(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
+        v[1] = pack_bf16_rne(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
+        *reinterpret_cast<u32x2*>(reg + l32 * kRowBytes + 16 * ((4 * db + rq) ^ (l32 & 15)) + 8 * h2) = v;
+      }
+    if (split && h2 == 0 && valid) {
+      const int64_t orow_id = static_cast<int64_t>(t0 + tok) * a.num_q_heads + head;
+      f32x2 ml = {m, lt};
+      *reinterpret_cast<f32x2*>(a.ws_ml + (static_cast<int64_t>(z) * total_rows + orow_id) * 2) = ml;
+    }
+    // Query token of row l32 (int32, as the start offsets are), -1 past the chunk.
+    const int tok_of_row = valid ? t0 + tok : -1;
+    __bf16* const dst = split ? reinterpret_cast<__bf16*>(a.ws_o) + static_cast<int64_t>(z) * total_rows * D
+                              : static_cast<__bf16*>(a.out);
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (lgkmcnt(0))
+    asm volatile("" ::: "memory");
+    const int c = lane & 15;
+#pragma unroll
+    for (int k = 0; k < 8; ++k) {
+      const int rr = 4 * k + (lane >> 4);
+      const u32x4 v = *reinterpret_cast<const u32x4*>(reg + rr * kRowBytes + 16 * (c ^ (rr & 15)));
+      const int tk = __shfl(tok_of_row, rr);
+      if (tk >= 0) {
+        const int hd = hk * G + (wr0 + rr - (tk - t0) * G);  // the row's query head
+        *reinterpret_cast<u32x4*>(dst + (static_cast<int64_t>(tk) * a.num_q_heads + hd) * D + 8 * c) = v;
+      }
+    }
+    return;
+  }
+  // (The fp8 long kernel keeps direct stores: staging its rows the same way
+  // changed its loop's register allocation and cost 8% on long fp8 chunks.)
+  if (!valid) return;
   const int64_t orow_id = static_cast<int64_t>(t0 + tok) * a.num_q_heads + head;
   if (a.num_splits > 1) {
     // The split's partial: its normalised output O / l (a weighted average of
