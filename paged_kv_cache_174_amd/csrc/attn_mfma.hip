@@ -1100,14 +1100,16 @@ attn_mfma_kernel(AttnArgs a) {
   }
 }
 
-// Merges the key splits of a row, in split order: 32 lanes per row, four
-// head-dim values per lane, eight rows per workgroup.  Every split has a
-// partial for every row (an empty one has max -inf and sum 0 and is skipped),
-// so no sequence or mask metadata has to be looked up first.
+// Merges the key splits of a row, in split order: 16 lanes per row, eight
+// head-dim values (16 bytes of each bf16 partial) per lane, sixteen rows per
+// workgroup.  Every split has a partial for every row (an empty one has max
+// -inf and sum 0 and is skipped), so no sequence or mask metadata has to be
+// looked up first.
+constexpr int kCombineRows = 16;
 template <int NZ>
 __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
-  const int sub = threadIdx.x & 31;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 8 + (threadIdx.x >> 5);
+  const int sub = threadIdx.x & 15;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * kCombineRows + (threadIdx.x >> 4);
   const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
   if (row >= total_rows) return;
   const int nz = a.num_splits;
@@ -1115,15 +1117,13 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   // round trip); an empty split (max -inf) wrote no numerator, so whatever
   // its slot holds is dropped by a select, never multiplied.
   f32x2 ml[NZ];
-  f32x4 ov[NZ];
+  u32x4 pv[NZ];
   const __bf16* wo = reinterpret_cast<const __bf16*>(a.ws_o);
 #pragma unroll
   for (int zz = 0; zz < NZ; ++zz) {
     if (zz < nz) {
       ml[zz] = *reinterpret_cast<const f32x2*>(a.ws_ml + (zz * total_rows + row) * 2);
-      const u32x2 pv = *reinterpret_cast<const u32x2*>(wo + (zz * total_rows + row) * D + 4 * sub);
-      ov[zz] = f32x4{__uint_as_float(pv[0] << 16), __uint_as_float(pv[0] & 0xFFFF0000u),
-                     __uint_as_float(pv[1] << 16), __uint_as_float(pv[1] & 0xFFFF0000u)};
+      pv[zz] = *reinterpret_cast<const u32x4*>(wo + (zz * total_rows + row) * D + 8 * sub);
     }
   }
   float M = -INFINITY;
@@ -1131,7 +1131,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   for (int zz = 0; zz < NZ; ++zz)
     if (zz < nz) M = fmaxf(M, ml[zz][0]);
   float den = 0.f;
-  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  float num[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int zz = 0; zz < NZ; ++zz) {
     if (zz < nz) {
@@ -1140,14 +1140,18 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
       const float wz = live ? __builtin_amdgcn_exp2f((ml[zz][0] - M) * a.scale_log2) * ml[zz][1] : 0.f;
       den = live ? den + wz : den;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) num[e] = live ? fmaf(wz, ov[zz][e], num[e]) : num[e];
+      for (int e = 0; e < 4; ++e) {
+        const float lo = __uint_as_float(pv[zz][e] << 16), hi = __uint_as_float(pv[zz][e] & 0xFFFF0000u);
+        num[2 * e] = live ? fmaf(wz, lo, num[2 * e]) : num[2 * e];
+        num[2 * e + 1] = live ? fmaf(wz, hi, num[2 * e + 1]) : num[2 * e + 1];
+      }
     }
   }
   const float inv = a.v_scale / den;
-  u32x2 packed;
-  packed[0] = pack_bf16_rne(num[0] * inv, num[1] * inv);
-  packed[1] = pack_bf16_rne(num[2] * inv, num[3] * inv);
-  *reinterpret_cast<u32x2*>(static_cast<__bf16*>(a.out) + row * D + 4 * sub) = packed;
+  u32x4 packed;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) packed[e] = pack_bf16_rne(num[2 * e] * inv, num[2 * e + 1] * inv);
+  *reinterpret_cast<u32x4*>(static_cast<__bf16*>(a.out) + row * D + 8 * sub) = packed;
 }
 
 }  // namespace
@@ -1176,7 +1180,7 @@ hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s) {
   if (rows <= 0) return hipSuccess;
   // (one instantiation per bound on the split count: registers for unused
   // splits would lower the occupancy this latency-bound kernel relies on)
-  const dim3 grid(static_cast<unsigned>((rows + 7) / 8));
+  const dim3 grid(static_cast<unsigned>((rows + kCombineRows - 1) / kCombineRows));
   if (a.num_splits <= 4) hipLaunchKernelGGL(attn_combine_kernel<4>, grid, dim3(256), 0, s, a);
   else if (a.num_splits <= 8) hipLaunchKernelGGL(attn_combine_kernel<8>, grid, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(attn_combine_kernel<kMaxSplits>, grid, dim3(256), 0, s, a);
