@@ -16,10 +16,12 @@
 //   that every read pattern below is free of bank conflicts (k_swz, v_swz).  A tile's four
 //   16-token blocks are found through the block table (one entry per block,
 //   staged in LDS once per workgroup; entries past ceil(seq_len / 16) are
-//   never read).  bf16 pools are copied straight from HBM into LDS with
-//   direct global-to-LDS loads; fp8 pools go through registers, where e4m3 is
-//   widened to bf16 exactly.  Keys outside the workgroup's range read a row
-//   of zeros, so a value row that does not exist is 0, never garbage.
+//   never read).  Pools are copied straight from HBM into LDS with direct
+//   global-to-LDS loads (the bf16 short-query path goes through registers);
+//   fp8 tiles stay e4m3 in LDS (8 KB each of K and V per 64-key tile, half
+//   the bf16 size) and are widened to bf16, exactly, after the LDS read.  Keys
+//   outside the workgroup's range read a row of zeros, so a value row that
+//   does not exist is 0, never garbage.
 //
 // Per tile, per wave
 //   * S^T = K Q^T on the MFMA: the accumulator holds one query per lane and
@@ -35,6 +37,10 @@
 //   The loop is software-pipelined over four LDS buffers: iteration t runs
 //   QK for tile t + 1 next to the exponentials of tile t, then PV of tile t,
 //   while tile t + 3 streams into LDS (staged by waves 0..3 for all eight).
+//
+// Epilogue: O / l rounded to bf16.  The bf16 long kernel stages each wave's
+// 32 rows through LDS and stores whole 256-byte rows (four per instruction);
+// the other kernels store from the accumulator layout.
 //
 // Split keys: with num_splits > 1 each workgroup writes a partial for its
 // key range to the workspace -- its normalised output O / l in bf16 and
