@@ -88,3 +88,24 @@ def test_more_key_splits_than_supported_are_refused():
     with pytest.raises(G.P.PkvError):
         G.P.pkv_paged_attn(li.q, pools, table, plan.query_start_loc, plan.seq_lens, plan.segments,
                            plan.segment_start_loc, 0.1, plan.max_query_len, max_seq_len)
+
+
+def test_gqa_rows_straddling_waves_with_key_splits():
+    """Five query heads per KV head (a token's rows straddle the 32-row wave
+    blocks), a ragged last row tile (1000 rows = 3 x 256 + 232), a full span
+    inside a causal chunk, and a history long enough that the planner splits
+    the keys: the output rows leave through each wave's LDS staging and the
+    split partials through the merge."""
+    geom = small_variant(CONFIGS["piecewise_gqa_bf16"], name="gqa5_splits_bf16", num_q_heads=10, num_kv_heads=2,
+                         history_lens=(20000,), query_lens=(200,), full_spans=(((20050, 20120),),))
+    wl = make_workload(geom, device="cuda")
+    li = wl.layer(0)
+    G.say("attn gqa5 with splits", geom.name)
+    plan, _, _, out = G.run(wl, li=li)
+    rng = np.random.default_rng(11)
+    rows = sorted({0, 31, 32, 63, 199} | set(rng.integers(0, 200, size=10).tolist()))
+    _, _, _, ref = H.run_layer(wl, li=li, rows=rows)
+    got = G.as_f64(out)[np.asarray(rows)]
+    assert np.isfinite(got).all()
+    err = float(np.max(np.abs(got - ref)))
+    assert err <= TOL["bf16"], f"{geom.name}: max abs error {err:.3e}"
