@@ -1068,8 +1068,10 @@ attn_mfma_kernel(AttnArgs a) {
     }
     return;
   }
-  // (The fp8 long kernel keeps direct stores: staging its rows the same way
-  // changed its loop's register allocation and cost 8% on long fp8 chunks.)
+  // (The fp8 long and the short-query kernels keep direct stores: staging
+  // the fp8 long kernel's rows the same way changed its loop's register
+  // allocation and cost 8% on long fp8 chunks, and the short-query kernels
+  // store only two waves' rows, where it measured no gain.)
   if (!valid) return;
   const int64_t orow_id = static_cast<int64_t>(t0 + tok) * a.num_q_heads + head;
   if (a.num_splits > 1) {
