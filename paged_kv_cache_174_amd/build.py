@@ -33,6 +33,16 @@ FLAGS = [
 ]
 
 
+# Per-source extra flags.  The long-chunk attention kernel keeps its MFMA
+# accumulators (O and the scores) in VGPRs, where the softmax and the rare
+# rescale work on them, and feeds the MFMAs' other operands from AGPRs; left
+# to its heuristics the allocator spills and shuffles accumulators between
+# the two register files at every phase of the loop.
+EXTRA_FLAGS = {
+    "attn_long.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+}
+
+
 def _hipcc() -> str:
     for cand in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
         if cand and os.path.exists(cand):
@@ -48,7 +58,7 @@ def sources() -> list[str]:
 
 def _compile(hipcc: str, src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [hipcc, *FLAGS, "-c", src, "-o", obj]
+    cmd = [hipcc, *FLAGS, *EXTRA_FLAGS.get(os.path.basename(src), []), "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

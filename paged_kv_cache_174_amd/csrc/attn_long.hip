@@ -1,0 +1,696 @@
+// Paged attention over long query chunks on the gfx950 matrix cores: bf16
+// queries over bf16 K/V pools, head_dim 128.
+//
+// Work decomposition
+//   A "row" is one (query token, query head) pair of a KV-head group, token
+//   major, so the G = Hq / Hkv heads that share a K/V tile are computed from
+//   one LDS copy of it (GQA).  A workgroup of four waves -- one per SIMD --
+//   owns 256 consecutive rows of one (sequence, KV head) and, when the key
+//   range is split, one range of keys.  Each wave owns 64 rows as two halves
+//   A and B of 32 rows, each one column block of the 32x32x16 bf16 MFMA.
+//
+// Why one wave per SIMD, two halves per wave
+//   A SIMD overlaps a wave's own VALU work with that wave's MFMAs almost for
+//   free (up to ~28 cycles of VALU beside each 32-cycle MFMA), while VALU
+//   work of a second wave on the same SIMD slows an MFMA stream by about half.
+//   So the softmax of one half runs inside the instruction stream that feeds
+//   the other half's MFMAs.  Per 64-key tile t a wave runs two phases:
+//     alpha(t): softmax of A(t)  beside  QK of B(t) and PV of B(t - 1)
+//     beta(t):  softmax of B(t)  beside  QK of A(t + 1) and PV of A(t)
+//   32 MFMAs per phase; the K and V operand reads of a tile feed both halves.
+//
+// Softmax without a per-tile maximum
+//   Probabilities are exp2(s * c - m * c) with the row's running maximum m,
+//   which only moves on a slow path: the wave's first tile takes the exact
+//   maximum, and a later tile whose probabilities sum past 2^32 in some lane
+//   (its scores exceed m by more than 32 / c) recomputes its scores from LDS,
+//   takes their maximum and rescales O and l.  Softmax is exact for any common
+//   offset, so a stale m changes nothing but rounding; it only lets
+//   probabilities grow up to 2^32, far inside fp32 and bf16 range.
+//
+// K/V tiles (64 keys) in LDS
+//   Row-major bf16, one 256-byte row per key, 16-byte chunks XOR-permuted
+//   (k_swz / v_swz) so the MFMA operand reads are free of bank conflicts.
+//   Wave w copies the tile's 16-key block w straight from HBM into LDS
+//   (global_load_lds_dwordx4, four rows per load) through the block-table
+//   slice staged in LDS once per workgroup; keys at or past the staged range
+//   read a row of zeros.  Four tile buffers: tile t + 3's K loads go out in
+//   beta(t) and its V loads in alpha(t + 1), into the buffer tile t - 1 left.
+//   One barrier per tile, between the phases.
+//
+// Epilogue: O / l rounded to bf16, staged through LDS and stored as whole
+// 256-byte rows; with split keys the partial (O / l in bf16, (max, sum) in
+// fp32) goes to the workspace for the merge kernel.
+#include <type_traits>
+
+#include "attn_common.hpp"
+#include "mfma_util.hpp"
+
+namespace pkv {
+
+namespace {
+
+using namespace mx;
+
+constexpr int NW = 4;  // waves per workgroup, one per SIMD
+constexpr int NT = 64 * NW;
+constexpr int kHalfRows = 32;
+constexpr int kWaveRows = 2 * kHalfRows;
+static_assert(kMfmaRows == NW * kWaveRows, "rows per workgroup");
+static_assert(kMfmaKeyTile == kTileKeys, "key tile");
+constexpr int kBufs = 4;
+// A row whose probability sum passes this (or is not a number) sends the
+// workgroup to the exact rerun: some score rose more than 64 / (scale log2 e)
+// above its first sub-tile's maximum, near the top of fp32's range.
+constexpr float kFastSumLimit = 18446744073709551616.0f;  // 2^64
+static_assert(NW * kWaveRows * kRowBytes <= kBufs * kTileBytes, "the epilogue stages every wave's rows in the K buffers");
+static_assert(2 * kBufs * kTileBytes + kTableSlice * 4 <= 160 * 1024, "LDS budget of a gfx950 CU");
+
+__shared__ __attribute__((aligned(16))) uint8_t s_k[kBufs][kTileBytes];
+__shared__ __attribute__((aligned(16))) uint8_t s_v[kBufs][kTileBytes];
+__shared__ int32_t s_tbl[kTableSlice];  // the workgroup's slice of its block-table row
+__shared__ int32_t s_overflow[NW];      // per wave: some row's probability sum passed kFastSumLimit
+
+// Fourth word of a raw buffer descriptor on gfx9 (32-bit data format).
+constexpr int kBufferWord3 = 0x00020000;
+
+template <int B>
+using Buf = std::integral_constant<int, B>;
+
+// One 16-byte-per-lane direct load through a buffer descriptor into LDS:
+// lane i's 16 bytes at byte offset off of the descriptor's range land at
+// l + 16 i; offsets at or past the range read zeros.  Inline assembly, so
+// the compiler adds no waits for it (the kernel waits with wait_vmcnt); it
+// carries the wait states after the descriptor's v_readfirstlane writes and
+// after M0 that the compiler would otherwise insert (PKV_VMEM_SGPR_WAIT).
+__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, const void* l) {
+  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)l));
+  asm volatile(PKV_VMEM_SGPR_WAIT "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0));
+}
+
+__global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void
+attn_long_kernel(AttnArgs a) {
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int l32 = lane & 31;
+  const int h2 = lane >> 5;
+
+  // ---- work item.  Workgroups are dealt to the 8 XCDs round-robin by id;
+  // all workgroups of one (sequence, KV head) go to one XCD (they share its
+  // L2 for the group's K/V), and consecutive groups to different XCDs.
+  const uint32_t xcd = blockIdx.x & 7u, pos = blockIdx.x >> 3;
+  const uint32_t per_group = static_cast<uint32_t>(a.num_splits) * static_cast<uint32_t>(a.row_tiles);
+  const uint32_t grp = xcd + 8u * (pos / per_group);
+  if (grp >= static_cast<uint32_t>(a.num_seqs) * static_cast<uint32_t>(a.num_kv_heads)) return;
+  const uint32_t item = pos % per_group;
+  const int rt = static_cast<int>(item % static_cast<uint32_t>(a.row_tiles));
+  const int z = static_cast<int>(item / static_cast<uint32_t>(a.row_tiles));
+  const int hk = static_cast<int>(grp % static_cast<uint32_t>(a.num_kv_heads));
+  const int b_pos = static_cast<int>(grp / static_cast<uint32_t>(a.num_kv_heads));
+  const int b = a.seq_order ? a.seq_order[b_pos] : b_pos;
+
+  const int G = a.group;
+  const int t0 = a.qsl[b];
+  const int q_len = a.qsl[b + 1] - t0;
+  const int s = a.seq_lens[b];
+  const int R = q_len * G;
+  const int r0 = rt * kMfmaRows;
+  if (r0 >= R) return;
+  const int seg0 = a.seg_loc[b], seg1 = a.seg_loc[b + 1];
+  const int gbase = a.query_pos ? a.query_pos[b] : s - q_len;  // key position of the first query row
+  // Row limits are non-decreasing in the row's key position (the metadata
+  // check enforces it), so the tile's last row bounds the workgroup's keys
+  // and a wave's first row its mask-free prefix.
+  const int wg_kmax = row_limit(a.segments, seg0, seg1, gbase + (min(r0 + kMfmaRows, R) - 1) / G);
+  const int k_begin = z * a.split_len;
+  const int k_end = min(k_begin + a.split_len, wg_kmax);
+  const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
+  if (k_begin >= k_end) {
+    // No key of this split is visible to any row of the tile: its partial is
+    // empty (max -inf, sum 0), which the merge skips.
+    if (a.num_splits > 1 && threadIdx.x < kMfmaRows) {
+      const int row = r0 + static_cast<int>(threadIdx.x);
+      if (row < R) {
+        const int64_t orow = static_cast<int64_t>(t0 + row / G) * a.num_q_heads + hk * G + row % G;
+        const f32x2 ml = {-INFINITY, 0.f};
+        *reinterpret_cast<f32x2*>(a.ws_ml + (static_cast<int64_t>(z) * total_rows + orow) * 2) = ml;
+      }
+    }
+    return;
+  }
+
+  const int wr0 = r0 + kWaveRows * w;  // first row of this wave
+  const bool active = wr0 < R;
+  const int wave_kmin = active ? row_limit(a.segments, seg0, seg1, gbase + wr0 / G) : 0;
+
+  // ---- this lane's query row in each half
+  bool valid[2];
+  int tok[2], head[2], lrow[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int row = wr0 + kHalfRows * h + l32;
+    valid[h] = row < R;
+    tok[h] = valid[h] ? row / G : 0;
+    head[h] = hk * G + (valid[h] ? row % G : 0);
+    lrow[h] = valid[h] ? row_limit(a.segments, seg0, seg1, gbase + tok[h]) : 0;
+  }
+
+  // Q^T fragments for S^T = K Q^T: for k-step t the lane holds head-dim
+  // [16 t + 8 h2, +8) of its row.
+  bf16x8 qf[2][8];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const __bf16* qr = static_cast<const __bf16*>(a.q) + (static_cast<int64_t>(t0 + tok[h]) * a.num_q_heads + head[h]) * D;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) {
+      u32x4 v = {0u, 0u, 0u, 0u};
+      if (valid[h]) v = *reinterpret_cast<const u32x4*>(qr + 16 * t + 8 * h2);
+      qf[h][t] = __builtin_bit_cast(bf16x8, v);
+    }
+  }
+  // ---- block-table slice for this workgroup's keys (no table: the K/V
+  // buffers are one contiguous run, logical block i is block i)
+  const int nblk = (s + 15) >> 4;
+  const int blk_lo = k_begin >> 4;
+  const int blk_hi = min((k_end + 15) >> 4, nblk);
+  if (a.block_table) {
+    const int32_t* table = a.block_table + static_cast<int64_t>(b) * a.table_width;
+    for (int i = threadIdx.x; i < blk_hi - blk_lo; i += NT) s_tbl[i] = table[blk_lo + i];
+  } else {
+    for (int i = threadIdx.x; i < blk_hi - blk_lo; i += NT) s_tbl[i] = blk_lo + i;
+  }
+  // Q and the table slice have landed before any K/V load is issued (the
+  // compiler cannot see the direct-to-LDS loads, and would otherwise guard a
+  // later use of Q with a full vmcnt(0) that drains the K/V prefetch).
+  wait_vmcnt<0>();
+  lds_barrier();
+  // Keys at or past kv_lim are staged as zeros: past seq_len they do not
+  // exist (their slots may hold anything), past the slice every row of the
+  // workgroup masks them.
+  const int kv_lim = min(s, blk_hi * 16);
+  const int ntiles = (k_end - k_begin + kTileKeys - 1) / kTileKeys;
+
+  // ---- staging geometry: wave w copies block w of each tile, rows
+  // 16 w + 4 st + lane / 16 (st = 0..3), chunk position lane % 16.
+  const int64_t row_bytes = static_cast<int64_t>(a.num_kv_heads) * D * 2;
+  const int64_t block_bytes = 16 * row_bytes;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.kpool) + static_cast<int64_t>(hk) * D * 2;
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.vpool) + static_cast<int64_t>(hk) * D * 2;
+  const int st_pos = lane & 15;
+  const int st_sub = lane >> 4;
+  uint32_t k_src_off[4], v_src_off[4];
+#pragma unroll
+  for (int st = 0; st < 4; ++st) {
+    const int rb = 4 * st + st_sub;  // row inside the block (= tile row - 16 w)
+    k_src_off[st] = static_cast<uint32_t>(rb * row_bytes + 16 * (st_pos ^ k_swz(rb)));
+    v_src_off[st] = static_cast<uint32_t>(rb * row_bytes + 16 * (st_pos ^ v_swz(rb)));
+  }
+  // Direct loads through a buffer descriptor whose range ends at the last
+  // key below kv_lim in this wave's block: rows past it are out of range and
+  // arrive as zeros (past seq_len they do not exist and their slots may hold
+  // anything; past the slice every row of the workgroup masks them), so a
+  // value row that does not exist is 0, never garbage.  Base, range and the
+  // lane offsets (k_src_off / v_src_off) need no vector arithmetic.
+  // (A block past the slice only feeds rows past kv_lim, so any entry of the
+  // slice serves; clamping keeps the lookup branch-free.)
+  auto block_entry = [&](int kt) { return s_tbl[min((kt >> 4) + w - blk_lo, blk_hi - blk_lo - 1)]; };
+  auto entry_base = [&](int e) { return static_cast<int64_t>(__builtin_amdgcn_readfirstlane(e)) * block_bytes; };
+  auto block_base = [&](int kt) { return entry_base(block_entry(kt)); };
+  // (The descriptor must live in SGPRs: its parts are made wave-uniform
+  // explicitly, as the compiler cannot prove it for the range.)
+  auto rsrc = [&](const uint8_t* pool, int64_t boff, int kt) {
+    const int valid = min(max(kv_lim - (kt + 16 * w), 0), 16);  // rows of the block below kv_lim
+    const int bytes = __builtin_amdgcn_readfirstlane(static_cast<int>(valid * row_bytes));
+    const uint64_t base = reinterpret_cast<uint64_t>(pool + boff);
+    const uint64_t ubase = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base >> 32))) << 32) |
+                           static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base)));
+    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ubase), 0, bytes, kBufferWord3);
+  };
+  // Row group st (four rows) of this wave's block into buffer B.
+  auto load_k = [&](int kt, auto bufc, int64_t boff, int st) {
+    constexpr int B = decltype(bufc)::value;
+    dma16_buf(rsrc(kpool, boff, kt), k_src_off[st], s_k[B] + (16 * w + 4 * st) * kRowBytes);
+  };
+  auto load_v = [&](int kt, auto bufc, int64_t boff, int st) {
+    constexpr int B = decltype(bufc)::value;
+    dma16_buf(rsrc(vpool, boff, kt), v_src_off[st], s_v[B] + (16 * w + 4 * st) * kRowBytes);
+  };
+
+  // ---- MFMA operand addresses (bytes, buffer 0; buffer and key block are
+  // constant offsets)
+  uint32_t k_rd[8];  // K row 32 kb + l32, chunk 2 t + h2
+#pragma unroll
+  for (int t = 0; t < 8; ++t) k_rd[t] = lds_addr(s_k[0] + l32 * kRowBytes + 16 * ((2 * t + h2) ^ k_swz(l32)));
+  // V^T via transposing reads: in each 16-lane group g, lane 4 j + q names the
+  // 8-byte piece of V row 4 (g / 2) + j holding head-dim [16 (g % 2) + 4 q, +4)
+  // of head-dim block db; the instruction hands lane i of the group element
+  // i % 4 of the pieces named by lanes 4 j + i / 4, i.e. V[key(j)][d(lane)].
+  uint32_t v_rd[4];
+  {
+    const int g = lane >> 4, j = (lane >> 2) & 3, q = lane & 3;
+#pragma unroll
+    for (int db = 0; db < 4; ++db) {
+      const int c = 4 * db + 2 * (g & 1) + (q >> 1);
+      v_rd[db] = lds_addr(s_v[0] + (4 * (g >> 1) + j) * kRowBytes + 16 * (c ^ v_swz(j)) + 8 * (q & 1));
+    }
+  }
+  auto k_frag = [&](uint32_t buf_off, int kb, int t) {
+    return *lds_at<bf16x8>(k_rd[t] + buf_off + kb * 32 * kRowBytes);
+  };
+  auto v_frag = [&](uint32_t buf_off, int kb, int k16, int db) {
+    const uint32_t base = v_rd[db] + buf_off + (32 * kb + 16 * k16) * kRowBytes;
+    const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(base));
+    const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(base + 8 * kRowBytes));
+    return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+  };
+
+  const float sl = a.scale_log2;
+  float m[2] = {-INFINITY, -INFINITY};
+  float l[2] = {0.f, 0.f};
+  f32x16 o[2][4];  // O^T of each half, head-dim blocks db = 0..3
+  f32x16 sc[2];    // scores of each half for one 32-key sub-tile
+  bf16x8 pb[2][2];  // probabilities of each half as PV operands, k16 = 0, 1
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) o[h][db][r] = 0.f;
+
+  // Byte offset of key block kb (0, 1) of the tile buffer B.
+  auto blk_off = [](int B, int kb) { return static_cast<uint32_t>(B * kTileBytes + kb * 32 * kRowBytes); };
+  // S^T of half h for the 32-key sub-tile at byte offset off (exact step).
+  auto qk_full = [&](int h, uint32_t off) __attribute__((always_inline)) {
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[h][r] = 0.f;
+#pragma unroll
+    for (int t = 0; t < 8; ++t) sc[h] = mfma(k_frag(off, 0, t), qf[h][t], sc[h]);
+  };
+  // Keys j >= L(row) of half h get -inf.  Lane (l32, h2) holds key
+  // kt + 8 (r / 4) + 4 h2 + r % 4 in element r, so one bound per lane is
+  // compared with constants.
+  auto mask = [&](int h, int kt) __attribute__((always_inline)) {
+    const int lim = lrow[h] - kt - 4 * h2;
+#pragma unroll
+    for (int r = 0; r < 16; ++r)
+      if (8 * (r >> 2) + (r & 3) >= lim) sc[h][r] = -INFINITY;
+  };
+  // Probabilities of half h at its running max, packed for PV; returns the
+  // lane's partial row sum.
+  auto exps = [&](int h) __attribute__((always_inline)) {
+    const float mc = (m[h] == -INFINITY) ? 0.f : m[h] * sl;
+    float ls[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int k16 = 0; k16 < 2; ++k16) {
+      u32x4 pk;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const float p0 = __builtin_amdgcn_exp2f(fmaf(sc[h][8 * k16 + 2 * e], sl, -mc));
+        const float p1 = __builtin_amdgcn_exp2f(fmaf(sc[h][8 * k16 + 2 * e + 1], sl, -mc));
+        pk[e] = pack_bf16_rne(p0, p1);
+        ls[e] = (ls[e] + p0) + p1;
+      }
+      pb[h][k16] = __builtin_bit_cast(bf16x8, pk);
+    }
+    return (ls[0] + ls[1]) + (ls[2] + ls[3]);
+  };
+  // First sub-tile of a half: its exact maximum is the running max m, fixed
+  // for the rest of the fast loop (O is still zero, so nothing is rescaled).
+  // mcs = m * scale * log2(e) is the shift of every later exponent.
+  float mcs[2] = {0.f, 0.f};
+  auto softmax_first = [&](int h, int kt) __attribute__((always_inline)) {
+    if (kt + 32 > wave_kmin) mask(h, kt);
+    float c4[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) c4[i] = fmaxf(fmaxf(fmaxf(sc[h][i], sc[h][i + 4]), sc[h][i + 8]), sc[h][i + 12]);
+    m[h] = max_halves(fmaxf(fmaxf(c4[0], c4[1]), fmaxf(c4[2], c4[3])));
+    mcs[h] = (m[h] == -INFINITY) ? 0.f : m[h] * sl;
+    (void)exps(h);
+  };
+
+  auto kt_of = [&](int t) { return k_begin + t * kTileKeys; };
+
+  // MFMA operands held in registers so that each K and V fragment is read
+  // from LDS once per wave and serves both halves: kfr the K operands of one
+  // sub-tile (k-steps 0..7), vfr[2] the V^T operands of two sub-tiles
+  // ([k16][db]), alternating with the sub-tile's parity.
+  bf16x8 kfr[8];
+  bf16x8 vfr[2][2][4];
+  // Row sums on the matrix cores: rs[h] += ones x P^T puts the sum of a
+  // row's bf16 probabilities -- exactly the weights that multiply V -- in
+  // every element of the row's lane (both lane halves hold all of it).
+  f32x16 rs[2];
+  bf16x8 ones;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) ones[i] = static_cast<__bf16>(1.0f);
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) rs[h][r] = 0.f;
+
+  // One phase: 18 slots, each one MFMA plus at most ~28 cycles of other
+  // issue (a 32-cycle MFMA hides that much of its own wave's work; a wave
+  // issues in order, so more, or an instruction waiting on a result, idles
+  // the matrix pipe).  Two forms:
+  //   alpha(u) (BETA false): slots 0-15 alternate QK B(u) (from kfr) and
+  //     PV B(u - 1) (from vfr[VPV]); 16-17 its row sums; slots 0-7 each read
+  //     one V(u) operand (tile buffer BR, key block KR) into vfr[1 - VPV].
+  //   beta(u) (BETA true): slots 0-7 PV A(u) (from vfr[VPV]), each reading
+  //     one K operand of u + 1 (BR, KR) into kfr; 8-9 the row sums; 10-17
+  //     QK A(u + 1) from those operands.
+  // With SOFT the probabilities of the other half (HS) from its scores:
+  // scale-and-shift of two scores in each of slots 0-7, their exponentials
+  // in slots 8-15 and their bf16 packs in slots 10-17, each stage a slot or
+  // more after the one it reads.  With LOAD 1 (K) or 2 (V), row groups ST0
+  // and ST0 + 1 of this wave's block of tile t_load go into buffer BL in
+  // slots 16 and 17 (boff: the block's byte offset, looked up before the
+  // previous barrier).  sched_barrier keeps every slot in place.
+  auto phase = [&](auto beta_c, auto br_c, auto kr_c, auto vpv_c, auto soft_c, auto load_c, auto st0_c, auto bl_c,
+                   int t_load, int64_t boff) __attribute__((always_inline)) {
+    constexpr bool BETA = decltype(beta_c)::value;
+    constexpr int BR = decltype(br_c)::value, KR = decltype(kr_c)::value, VPV = decltype(vpv_c)::value;
+    constexpr bool SOFT = decltype(soft_c)::value;
+    constexpr int LOAD = decltype(load_c)::value, ST0 = decltype(st0_c)::value, BL = decltype(bl_c)::value;
+    constexpr int HQ = BETA ? 0 : 1, HS = 1 - HQ, HP = HQ;
+    const uint32_t roff = blk_off(BR, KR);
+    const int kt_load = kt_of(t_load);
+    __amdgpu_buffer_rsrc_t drs;
+    if constexpr (LOAD != 0) drs = rsrc(LOAD == 1 ? kpool : vpool, boff, kt_load);
+    float p[16];
+    u32x4 pk[2];
+#pragma unroll
+    for (int r = 0; r < 16; ++r) sc[HQ][r] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 18; ++j) {
+      // the slot's MFMA
+      if constexpr (!BETA) {
+        if (j < 16 && (j & 1) == 0) {
+          sc[HQ] = mfma(kfr[j >> 1], qf[HQ][j >> 1], sc[HQ]);
+        } else if (j < 16) {
+          const int q = j >> 1;  // PV operand (k16, db) = (q / 4, q % 4)
+          o[HP][q & 3] = mfma(vfr[VPV][q >> 2][q & 3], pb[HP][q >> 2], o[HP][q & 3]);
+        } else {
+          rs[HP] = mfma(ones, pb[HP][j - 16], rs[HP]);
+        }
+      } else {
+        if (j < 8) {
+          o[HP][j & 3] = mfma(vfr[VPV][j >> 2][j & 3], pb[HP][j >> 2], o[HP][j & 3]);
+        } else if (j < 10) {
+          rs[HP] = mfma(ones, pb[HP][j - 8], rs[HP]);
+        } else {
+          sc[HQ] = mfma(kfr[j - 10], qf[HQ][j - 10], sc[HQ]);
+        }
+      }
+      // LDS operand reads
+      if (j < 8) {
+        if constexpr (!BETA) vfr[1 - VPV][j >> 2][j & 3] = v_frag(roff, 0, j >> 2, j & 3);
+        else kfr[j] = k_frag(roff, 0, j);
+      }
+      // softmax of half HS
+      if constexpr (SOFT) {
+        if (j < 8) {
+          p[2 * j] = fmaf(sc[HS][2 * j], sl, -mcs[HS]);
+          p[2 * j + 1] = fmaf(sc[HS][2 * j + 1], sl, -mcs[HS]);
+          asm volatile("" : "+v"(p[2 * j]), "+v"(p[2 * j + 1]));
+        }
+        if (j >= 8 && j < 16) {
+          const int e = j - 8;
+          p[2 * e] = __builtin_amdgcn_exp2f(p[2 * e]);
+          p[2 * e + 1] = __builtin_amdgcn_exp2f(p[2 * e + 1]);
+          asm volatile("" : "+v"(p[2 * e]), "+v"(p[2 * e + 1]));
+        }
+        if (j >= 10) {
+          const int e = j - 10;  // scores 2 e, 2 e + 1: pair e % 4 of operand k16 = e / 4
+          uint32_t x = pack_bf16_rne(p[2 * e], p[2 * e + 1]);
+          asm volatile("" : "+v"(x));
+          pk[e >> 2][e & 3] = x;
+        }
+      }
+      if constexpr (LOAD != 0) {
+        if (j >= 16) {
+          const int st = ST0 + (j - 16);
+          dma16_buf(drs, LOAD == 1 ? k_src_off[st] : v_src_off[st],
+                    (LOAD == 1 ? s_k[BL] : s_v[BL]) + (16 * w + 4 * st) * kRowBytes);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if constexpr (SOFT) {
+#pragma unroll
+      for (int k16 = 0; k16 < 2; ++k16) pb[HS][k16] = __builtin_bit_cast(bf16x8, pk[k16]);
+    }
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+  using I2 = std::integral_constant<int, 2>;
+  using Soft = std::true_type;
+  using NoSoft = std::false_type;
+  using Alpha = std::false_type;
+  using Beta = std::true_type;
+
+  // The pipeline over 32-key sub-tiles u (tile u / 2, key block u % 2):
+  //   alpha(u): softmax A(u) | QK B(u), PV B(u - 1); reads V(u)
+  //   beta(u):  softmax B(u) | PV A(u), QK A(u + 1); reads K(u + 1)
+  // Tile t runs alpha(2t), beta(2t), alpha(2t+1), then -- once every wave's
+  // loads of tile t+1 have landed -- the barrier, then beta(2t+1), which
+  // reads tile t+1.  Tile X's loads go out in the four phases after the
+  // barrier of tile X - 3 (K row groups 0-1, K 2-3, V 0-1, V 2-3), into the
+  // buffer tile X - 4 left: its last reads (V of its second sub-tile) ran in
+  // alpha of that sub-tile, before the barrier of tile X - 3.  The QK of A
+  // one past the last sub-tile reads a stale buffer and is never used.
+  // Prologue: tiles 0, 1, 2 in full.
+  {
+    auto go = [&](int j, auto bufc) {
+      const int kt = kt_of(j);
+      const int64_t boff = block_base(kt);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) load_k(kt, bufc, boff, st);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) load_v(kt, bufc, boff, st);
+    };
+    go(0, Buf<0>{});
+    go(1, Buf<1>{});
+    go(2, Buf<2>{});
+  }
+  wait_vmcnt<16>();  // tile 0 landed
+  lds_barrier();
+  // A wave with no rows (the chunk's last row tile) only takes its share of
+  // the loads and the barriers.
+  auto idle_loads = [&](auto load_c, auto st0_c, auto buf_c, int t_load, int64_t boff) {
+    constexpr int LOAD = decltype(load_c)::value, ST0 = decltype(st0_c)::value;
+    const int kt = kt_of(t_load);
+#pragma unroll
+    for (int st = ST0; st < ST0 + 2; ++st) {
+      if constexpr (LOAD == 1) load_k(kt, buf_c, boff, st);
+      else load_v(kt, buf_c, boff, st);
+    }
+  };
+  const int kt0 = kt_of(0);
+  const bool edge0 = kt0 + 64 > wave_kmin;
+  if (active) {
+    qk_full(0, blk_off(0, 0));
+    softmax_first(0, kt0);
+    qk_full(1, blk_off(0, 0));
+    softmax_first(1, kt0);
+    // V(0) operands
+#pragma unroll
+    for (int k16 = 0; k16 < 2; ++k16)
+#pragma unroll
+      for (int db = 0; db < 4; ++db) vfr[0][k16][db] = v_frag(blk_off(0, 0), 0, k16, db);
+    // beta(0) without a softmax: PV A(0), QK A(1) (K(1) read here)
+    phase(Beta{}, Buf<0>{}, I1{}, I0{}, NoSoft{}, I0{}, I0{}, Buf<0>{}, 0, 0);
+    // alpha(1): QK B(1), PV B(0); reads V(1)
+    if (edge0) mask(0, kt0 + 32);
+    phase(Alpha{}, Buf<0>{}, I1{}, I0{}, Soft{}, I0{}, I0{}, Buf<0>{}, 0, 0);
+  }
+  // Block of this wave's loads of tile 3 (the barrier's wait covers the LDS read).
+  const int e3 = block_entry(kt_of(3));
+  wait_vmcnt<8>();  // tile 1 landed
+  lds_barrier();
+  const int64_t boff_next = entry_base(e3);
+  if (active) {
+    // beta(1): PV A(1), QK A(2) (K(2) from tile 1); K rows 0-1 of tile 3
+    if (edge0) mask(1, kt0 + 32);
+    phase(Beta{}, Buf<1>{}, I0{}, I1{}, Soft{}, I1{}, I0{}, Buf<3>{}, 3, boff_next);
+  } else {
+    idle_loads(I1{}, I0{}, Buf<3>{}, 3, boff_next);
+  }
+
+  // Tile t >= 1 in buffer T = t % 4.
+  // boff_load: block offset of this wave's loads of tile t + 2 (looked up
+  // in the previous tile); the lookup for tile t + 3 goes before the barrier.
+  int64_t boff_load = boff_next;
+  auto tile = [&](auto tc, int t) __attribute__((always_inline)) {
+    constexpr int T = decltype(tc)::value;
+    constexpr int Tp1 = (T + 1) % kBufs, Tp2 = (T + 2) % kBufs, Tp3 = (T + 3) % kBufs;
+    const int kt = kt_of(t);
+    const bool edge = kt + kTileKeys > wave_kmin;  // some row of the wave masks keys of this tile
+    if (active) {
+      // alpha(2t): QK B(2t), PV B(2t-1) [vfr 1]; reads V(2t) [T, 0] into vfr 0; K rows 2-3 of tile t+2
+      if (edge) mask(0, kt);
+      phase(Alpha{}, Buf<T>{}, I0{}, I1{}, Soft{}, I1{}, I2{}, Buf<Tp2>{}, t + 2, boff_load);
+      // beta(2t): PV A(2t) [vfr 0], QK A(2t+1) (reads K(2t+1) [T, 1]); V rows 0-1 of tile t+2
+      if (edge) mask(1, kt);
+      phase(Beta{}, Buf<T>{}, I1{}, I0{}, Soft{}, I2{}, I0{}, Buf<Tp2>{}, t + 2, boff_load);
+      // alpha(2t+1): QK B(2t+1), PV B(2t) [vfr 0]; reads V(2t+1) [T, 1] into vfr 1; V rows 2-3 of tile t+2
+      if (edge) mask(0, kt + 32);
+      phase(Alpha{}, Buf<T>{}, I1{}, I0{}, Soft{}, I2{}, I2{}, Buf<Tp2>{}, t + 2, boff_load);
+    } else {
+      idle_loads(I1{}, I2{}, Buf<Tp2>{}, t + 2, boff_load);
+      idle_loads(I2{}, I0{}, Buf<Tp2>{}, t + 2, boff_load);
+      idle_loads(I2{}, I2{}, Buf<Tp2>{}, t + 2, boff_load);
+    }
+    const int e_next = block_entry(kt_of(t + 3));
+    wait_vmcnt<8>();  // tile t + 1 landed (tile t + 2's eight loads may be in flight)
+    lds_barrier();
+    boff_load = entry_base(e_next);
+    if (active) {
+      // beta(2t+1): PV A(2t+1) [vfr 1], QK A(2t+2) (reads K(2t+2) [T+1, 0]); K rows 0-1 of tile t+3
+      if (edge) mask(1, kt + 32);
+      phase(Beta{}, Buf<Tp1>{}, I0{}, I1{}, Soft{}, I1{}, I0{}, Buf<Tp3>{}, t + 3, boff_load);
+    } else {
+      idle_loads(I1{}, I0{}, Buf<Tp3>{}, t + 3, boff_load);
+    }
+  };
+  for (int t = 1; t < ntiles; t += 4) {
+    tile(Buf<1>{}, t);
+    if (t + 1 < ntiles) tile(Buf<2>{}, t + 1);
+    if (t + 2 < ntiles) tile(Buf<3>{}, t + 2);
+    if (t + 3 < ntiles) tile(Buf<0>{}, t + 3);
+  }
+  // Drain: PV B of the last sub-tile (odd: vfr 1).  Every load (including
+  // those of tiles past the range, which read zeros) has landed and every
+  // wave has finished reading the tiles before the K buffers are reused for
+  // the output rows.
+  if (active) {
+#pragma unroll
+    for (int k16 = 0; k16 < 2; ++k16) {
+#pragma unroll
+      for (int db = 0; db < 4; ++db) o[1][db] = mfma(vfr[1][k16][db], pb[1][k16], o[1][db]);
+      rs[1] = mfma(ones, pb[1][k16], rs[1]);
+    }
+  }
+  // Row sums (the whole row's, in every lane of it).
+  l[0] = rs[0][0];
+  l[1] = rs[1][0];
+  const bool overflow = __builtin_amdgcn_ballot_w64(active && !(fmaxf(l[0], l[1]) <= kFastSumLimit)) != 0;
+  wait_vmcnt<0>();
+  if (lane == 0) s_overflow[w] = overflow ? 1 : 0;
+  lds_barrier();
+  if (s_overflow[0] | s_overflow[1] | s_overflow[2] | s_overflow[3]) {
+    // Exact rerun (some row's sum passed kFastSumLimit): tile by tile through
+    // buffer 0, each sub-tile's maximum moving the running max and rescaling
+    // O and l.
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      m[h] = -INFINITY;
+      l[h] = 0.f;
+#pragma unroll
+      for (int db = 0; db < 4; ++db)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[h][db][r] = 0.f;
+    }
+    for (int t = 0; t < ntiles; ++t) {
+      const int kt = kt_of(t);
+      const int64_t boff = block_base(kt);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) load_k(kt, Buf<0>{}, boff, st);
+#pragma unroll
+      for (int st = 0; st < 4; ++st) load_v(kt, Buf<0>{}, boff, st);
+      wait_vmcnt<0>();
+      lds_barrier();
+      if (active) {
+        for (int sub = 0; sub < 2; ++sub) {
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            qk_full(h, blk_off(0, 0) + static_cast<uint32_t>(sub) * 32 * kRowBytes);
+            const int ks = kt + 32 * sub;
+            if (ks + 32 > wave_kmin) mask(h, ks);
+            float c4[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c4[i] = fmaxf(fmaxf(fmaxf(sc[h][i], sc[h][i + 4]), sc[h][i + 8]), sc[h][i + 12]);
+            const float mx = max_halves(fmaxf(fmaxf(c4[0], c4[1]), fmaxf(c4[2], c4[3])));
+            const float m_new = fmaxf(m[h], mx);
+            const float alpha = (m[h] == -INFINITY) ? 0.f : __builtin_amdgcn_exp2f((m[h] - m_new) * sl);
+            l[h] *= alpha;
+#pragma unroll
+            for (int db = 0; db < 4; ++db)
+#pragma unroll
+              for (int r = 0; r < 16; ++r) o[h][db][r] *= alpha;
+            m[h] = m_new;
+            l[h] += exps(h);
+            const uint32_t off = blk_off(0, 0) + static_cast<uint32_t>(sub) * 32 * kRowBytes;
+#pragma unroll
+            for (int k16 = 0; k16 < 2; ++k16)
+#pragma unroll
+              for (int db = 0; db < 4; ++db) o[h][db] = mfma(v_frag(off, 0, k16, db), pb[h][k16], o[h][db]);
+          }
+        }
+      }
+      lds_barrier();
+    }
+#pragma unroll
+    for (int h = 0; h < 2; ++h) l[h] = sum_halves(l[h]);  // lane partials -> the row's sum
+  }
+
+  // ---- epilogue: each wave rounds its 64 rows to bf16, writes them into its
+  // own 16 KB of the K tile buffers (chunk c of row r at c ^ (r mod 16)) and
+  // stores them back as whole 256-byte rows, four rows per instruction.
+  const bool split = a.num_splits > 1;
+  uint8_t* const reg = &s_k[0][0] + w * (kWaveRows * kRowBytes);
+  int tok_of_row[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const float lt = l[h];
+    const float inv = split ? 1.0f / lt : a.v_scale / lt;
+#pragma unroll
+    for (int db = 0; db < 4; ++db)
+#pragma unroll
+      for (int rq = 0; rq < 4; ++rq) {
+        u32x2 v;
+        v[0] = pack_bf16_rne(o[h][db][4 * rq] * inv, o[h][db][4 * rq + 1] * inv);
+        v[1] = pack_bf16_rne(o[h][db][4 * rq + 2] * inv, o[h][db][4 * rq + 3] * inv);
+        *reinterpret_cast<u32x2*>(reg + (kHalfRows * h + l32) * kRowBytes + 16 * ((4 * db + rq) ^ (l32 & 15)) +
+                                  8 * h2) = v;
+      }
+    if (split && h2 == 0 && valid[h]) {
+      const int64_t orow_id = static_cast<int64_t>(t0 + tok[h]) * a.num_q_heads + head[h];
+      const f32x2 ml = {m[h], lt};
+      *reinterpret_cast<f32x2*>(a.ws_ml + (static_cast<int64_t>(z) * total_rows + orow_id) * 2) = ml;
+    }
+    // Query token of the row (int32, as the start offsets are), -1 past the chunk.
+    tok_of_row[h] = valid[h] ? t0 + tok[h] : -1;
+  }
+  __bf16* const dst = split ? reinterpret_cast<__bf16*>(a.ws_o) + static_cast<int64_t>(z) * total_rows * D
+                            : static_cast<__bf16*>(a.out);
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (lgkmcnt(0))
+  asm volatile("" ::: "memory");
+  if (!active) return;
+  const int c = lane & 15;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int rr = 4 * k + (lane >> 4);  // row of the wave, 0..63
+    const u32x4 v = *reinterpret_cast<const u32x4*>(reg + rr * kRowBytes + 16 * (c ^ (rr & 15)));
+    const int tk = __shfl(tok_of_row[k >> 3], rr & 31);  // rows 0..31 are half A, 32..63 half B
+    if (tk >= 0) {
+      const int hd = hk * G + (wr0 + rr - (tk - t0) * G);  // the row's query head
+      *reinterpret_cast<u32x4*>(dst + (static_cast<int64_t>(tk) * a.num_q_heads + hd) * D + 8 * c) = v;
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_attn_long(const AttnArgs& a, hipStream_t s) {
+  // Groups (sequence, KV head) padded to a multiple of the 8 XCDs; see the
+  // work-item mapping at the top of the kernel.
+  const int64_t groups = static_cast<int64_t>(a.num_seqs) * a.num_kv_heads;
+  const int64_t n = (groups + 7) / 8 * 8 * a.num_splits * a.row_tiles;
+  if (n <= 0) return hipSuccess;
+  if (n > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(attn_long_kernel, dim3(static_cast<unsigned>(n)), dim3(NT), 0, s, a);
+  return hipGetLastError();
+}
+
+}  // namespace pkv

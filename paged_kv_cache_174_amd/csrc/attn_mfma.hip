@@ -49,6 +49,7 @@
 #include <type_traits>
 
 #include "attn_common.hpp"
+#include "mfma_util.hpp"
 
 namespace pkv {
 
@@ -58,26 +59,13 @@ __device__ __attribute__((aligned(16))) uint32_t g_zero_row[64 * 4];
 
 namespace {
 
-typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
-typedef float f32x4 __attribute__((ext_vector_type(4)));
-typedef float f32x2 __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef short v4i16 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void* lds_ptr;
-typedef __attribute__((address_space(3))) v4i16* lds_v4i16_ptr;
-typedef int v2i32 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(3))) v2i32* lds_v2i32_ptr;
+using namespace mx;
 
-constexpr int D = 128;
 constexpr int KT = kMfmaKeyTile;  // keys per tile
 constexpr int NW = 8;             // waves per workgroup (two per SIMD)
 constexpr int NT = 64 * NW;
-constexpr int kRowBytes = D * 2;            // one bf16 K or V row of an LDS tile
-constexpr int kTileBytes = KT * kRowBytes;   // 16 KB
 constexpr int kWaveRows = 32;     // query rows per wave: one 32-wide MFMA column block
+static_assert(KT == kTileKeys, "tile size");
 static_assert(kMfmaRows == NW * kWaveRows, "rows per workgroup");
 constexpr float kRescaleLog2 = 8.0f;  // stale-max slack before O and l are rescaled
 constexpr int kBufs = 4;             // LDS K/V tile buffers: tiles t, t + 1 read while t + 2, t + 3 arrive
@@ -98,115 +86,10 @@ __device__ __forceinline__ uint8_t* kbuf() { return s_k[B]; }
 template <int B>
 __device__ __forceinline__ uint8_t* vbuf() { return s_v[B]; }
 
-// LDS byte address of p, hidden from the optimiser: addresses built as
-// opaque base + constant keep the constant (buffer, key block) in the 16-bit
-// offset field of the LDS instruction instead of an add per read.
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  uint32_t a = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)p));
-  asm volatile("" : "+v"(a));
-  return a;
-}
-template <typename T>
-__device__ __forceinline__ const __attribute__((address_space(3))) T* lds_at(uint32_t a) {
-  return (const __attribute__((address_space(3))) T*)(a);
-}
-
 template <int B>
 using Buf = std::integral_constant<int, B>;
 
-// One 16-byte-per-lane direct global-to-LDS load: lane i's 16 bytes from g
-// land at l + 16 i (l is wave-uniform, passed in M0).  Issued as inline
-// assembly so that the compiler does not add waits of its own for it: the
-// kernel waits for these loads explicitly (wait_vmcnt) before the barrier
-// that precedes their first reader.
-__device__ __forceinline__ void dma16(const void* g, uint8_t* l) {
-  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)l));
-  asm volatile("global_load_lds_dwordx4 %0, off" ::"v"(g), "{m0}"(m0));
-}
-// The same with a wave-uniform base address in SGPRs and a per-lane 32-bit
-// byte offset, so the address takes no vector arithmetic.
-__device__ __forceinline__ void dma16(const uint8_t* base, uint32_t off, uint8_t* l) {
-  const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)l));
-  asm volatile("global_load_lds_dwordx4 %0, %1" ::"v"(off), "s"(base), "{m0}"(m0));
-}
 static_assert(kTableSlice * 16 >= kMaxSplitKeys, "table slice must cover a split");
-
-// Workgroup barrier for the K/V tile pipeline.  __syncthreads() -- and any
-// release fence on LDS -- makes every wave wait for all of its outstanding
-// vector-memory loads, including the direct-to-LDS loads of tiles that are
-// only read iterations later, which would drain the prefetch at every tile.
-// Here each wave waits for its own LDS stores (lgkmcnt) and, before calling
-// this, for exactly the direct loads the next iteration reads (wait_vmcnt);
-// the empty asm statements keep the compiler from moving memory accesses
-// across the barrier.
-__device__ __forceinline__ void lds_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0); vmcnt and expcnt not waited on
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Chunk permutation of LDS tile rows.  The LDS serves 256 bytes per clock
-// from 64 four-byte banks, and a 256-byte row maps onto all of them, so the
-// 16-byte chunk c of row r is stored at position c ^ swz(r):
-//   K: the MFMA reads one chunk from 16 consecutive rows per clock -> XOR with
-//      r mod 16 puts them in 16 distinct positions;
-//   V: a transposing read takes four consecutive rows x 64 bytes (four
-//      chunks 4 k .. 4 k + 3) per clock -> XOR with 4 (r mod 4) moves each row
-//      to its own 64-byte quarter.
-__device__ __forceinline__ int k_swz(int r) { return r & 15; }
-__device__ __forceinline__ int v_swz(int r) { return 4 * (r & 3); }
-
-// Waits until at most N of this wave's vector-memory loads are outstanding
-// (loads complete in order).  Direct-to-LDS loads are only counted here, so
-// the consumer's barrier must be preceded by this wait.
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
-
-__device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
-  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-// Lanes l and l ^ 32 hold the two key halves of one query row in the S^T
-// accumulator layout.  v_permlane32_swap exchanges the upper half of its first
-// operand with the lower half of its second; with the same value in both, each
-// lane ends up with its own value in one result and its partner's in the
-// other, so max / sum over the pair are order-free functions of the two.
-__device__ __forceinline__ float max_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-__device__ __forceinline__ float sum_halves(float x) {
-  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
-}
-
-// Two floats known to be exact in bf16 (decoded e4m3 values) -> packed bf16 pair.
-__device__ __forceinline__ uint32_t pack_exact_bf16(float lo, float hi) {
-  return (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
-}
-
-// Eight e4m3 codes -> eight bf16 (exact: every e4m3 value is a bf16 value),
-// two codes per v_cvt_scalef32_pk_bf16_fp8 with scale 1.
-__device__ __forceinline__ u32x4 e4m3x8_to_bf16x8(u32x2 c) {
-  u32x4 r;
-#pragma unroll
-  for (int w = 0; w < 2; ++w) {
-    r[2 * w] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[w], 1.0f, false));
-    r[2 * w + 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(c[w], 1.0f, true));
-  }
-  return r;
-}
-
-// Two floats -> packed bf16 pair, round to nearest even (one v_cvt_pk_bf16_f32;
-// converting the two halves separately costs five instructions).
-__device__ __forceinline__ uint32_t pack_bf16_rne(float lo, float hi) {
-  const f32x2 v = {lo, hi};
-  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2));
-}
 
 // SHORT: at most 64 rows per (sequence, KV head) (short query chunks).  The
 // eight waves then split the keys instead of the rows: wave w takes row block
@@ -537,8 +420,8 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const uint32_t base = v_rd[db] + B * kTileBytes + (32 * kb + 16 * k16) * kRowBytes;
-          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base));
-          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4i16_ptr)(base + 8 * kRowBytes));
+          const v4i16 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(base));
+          const v4i16 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(lds_v4i16(base + 8 * kRowBytes));
           const bf16x8 va = __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
           o[db] = mfma(va, pb[kb][k16], o[db]);
         }
@@ -623,7 +506,7 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int db = 0; db < 4; ++db) {
           const uint32_t addr = v8_rd[db] + buf * kF8Tile + (32 * kb + 16 * k16) * D;
-          const v2i32 c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32_ptr)(addr));
+          const v2i32 c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(lds_v2i32(addr));
           const bf16x8 va = __builtin_bit_cast(
               bf16x8, e4m3x8_to_bf16x8(u32x2{static_cast<uint32_t>(c[0]), static_cast<uint32_t>(c[1])}));
           o[db] = mfma(va, pb[kb][k16], o[db]);
@@ -765,7 +648,7 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
           for (int db = 0; db < 4; ++db) {
             const uint32_t addr = v8_rd[db] + buf * kTile32 + 16 * k16 * D;
-            const v2i32 c = __builtin_amdgcn_ds_read_tr8_b64_v2i32((lds_v2i32_ptr)(addr));
+            const v2i32 c = __builtin_amdgcn_ds_read_tr8_b64_v2i32(lds_v2i32(addr));
             const bf16x8 va = __builtin_bit_cast(
                 bf16x8, e4m3x8_to_bf16x8(u32x2{static_cast<uint32_t>(c[0]), static_cast<uint32_t>(c[1])}));
             o[db] = mfma(va, pb[k16], o[db]);

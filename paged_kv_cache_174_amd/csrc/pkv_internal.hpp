@@ -103,6 +103,8 @@ constexpr int kMaxSplitKeys = (kTableSlice - 1) * 16;
 constexpr int kShortRows = 64;
 // short_rows: every sequence has at most kShortRows rows per KV head (row_tiles == 1).
 hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, bool short_rows, hipStream_t s);
+// bf16 K/V, more than kShortRows rows per KV head: four waves, one per SIMD (attn_long.hip).
+hipError_t launch_attn_long(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_combine(const AttnArgs& a, hipStream_t s);
 hipError_t launch_attn_f32(const AttnArgs& a, int max_query_len, hipStream_t s);
 

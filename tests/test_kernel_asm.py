@@ -1,0 +1,90 @@
+"""Static checks of the long-chunk attention kernel's gfx950 assembly (CPU).
+
+The kernel loads K/V tiles with inline-assembly buffer loads whose
+descriptor must sit in SGPRs, and its schedule assumes that nothing spills.
+Both properties are fixed by the compiler, not by the source text, so the
+kernel is compiled here and its assembly checked.
+"""
+
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from paged_kv_cache_174_amd import build as B
+
+SRC = os.path.join(B.CSRC, "attn_long.hip")
+
+
+@pytest.fixture(scope="module")
+def asm(tmp_path_factory):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    out = tmp_path_factory.mktemp("asm") / "attn_long.s"
+    cmd = [hipcc, *B.FLAGS, *B.EXTRA_FLAGS.get("attn_long.hip", []), "--cuda-device-only", "-S", SRC, "-o", str(out)]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    return out.read_text()
+
+
+def test_buffer_descriptors_are_scalar(asm):
+    loads = re.findall(r"^\s*buffer_load_dwordx4\s+v\d+,\s*([sv])\[", asm, flags=re.M)
+    assert loads, "expected direct-to-LDS buffer loads"
+    assert set(loads) == {"s"}, "a buffer load takes its descriptor from VGPRs"
+
+
+def test_no_spills(asm):
+    meta = dict(re.findall(r"^\s*\.(vgpr_spill_count|sgpr_spill_count|private_segment_fixed_size):\s*(\d+)", asm, flags=re.M))
+    assert int(meta["vgpr_spill_count"]) == 0
+    assert int(meta["private_segment_fixed_size"]) == 0
+
+
+def _compile(name):
+    hipcc = shutil.which("hipcc") or "/opt/rocm/bin/hipcc"
+    if not os.path.exists(hipcc):
+        pytest.skip("hipcc not available")
+    res = subprocess.run(
+        [hipcc, *B.FLAGS, *B.EXTRA_FLAGS.get(name, []), "--cuda-device-only", "-S", os.path.join(B.CSRC, name), "-o", "-"],
+        capture_output=True, text=True)
+    assert res.returncode == 0, res.stderr
+    return res.stdout
+
+
+def _sgprs(text):
+    regs = set()
+    for m in re.finditer(r"s\[(\d+):(\d+)\]", text):
+        regs |= set(range(int(m.group(1)), int(m.group(2)) + 1))
+    for m in re.finditer(r"(?<![\w\[])s(\d+)\b", text):
+        regs.add(int(m.group(1)))
+    return regs
+
+
+@pytest.mark.parametrize("name", ["attn_long.hip", "attn_mfma.hip"])
+def test_lds_dma_sgpr_wait_states(name):
+    """A direct-to-LDS load written as inline assembly reads SGPRs (base or
+    descriptor) that a v_readfirstlane may have written just before; the
+    hardware needs five wait states in between, which the compiler does not
+    insert for inline assembly."""
+    lines = [ln.strip() for ln in _compile(name).splitlines()]
+    insts = [ln for ln in lines if ln and not ln.startswith((";", ".")) and not ln.endswith(":")]
+    checked = 0
+    for i, ins in enumerate(insts):
+        if not ins.startswith(("buffer_load", "global_load_lds")):
+            continue
+        checked += 1
+        need = _sgprs(ins.split(None, 1)[1])
+        waits = 0
+        for prev in reversed(insts[max(0, i - 8):i]):
+            op = prev.split()[0]
+            if op == "s_nop":
+                waits += int(prev.split()[1], 0) + 1
+            else:
+                if op.startswith(("v_readfirstlane", "v_readlane")) and _sgprs(prev.split(None, 1)[1].split(",")[0]) & need:
+                    assert waits >= 5, f"{prev!r} then {ins!r} after {waits} wait states"
+                waits += 1
+            if waits >= 5:
+                break
+    assert checked > 0
