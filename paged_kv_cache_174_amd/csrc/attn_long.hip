@@ -80,9 +80,11 @@ using Buf = std::integral_constant<int, B>;
 // One 16-byte-per-lane direct load through a buffer descriptor into LDS:
 // lane i's 16 bytes at byte offset off of the descriptor's range land at
 // l + 16 i; offsets at or past the range read zeros.  Inline assembly, so
-// the compiler adds no waits for it (the kernel waits with wait_vmcnt); it
-// carries the wait states after the descriptor's v_readfirstlane writes and
-// after M0 that the compiler would otherwise insert (PKV_VMEM_SGPR_WAIT).
+// the compiler adds no waits for it (the kernel waits with wait_vmcnt).  It
+// carries the five wait states that a vector-memory read of an SGPR needs
+// after a VALU write of it (v_readfirstlane), which the compiler does not
+// insert for inline assembly, whether or not the descriptor's parts were
+// made on the scalar unit in a given build, and the one after M0.
 __device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, const void* l) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)l));
   asm volatile(PKV_VMEM_SGPR_WAIT "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0));
@@ -218,9 +220,19 @@ attn_long_kernel(AttnArgs a) {
   auto block_base = [&](int kt) { return entry_base(block_entry(kt)); };
   // (The descriptor must live in SGPRs: its parts are made wave-uniform
   // explicitly, as the compiler cannot prove it for the range.)
+  // The range, (rows of the block below kv_lim) x row_bytes, on the scalar
+  // unit (the compiler would clamp with a vector med3 and multiply).
+  const int kv_lim_w = __builtin_amdgcn_readfirstlane(kv_lim - 16 * w);
+  const int row_bytes32 = __builtin_amdgcn_readfirstlane(static_cast<int>(row_bytes));
   auto rsrc = [&](const uint8_t* pool, int64_t boff, int kt) {
-    const int valid = min(max(kv_lim - (kt + 16 * w), 0), 16);  // rows of the block below kv_lim
-    const int bytes = __builtin_amdgcn_readfirstlane(static_cast<int>(valid * row_bytes));
+    int bytes;
+    asm("s_sub_i32 %0, %1, %2\n"
+        "s_max_i32 %0, %0, 0\n"
+        "s_min_i32 %0, %0, 16\n"
+        "s_mul_i32 %0, %0, %3"
+        : "=&s"(bytes)
+        : "s"(kv_lim_w), "s"(kt), "s"(row_bytes32)
+        : "scc");
     const uint64_t base = reinterpret_cast<uint64_t>(pool + boff);
     const uint64_t ubase = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base >> 32))) << 32) |
                            static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base)));

@@ -62,17 +62,33 @@ def _sgprs(text):
     return regs
 
 
+# VALU instructions that write SGPRs, with the position of the SGPR
+# destination among their operands.
+_VALU_SGPR_DST = (("v_readfirstlane", 0), ("v_readlane", 0), ("v_cmp", 0), ("v_div_scale", 1),
+                  ("v_add_co", 1), ("v_sub_co", 1), ("v_subrev_co", 1), ("v_addc_co", 1), ("v_subb_co", 1),
+                  ("v_subbrev_co", 1), ("v_mad_u64_u32", 1), ("v_mad_i64_i32", 1))
+
+
+def _valu_sgpr_writes(ins):
+    op = ins.split()[0]
+    for prefix, pos in _VALU_SGPR_DST:
+        if op.startswith(prefix) and not op.startswith("v_cmpx"):
+            ops = ins.split(None, 1)[1].split(",") if " " in ins else []
+            return _sgprs(ops[pos]) if len(ops) > pos else set()
+    return set()
+
+
 @pytest.mark.parametrize("name", ["attn_long.hip", "attn_mfma.hip"])
 def test_lds_dma_sgpr_wait_states(name):
     """A direct-to-LDS load written as inline assembly reads SGPRs (base or
-    descriptor) that a v_readfirstlane may have written just before; the
-    hardware needs five wait states in between, which the compiler does not
-    insert for inline assembly."""
+    descriptor) that a VALU instruction may have written just before; the
+    hardware needs five wait states in between, and one after M0 is written,
+    which the compiler does not insert for inline assembly."""
     lines = [ln.strip() for ln in _compile(name).splitlines()]
     insts = [ln for ln in lines if ln and not ln.startswith((";", ".")) and not ln.endswith(":")]
     checked = 0
     for i, ins in enumerate(insts):
-        if not ins.startswith(("buffer_load", "global_load_lds")):
+        if not ins.startswith(("buffer_load", "global_load_lds")) or (ins.startswith("buffer_load") and " lds" not in ins):
             continue
         checked += 1
         need = _sgprs(ins.split(None, 1)[1])
@@ -81,10 +97,12 @@ def test_lds_dma_sgpr_wait_states(name):
             op = prev.split()[0]
             if op == "s_nop":
                 waits += int(prev.split()[1], 0) + 1
-            else:
-                if op.startswith(("v_readfirstlane", "v_readlane")) and _sgprs(prev.split(None, 1)[1].split(",")[0]) & need:
-                    assert waits >= 5, f"{prev!r} then {ins!r} after {waits} wait states"
-                waits += 1
+                continue
+            if _valu_sgpr_writes(prev) & need:
+                assert waits >= 5, f"{prev!r} then {ins!r} after {waits} wait states"
+            if waits < 1 and re.match(r"^\S+\s+m0\b", prev):
+                raise AssertionError(f"{prev!r} writes M0 right before {ins!r}")
+            waits += 1
             if waits >= 5:
                 break
     assert checked > 0
