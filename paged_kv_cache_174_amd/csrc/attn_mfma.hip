@@ -1002,7 +1002,9 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   const int sub = threadIdx.x & 15;
   const int64_t row = static_cast<int64_t>(blockIdx.x) * kCombineRows + (threadIdx.x >> 4);
   const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
-  if (row >= total_rows) return;
+  // Rows past the last sequence's queries belong to no sequence: no split
+  // wrote a partial for them, and their output rows are left untouched.
+  if (row >= min(total_rows, static_cast<int64_t>(a.qsl[a.num_seqs]) * a.num_q_heads)) return;
   const int nz = a.num_splits;
   // Every split's (max, sum) and numerator slice are loaded at once (one
   // round trip); an empty split (max -inf) wrote no numerator, so whatever

@@ -61,6 +61,10 @@ int check_pools(const pkv_pools* p) {
   return PKV_OK;
 }
 
+// Workspace bytes per query row and key split: the bf16 partial output
+// (head_dim 128), then the fp32 (max, sum) pair, in two regions.
+constexpr int64_t kPartialRowBytes = 128 * 2 + 2 * 4;
+
 struct SplitPlan {
   int row_tiles;
   int splits;
@@ -88,7 +92,7 @@ bool plan_short_packed(SplitPlan& p, int64_t num_q_tokens, int num_q_heads, int 
                        int kv_elem_bytes) {
   if (!host_lens || num_seqs > kMaxPackedSeqs || !have_workspace) return false;
   const int cus = cu_count();
-  const int64_t per_split_bytes = num_q_tokens * num_q_heads * (128 + 2) * static_cast<int64_t>(sizeof(float));
+  const int64_t per_split_bytes = num_q_tokens * num_q_heads * kPartialRowBytes;
   constexpr double kCuBytesPerS = 20e9;  // K+V streamed by one short-kernel workgroup
   constexpr double kWgStart = 4e-6;      // s: start-up and epilogue of one workgroup
   constexpr double kPartialBw = 5.0e12;
@@ -136,7 +140,7 @@ SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, i
   const int64_t base = static_cast<int64_t>(num_seqs) * num_kv_heads * p.row_tiles;
   const int cus = cu_count();
   const int max_by_len = std::max(1, max_seq_len / 512);
-  const int64_t per_split_bytes = num_q_tokens * num_q_heads * (128 + 2) * static_cast<int64_t>(sizeof(float));
+  const int64_t per_split_bytes = num_q_tokens * num_q_heads * kPartialRowBytes;
   constexpr double kCuFlops = 4.9e12;     // sustained FLOP/s of one CU on this kernel (about half of peak)
   constexpr double kPartialBw = 5.0e12;   // B/s for writing and re-reading the partials
   constexpr double kCombineLaunch = 3e-6; // s
@@ -307,7 +311,7 @@ size_t pkv_paged_attn_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, 
   // up to kMaxSplits splits (their rows are few).
   const int splits = p.short_rows ? std::max(p.splits, std::min(kMaxSplits, (max_seq_len + 127) / 128)) : p.splits;
   if (splits <= 1) return 0;
-  return static_cast<size_t>(splits) * static_cast<size_t>(num_q_tokens) * num_q_heads * (head_dim + 2) * sizeof(float);
+  return static_cast<size_t>(splits) * static_cast<size_t>(num_q_tokens) * num_q_heads * kPartialRowBytes;
 }
 
 }  // extern "C"
@@ -403,7 +407,7 @@ int attn_setup(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num
     return fail(PKV_EUNSUPPORTED, "max_seq_len %d needs more than %d key splits", max_seq_len, kMaxSplits);
   if (p.splits > 1 &&
       (!workspace ||
-       workspace_bytes < static_cast<size_t>(p.splits) * num_q_tokens * num_q_heads * (128 + 2) * sizeof(float)))
+       workspace_bytes < static_cast<size_t>(p.splits) * num_q_tokens * num_q_heads * kPartialRowBytes))
     return fail(PKV_EINVAL, "max_seq_len %d needs %d key splits and a workspace of pkv_paged_attn_workspace_size() bytes",
                 max_seq_len, p.splits);
   L.p = p;
@@ -414,7 +418,7 @@ int attn_setup(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num
   if (p.splits > 1) {
     const int64_t rows = num_q_tokens * num_q_heads;
     a.ws_o = static_cast<float*>(workspace);
-    a.ws_ml = a.ws_o + static_cast<int64_t>(p.splits) * rows * 128;
+    a.ws_ml = reinterpret_cast<float*>(static_cast<char*>(workspace) + static_cast<int64_t>(p.splits) * rows * 128 * 2);
   }
   return PKV_OK;
 }

@@ -70,8 +70,8 @@ struct AttnArgs {
   const int32_t* seg_loc;
   const int32_t* seq_order;  // dispatch order of the sequences, or null (natural order)
   const int32_t* query_pos;  // key position of each sequence's first query row, or null (the suffix)
-  float* ws_o;   // split mode: [splits][rows][head_dim] bf16 partial outputs O / l (in the first half of a fp32-sized region)
-  float* ws_ml;  // [splits][rows][2] partial (max, sum)
+  float* ws_o;   // split mode: [splits][rows][head_dim] bf16 partial outputs O / l
+  float* ws_ml;  // [splits][rows][2] fp32 partial (max, sum), right after ws_o's bf16 rows
   int64_t num_q_tokens;
   int32_t table_width;
   int32_t num_seqs;
