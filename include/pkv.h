@@ -192,6 +192,30 @@ int pkv_paged_attn_merge(const void* q, int32_t q_dtype, int64_t num_q_tokens, i
                          float softmax_scale, void* out, void* workspace, size_t workspace_bytes, void* stream);
 
 /*
+ * pkv_paged_attn for callers that cannot allocate device memory: code under
+ * HIP graph capture, serving loops and harnesses that forbid hipMalloc.  The
+ * arguments, result and errors are pkv_paged_attn's, without the workspace:
+ * the split-key partials go to a scratch array of PKV_NOALLOC_SCRATCH_BYTES
+ * that the library holds on every device it runs on, for the life of the
+ * process.  The call allocates and frees nothing.  It plans the splits
+ * pkv_paged_attn plans with a workspace of pkv_paged_attn_workspace_size()
+ * bytes, so the two give identical results.
+ * Errors: PKV_ERANGE when pkv_paged_attn_workspace_size() exceeds
+ * PKV_NOALLOC_SCRATCH_BYTES for these sizes (nothing is enqueued).
+ * Every call on one device uses that device's one array and leaves its
+ * contents behind (no part of it needs to start cleared: each partial the
+ * merge reads is written by the same call): calls that may overlap on one
+ * device, e.g. on two streams, race and must be serialised by the caller.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (128u * 1024u * 1024u)
+int pkv_paged_attn_noalloc(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num_q_heads,
+                           const pkv_pools* pools, const int32_t* block_table, int32_t table_width,
+                           const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
+                           int32_t max_query_len, int32_t max_seq_len, const int32_t* segments,
+                           const int32_t* segment_start_loc, const int32_t* seq_order, const int32_t* host_seq_lens,
+                           float softmax_scale, void* out, void* stream);
+
+/*
  * Attention metadata of one forward, shared by every layer (P1
  * ARDiffusionPagedForwardContext.prepare builds it once per KV branch).  The
  * fields are pkv_paged_attn's arguments of the same names.  For capture in a

@@ -24,6 +24,7 @@ from ._lib import (  # noqa: F401
     pkv_paged_attn,
     pkv_paged_attn_main,
     pkv_paged_attn_merge,
+    pkv_paged_attn_noalloc,
     pkv_paged_attn_workspace_size,
     pkv_paged_write,
     pkv_paged_write_attn,

@@ -112,6 +112,7 @@ _SIGNATURES = {
     "pkv_paged_attn": (ctypes.c_int, _ATTN_ARGS),
     "pkv_paged_attn_main": (ctypes.c_int, _ATTN_ARGS),
     "pkv_paged_attn_merge": (ctypes.c_int, _ATTN_ARGS),
+    "pkv_paged_attn_noalloc": (ctypes.c_int, _ATTN_ARGS[:-3] + [_P]),  # no workspace, workspace_bytes
     "pkv_paged_write_attn": (
         ctypes.c_int,
         [_P, _I32, _I64, _I32, _P, _P, _I32, _I64, _P, _P, _P, _I64, _P, _PPOOLS,
@@ -328,6 +329,11 @@ def pkv_paged_attn(
     ws_ptr, ws_bytes = None, 0
     if workspace is not None:
         ws_ptr, ws_bytes = _dev(workspace, "workspace"), workspace.numel() * workspace.element_size()
+    ws_args = (ws_ptr, ws_bytes)
+    if _entry == "pkv_paged_attn_noalloc":
+        if workspace is not None:
+            raise ValueError("pkv_paged_attn_noalloc takes no workspace")
+        ws_args = ()
     ps = pools.c_struct()
     _check(
         getattr(lib(), _entry)(
@@ -349,12 +355,17 @@ def pkv_paged_attn(
             None if hl is None else _ptr(hl, ctypes.c_int32),
             float(softmax_scale),
             _dev(out, "out"),
-            ws_ptr,
-            ws_bytes,
+            *ws_args,
             _stream(stream),
         )
     )
     return out
+
+
+def pkv_paged_attn_noalloc(*args, **kwargs) -> torch.Tensor:
+    """pkv_paged_attn without a workspace: the split partials go to the
+    library's static per-device scratch (see include/pkv.h)."""
+    return pkv_paged_attn(*args, _entry="pkv_paged_attn_noalloc", **kwargs)
 
 
 def pkv_paged_attn_main(*args, **kwargs) -> torch.Tensor:
