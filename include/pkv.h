@@ -126,6 +126,10 @@ int pkv_gather(const pkv_pools* pools, const int32_t* block_ids, int32_t n_block
  * [seq_len - q_len, seq_len) in order.  A row g in a FULL segment sees keys
  * j < kv_end; in a CAUSAL segment keys j <= g (bottom-right alignment).
  * The AR default of P1 (causal=False) is one FULL segment with kv_end = seq_len.
+ * Precondition: the per-row key limit L(g) (kv_end, or g + 1) never decreases
+ * from one row to the next.  P3 build_segments' lists satisfy it (a FULL
+ * segment reaches past its q_end only when it is the last one);
+ * pkv_validate_metadata_host refuses lists that break it.
  *
  * GQA: query head h reads KV head h / (num_q_heads / num_kv_heads) (P4 requires
  * num_q_heads % num_kv_heads == 0).
@@ -135,7 +139,8 @@ int pkv_gather(const pkv_pools* pools, const int32_t* block_ids, int32_t n_block
  *   q                 device [num_q_tokens, num_q_heads, head_dim]; q_dtype PKV_F32 with
  *                     F32 pools, PKV_BF16 with BF16 or FP8_E4M3 pools
  *   block_table       device int32 [num_seqs, table_width]
- *   query_start_loc   device int32 [num_seqs + 1], query_start_loc[num_seqs] == num_q_tokens
+ *   query_start_loc   device int32 [num_seqs + 1]; rows of q/out at or past
+ *                     query_start_loc[num_seqs] belong to no sequence and are not written
  *   seq_lens          device int32 [num_seqs]
  *   max_query_len     host bound on every query length (grid sizing)
  *   max_seq_len       host bound on every seq_lens[b] (a capacity, P1 build_block_table)
@@ -258,6 +263,44 @@ typedef struct {
 } pkv_staging;
 
 /*
+ * What one KV branch's staging buffers held after its last staged forward
+ * (P1 history_staging_state), for pkv_staging_decide.  Caller-owned: set
+ * session to -1 before the first use.  history_blocks is caller-owned storage
+ * for block_capacity block ids (the most a visible history can list).
+ */
+typedef struct {
+  int64_t session;             /* caller's id of the request staged last; -1: none */
+  int64_t history_tokens;      /* its history length */
+  int64_t chunk_tokens;        /* its current chunk's length */
+  int32_t max_seq_len;         /* its staged extent */
+  int32_t num_history_blocks;  /* its visible history's blocks, listed in history_blocks */
+  int32_t* history_blocks;
+  int32_t block_capacity;
+} pkv_staging_state;
+
+/*
+ * Whether a forward may keep the rows its staging buffers already hold (P1
+ * _prepare_history_staging): the staged history is still this forward's when
+ * the last staged forward was for the same request (`session`, a caller id
+ * >= 0), with the same history (length and visible blocks), extent
+ * (max_seq_len) and chunk length, and the chunk starts on a block edge and
+ * fills whole blocks (so no block holds both history and chunk rows).
+ *   table          host, the forward's visible-window table (table_len entries,
+ *                  as pkv_window_table builds it): the history's blocks, then the
+ *                  blocks the current chunk touches
+ *   capacity_tokens  rows the staging buffers hold
+ * Writes *out_reuse (1 or 0) and *out_first_block: the pkv_staging.first_block
+ * of this forward -- the visible history's block count when reusing, else 0
+ * (restage everything).  The state then describes this forward.
+ * Errors: PKV_ERANGE when max_seq_len > capacity_tokens (P1 raises) or the
+ * history lists more blocks than state->block_capacity; PKV_EINVAL for bad
+ * sizes or a table too short for the chunk.  The state is unchanged on error.
+ */
+int pkv_staging_decide(pkv_staging_state* state, int64_t session, const int32_t* table, int32_t table_len,
+                       int64_t history_tokens, int64_t chunk_tokens, int32_t max_seq_len, int32_t block_size,
+                       int64_t capacity_tokens, int32_t* out_reuse, int32_t* out_first_block);
+
+/*
  * One layer of the per-layer op (P1 _paged_write_attn_impl): enqueues, in
  * order on `stream`,
  *   1. the slot writes of the current video K/V (as pkv_paged_write with
@@ -359,8 +402,9 @@ int pkv_build_segments(const int32_t* full_spans, int32_t num_spans, int32_t que
  * referenced table entries in [0, num_blocks), the query rows
  * [g0, g0 + q_len) inside [0, seq_len) with g0 = query_pos[b] (host, may be
  * NULL: g0 = seq_len - q_len), segments tiling [g0, g0 + q_len) in order with
- * causal kv_end == q_end and full kv_end in [q_end, seq_len].  Returns PKV_OK
- * or PKV_EINVAL with a message.
+ * causal kv_end == q_end, full kv_end in [q_end, seq_len], and row key limits
+ * that never decrease from one segment to the next (the kernels' precondition,
+ * see pkv_paged_attn).  Returns PKV_OK or PKV_EINVAL with a message.
  */
 int pkv_validate_metadata_host(const int32_t* query_start_loc, const int32_t* seq_lens, int32_t num_seqs,
                                const int32_t* block_table, int32_t table_width, int64_t num_blocks,

@@ -363,7 +363,8 @@ def staging_decision(
     state.session = session
     state.signature = signature
     touched = -(-(offset + int(chunk_tokens)) // B)
-    return True, bool(reuse), window.kv_len // B - touched
+    # without reuse the whole window is staged again: from block row 0
+    return True, bool(reuse), window.kv_len // B - touched if reuse else 0
 
 
 @dataclass(frozen=True)
@@ -378,29 +379,37 @@ class Segment:
 
 
 def build_segments(full_spans, query_offset: int, query_len: int) -> list[Segment]:
-    """P3 ``build_segments``: split the query range ``[o, o + n)`` into causal
-    runs and full-attention runs.
+    """P3 ``build_segments``, from the rule of P3's module docstring: rows of
+    the query range ``[o, o + n)`` that lie in a full span ``[a, b)`` attend
+    ``K[:b]`` with no mask (``b`` is the span's own end, even where the query
+    stops inside the span); the other rows are cut into causal segments
+    ``[s, e)`` that attend ``K[:e]`` aligned at the bottom-right corner, so
+    their ``kv_end`` is ``e``.
 
-    Each full span ``[a, b)`` is clipped to the query range; the rows before it
-    that no span has claimed yet become a causal run whose ``kv_end`` is its own
-    end, the clipped span becomes a full run whose ``kv_end`` is the span's
-    *unclipped* end ``b``, and whatever is left after the last span is a causal
-    run to the end of the query.  Spans that miss the query range are dropped.
+    Written row by row: each row gets its rule -- the end of the span holding
+    it, or none -- and consecutive rows with the same rule form one segment.
+    The spans are sorted and disjoint (P3 ``build_paged_piecewise_plan``
+    refuses anything else).
     """
     lo, hi = int(query_offset), int(query_offset) + int(query_len)
-    segs: list[Segment] = []
-    cursor = lo
-    for a, b in full_spans:
-        start, stop = max(int(a), lo), min(int(b), hi)
-        if start >= stop:
-            continue
-        if cursor < start:
-            segs.append(Segment(cursor, start, start, "causal"))
-        segs.append(Segment(start, stop, int(b), "full"))
-        cursor = stop
-    if cursor < hi:
-        segs.append(Segment(cursor, hi, hi, "causal"))
-    return segs
+    spans = [(int(a), int(b)) for a, b in full_spans]
+    if any(b0 > a1 for (_, b0), (a1, _) in zip(spans, spans[1:])):
+        raise ValueError("full spans must be sorted and disjoint")
+
+    def span_end(g):
+        for a, b in spans:
+            if a <= g < b:
+                return b
+        return None
+
+    runs: list[list] = []  # [first row, end row, span end or None]
+    for g in range(lo, hi):
+        rule = span_end(g)
+        if runs and runs[-1][2] == rule:
+            runs[-1][1] = g + 1
+        else:
+            runs.append([g, g + 1, rule])
+    return [Segment(s, e, r, "full") if r is not None else Segment(s, e, e, "causal") for s, e, r in runs]
 
 
 def segments_for_rows(full_spans_per_seq, query_lens, seq_lens, causal_default: bool = False):

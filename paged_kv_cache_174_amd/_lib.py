@@ -96,6 +96,18 @@ class _Staging(ctypes.Structure):
     ]
 
 
+class _StagingState(ctypes.Structure):
+    _fields_ = [
+        ("session", ctypes.c_int64),
+        ("history_tokens", ctypes.c_int64),
+        ("chunk_tokens", ctypes.c_int64),
+        ("max_seq_len", ctypes.c_int32),
+        ("num_history_blocks", ctypes.c_int32),
+        ("history_blocks", ctypes.POINTER(ctypes.c_int32)),
+        ("block_capacity", ctypes.c_int32),
+    ]
+
+
 _lib = None
 
 _P = ctypes.c_void_p
@@ -123,6 +135,10 @@ _SIGNATURES = {
     "pkv_window_table": (ctypes.c_int, [_PI32, _I64, _I64, _I64, _I64, _I64, _I32, _PI32, _I32, _PI32, _PI32]),
     "pkv_action_table": (ctypes.c_int, [_PI32, _I32, _PI32, _PI32, _PI32, _I32, _I64, _I32]),
     "pkv_build_segments": (ctypes.c_int, [_PI32, _I32, _I32, _I32, _PI32, _I32, _PI32]),
+    "pkv_staging_decide": (
+        ctypes.c_int,
+        [ctypes.POINTER(_StagingState), _I64, _PI32, _I32, _I64, _I64, _I32, _I32, _I64, _PI32, _PI32],
+    ),
     "pkv_validate_metadata_host": (
         ctypes.c_int,
         [_PI32, _PI32, _I32, _PI32, _I32, _I64, _I32, _I32, _I32, _PI32, _PI32, _PI32],
@@ -558,6 +574,28 @@ def pkv_build_segments(full_spans, query_offset: int, query_len: int) -> np.ndar
         )
     )
     return out[: count.value].copy()
+
+
+class StagingState:
+    """Caller-owned pkv_staging_state with room for ``block_capacity`` history block ids."""
+
+    def __init__(self, block_capacity: int):
+        self.blocks = np.zeros(max(int(block_capacity), 1), dtype=np.int32)
+        self.c = _StagingState(-1, 0, 0, 0, 0, self.blocks.ctypes.data_as(ctypes.POINTER(ctypes.c_int32)),
+                               int(block_capacity))
+
+
+def pkv_staging_decide(state: StagingState, session: int, table, history_tokens: int, chunk_tokens: int,
+                       max_seq_len: int, block_size: int, capacity_tokens: int) -> tuple[bool, int]:
+    """(reuse, first_block) of one staged forward; see include/pkv.h."""
+    t = _host_i32(table)
+    reuse, first = ctypes.c_int32(0), ctypes.c_int32(0)
+    _check(
+        lib().pkv_staging_decide(ctypes.byref(state.c), int(session), _ptr(t, ctypes.c_int32), t.size,
+                                 int(history_tokens), int(chunk_tokens), int(max_seq_len), int(block_size),
+                                 int(capacity_tokens), ctypes.byref(reuse), ctypes.byref(first))
+    )
+    return bool(reuse.value), int(first.value)
 
 
 def pkv_validate_metadata_host(query_start_loc, seq_lens, block_table, num_blocks, block_size, max_query_len, max_seq_len,

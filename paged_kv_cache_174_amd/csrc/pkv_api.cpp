@@ -640,30 +640,86 @@ int pkv_build_segments(const int32_t* full_spans, int32_t num_spans, int32_t que
       return fail(PKV_EINVAL, "full spans must be sorted, non-empty and non-overlapping (span %d = [%d, %d))", k, a, b);
     prev_end = b;
   }
+  // The mask rule (P3 module docstring): a query row inside a full span
+  // [a, b) attends K[:b]; every other row belongs to a causal segment [s, e)
+  // that attends K[:e] bottom-right aligned.  Sweep the span edges that fall
+  // strictly inside the query range: between two consecutive edges every row
+  // has the same rule, and neighbouring pieces with the same rule (the rows
+  // outside spans, or one span's rows) are one segment.
   const int32_t lo = query_offset, hi = query_offset + query_len;
+  std::vector<int32_t> edges{lo, hi};
+  for (int32_t k = 0; k < num_spans; ++k)
+    for (int32_t e : {full_spans[2 * k], full_spans[2 * k + 1]})
+      if (e > lo && e < hi) edges.push_back(e);
+  std::sort(edges.begin(), edges.end());
+  edges.erase(std::unique(edges.begin(), edges.end()), edges.end());
   int32_t n = 0;
-  auto emit = [&](int32_t qs, int32_t qe, int32_t kv, int32_t mode) -> int {
+  int32_t span = 0;  // first span that does not end at or before the current piece
+  for (size_t i = 0; i + 1 < edges.size(); ++i) {
+    const int32_t p0 = edges[i], p1 = edges[i + 1];
+    while (span < num_spans && full_spans[2 * span + 1] <= p0) ++span;
+    const bool full = span < num_spans && full_spans[2 * span] <= p0;
+    const int32_t mode = full ? PKV_SEG_FULL : PKV_SEG_CAUSAL;
+    const int32_t kv = full ? full_spans[2 * span + 1] : p1;
+    int32_t* last = n > 0 ? out_segments + 4 * (n - 1) : nullptr;
+    if (last && last[3] == mode && (mode == PKV_SEG_CAUSAL || last[2] == kv)) {
+      last[1] = p1;
+      if (mode == PKV_SEG_CAUSAL) last[2] = p1;
+      continue;
+    }
     if (n >= capacity) return fail(PKV_ERANGE, "segment capacity %d too small", capacity);
-    out_segments[4 * n + 0] = qs;
-    out_segments[4 * n + 1] = qe;
-    out_segments[4 * n + 2] = kv;
-    out_segments[4 * n + 3] = mode;
-    ++n;
-    return PKV_OK;
-  };
-  int32_t cursor = lo;
-  for (int32_t k = 0; k < num_spans; ++k) {
-    const int32_t a = std::max(full_spans[2 * k], lo);
-    const int32_t b = std::min(full_spans[2 * k + 1], hi);
-    if (a >= b) continue;  // span misses the query range
-    if (cursor < a)
-      if (int rc = emit(cursor, a, a, PKV_SEG_CAUSAL)) return rc;
-    if (int rc = emit(a, b, full_spans[2 * k + 1], PKV_SEG_FULL)) return rc;
-    cursor = b;
+    int32_t* seg = out_segments + 4 * n++;
+    seg[0] = p0;
+    seg[1] = p1;
+    seg[2] = kv;
+    seg[3] = mode;
   }
-  if (cursor < hi)
-    if (int rc = emit(cursor, hi, hi, PKV_SEG_CAUSAL)) return rc;
   *out_count = n;
+  return PKV_OK;
+}
+
+// P1 _prepare_history_staging, restated: a staged window may be kept when
+// the buffers were last filled for the same request and nothing they hold
+// has moved since -- the history (its length and the blocks the window lists
+// for it), the staged extent and the chunk length -- and the chunk owns its
+// blocks outright (it starts on a block edge and fills whole blocks).  Then
+// only the chunk's blocks, after the history's, are gathered again.
+int pkv_staging_decide(pkv_staging_state* st, int64_t session, const int32_t* table, int32_t table_len,
+                       int64_t history_tokens, int64_t chunk_tokens, int32_t max_seq_len, int32_t block_size,
+                       int64_t capacity_tokens, int32_t* out_reuse, int32_t* out_first_block) {
+  g_error[0] = '\0';
+  if (!st || !out_reuse || !out_first_block || (table_len > 0 && !table) ||
+      (st->block_capacity > 0 && !st->history_blocks))
+    return fail(PKV_EINVAL, "NULL pointer");
+  if (session < 0 || table_len < 0 || history_tokens < 0 || chunk_tokens <= 0 || block_size <= 0 ||
+      max_seq_len <= 0 || st->block_capacity < 0)
+    return fail(PKV_EINVAL, "bad sizes");
+  if (max_seq_len > capacity_tokens)
+    return fail(PKV_ERANGE, "the staging buffers hold %lld tokens but this forward stages %d",
+                static_cast<long long>(capacity_tokens), max_seq_len);
+  const int64_t offset = history_tokens % block_size;  // where the chunk starts in its first block
+  const int64_t chunk_blocks = (offset + chunk_tokens + block_size - 1) / block_size;
+  if (chunk_blocks > table_len)
+    return fail(PKV_EINVAL, "a %d-entry table cannot hold a chunk spanning %lld blocks", table_len,
+                static_cast<long long>(chunk_blocks));
+  const int32_t hist_blocks = table_len - static_cast<int32_t>(chunk_blocks);
+  if (hist_blocks > st->block_capacity)
+    return fail(PKV_ERANGE, "the visible history lists %d blocks; the state records at most %d", hist_blocks,
+                st->block_capacity);
+  const bool chunk_owns_blocks = offset == 0 && chunk_tokens % block_size == 0;
+  const bool unchanged = st->session == session && st->history_tokens == history_tokens &&
+                         st->chunk_tokens == chunk_tokens && st->max_seq_len == max_seq_len &&
+                         st->num_history_blocks == hist_blocks &&
+                         std::equal(table, table + hist_blocks, st->history_blocks);
+  const bool reuse = chunk_owns_blocks && unchanged;
+  st->session = session;
+  st->history_tokens = history_tokens;
+  st->chunk_tokens = chunk_tokens;
+  st->max_seq_len = max_seq_len;
+  st->num_history_blocks = hist_blocks;
+  std::copy(table, table + hist_blocks, st->history_blocks);
+  *out_reuse = reuse ? 1 : 0;
+  *out_first_block = reuse ? hist_blocks : 0;
   return PKV_OK;
 }
 
@@ -699,6 +755,7 @@ int pkv_validate_metadata_host(const int32_t* qsl, const int32_t* seq_lens, int3
     const int32_t s0 = seg_loc[b], s1 = seg_loc[b + 1];
     if (s1 <= s0) return fail(PKV_EINVAL, "sequence %d has no segments", b);
     int32_t cursor = g0;
+    int32_t prev_limit = 0;  // key limit of the previous segment's last row
     for (int32_t k = s0; k < s1; ++k) {
       const int32_t qs = segments[4 * k], qe = segments[4 * k + 1], kv = segments[4 * k + 2], mode = segments[4 * k + 3];
       if (qs != cursor || qe <= qs) return fail(PKV_EINVAL, "sequence %d: segments must tile the query in order", b);
@@ -709,6 +766,16 @@ int pkv_validate_metadata_host(const int32_t* qsl, const int32_t* seq_lens, int3
       } else {
         return fail(PKV_EINVAL, "sequence %d: unknown segment mode %d", b, mode);
       }
+      // Row limits L(g): kv_end over a full segment, g + 1 down a causal
+      // one.  The kernels bound a tile of rows by its last row's limit and
+      // skip the mask below a wave's first row's, so L must not decrease.
+      const int32_t first_limit = mode == PKV_SEG_FULL ? kv : qs + 1;
+      if (k > s0 && first_limit < prev_limit)
+        return fail(PKV_EINVAL,
+                    "sequence %d: segment %d's rows see %d keys but the row before them sees %d; key limits must "
+                    "not decrease down the query",
+                    b, k - s0, first_limit, prev_limit);
+      prev_limit = mode == PKV_SEG_FULL ? kv : qe;
       cursor = qe;
     }
     if (cursor != g0 + q)

@@ -268,45 +268,46 @@ class StagingDecision:
 
 class HistoryStaging:
     """Reuse state of one KV branch's staging buffers (P1
-    ``_prepare_history_staging``).
+    ``_prepare_history_staging``); the decision itself is the C library's
+    ``pkv_staging_decide``.
 
-    The staged window can be kept when nothing about it moved since the last
-    forward: the same session, the same visible history (its length, its
-    blocks), the same capacity and chunk length, and a current chunk that is
-    whole blocks starting on a block edge (a chunk that shares its first block
-    with the history's tail makes the whole window restage).  Then only the
-    current chunk's blocks are gathered again: block rows from the visible
-    history's block count on.  The decision is a host value, the same for all
-    layers of a forward.  One sequence and no action tokens only.
+    A forward keeps the staged history when the buffers were last filled for
+    the same session (compared by identity) and its history, extent and chunk
+    length are unchanged, and the chunk fills whole blocks from a block edge;
+    then only the chunk's blocks are gathered again, from the visible
+    history's block count on.  Otherwise ``first_block`` is 0: everything is
+    restaged.  The decision is a host value, the same for all layers of a
+    forward.  One sequence and no action tokens only.
     """
 
     def __init__(self, capacity_tokens: int):
         self.capacity_tokens = int(capacity_tokens)
-        self._session = None  # weak reference to the last session
-        self._signature = None
+        self._session = None  # weak reference to the session staged last
+        self._session_id = -1
+        self._next_id = 0
+        self._state = None
+        self._block_size = None
+
+    def _id_of(self, session) -> int:
+        last = self._session() if self._session is not None else None
+        if last is None or last is not session:
+            self._session_id, self._next_id = self._next_id, self._next_id + 1
+            try:
+                self._session = weakref.ref(session)
+            except TypeError:  # not weakly referenceable: keep it alive instead
+                self._session = (lambda s: (lambda: s))(session)
+        return self._session_id
 
     def decide(self, session, plan: ForwardPlan) -> StagingDecision:
         """``session`` identifies the request (compared by identity)."""
         if plan.num_seqs != 1 or any(plan.action_lens):
             return StagingDecision(False, False, 0)
-        if plan.max_seq_len > self.capacity_tokens:
-            raise RuntimeError(
-                f"history staging buffers hold {self.capacity_tokens} tokens but this forward stages {plan.max_seq_len}"
-            )
         B = plan.block_size
-        h, q, kv_len = plan.history_lens[0], plan.chunk_lens[0], plan.kv_lens[0]
-        start_offset = h % B  # where the chunk starts inside its first block
-        current_blocks = -(-(start_offset + q) // B)
-        table = [int(x) for x in plan.tables[0]]
-        history_blocks = tuple(table[: len(table) - current_blocks])
-        signature = (h, history_blocks, int(plan.max_seq_len), q)
-        last = self._session() if self._session is not None else None
-        same_session = last is not None and last is session
-        block_aligned = start_offset == 0 and q % B == 0
-        reuse = same_session and self._signature == signature and block_aligned
-        try:
-            self._session = weakref.ref(session)
-        except TypeError:  # not weakly referenceable: keep it alive instead
-            self._session = (lambda s: (lambda: s))(session)
-        self._signature = signature
-        return StagingDecision(True, bool(reuse), kv_len // B - current_blocks)
+        if self._state is None or self._block_size != B:
+            self._state = L.StagingState(self.capacity_tokens // B + 1)
+            self._block_size = B
+        reuse, first = L.pkv_staging_decide(
+            self._state, self._id_of(session), plan.tables[0], plan.history_lens[0], plan.chunk_lens[0],
+            plan.max_seq_len, B, self.capacity_tokens,
+        )
+        return StagingDecision(True, reuse, first)

@@ -162,10 +162,10 @@ def test_staged_fused_call_restages_then_reuses(pool):
         li.k_hist, li.v_hist = li0.k_hist, li0.v_hist
         d = staging.decide(session, plan)
         assert d.enabled and d.reuse == (probe == 1)
-        assert d.first_block == plan.kv_lens[0] // B - geom.query_lens[0] // B
-        G.say("staged", pool, "probe", probe, "first_block", d.first_block if d.reuse else 0)
+        assert d.first_block == (plan.kv_lens[0] // B - geom.query_lens[0] // B if d.reuse else 0)
+        G.say("staged", pool, "probe", probe, "first_block", d.first_block)
         out = G.write_attend(plan, pools, li, geom, stage_key=sk, stage_value=sv,
-                             first_block=d.first_block if d.reuse else 0)
+                             first_block=d.first_block)
         torch.cuda.synchronize()
         H.write_current(geom, meta, li, k_ref, v_ref)
         want_k = np.full((shape[0],) + k_ref.shape[1:], 0, dtype=k_ref.dtype)
@@ -342,7 +342,10 @@ def test_staged_calls_replay_in_two_graphs():
     static = dict(q=li0.q.clone(), k=li0.k_cur.clone(), v=li0.v_cur.clone())
     out = torch.empty_like(static["q"])
     staging = G.P.HistoryStaging(capacity_tokens=shape[0])
-    d = staging.decide(object(), plan)
+    session = object()
+    staging.decide(session, plan)
+    d = staging.decide(session, plan)  # the same window again: the history is kept
+    assert d.reuse and d.first_block > 0
     first = d.first_block
     scale = H.softmax_scale(geom.head_dim)
 

@@ -47,9 +47,10 @@ def test_reruns_are_bit_identical(kind, workspace):
 
 
 def test_one_workspace_serves_calls_of_different_shapes():
-    """The split path keeps per-tile arrival counters in the workspace: a
-    workspace full of garbage, then reused by a call with another tiling, gives
-    the same bits as a fresh one each time."""
+    """The split path writes one partial result per split into the workspace
+    and a second launch merges them: a workspace full of garbage, then reused
+    by a call with another tiling, gives the same bits as a fresh one each
+    time."""
     geoms = [
         small_variant(CONFIGS["piecewise_gqa_bf16"], name="ws_a", num_q_heads=2, num_kv_heads=2,
                       history_lens=(2000,), query_lens=(700,), full_spans=((),)),

@@ -92,6 +92,8 @@ def test_segments_match_oracle(pkv):
         q = int(rng.integers(1, s + 1))
         cuts = sorted(set(rng.integers(0, s + 1, size=int(rng.integers(0, 8))).tolist()))
         spans = [(cuts[i], cuts[i + 1]) for i in range(0, len(cuts) - 1, 2) if cuts[i] < cuts[i + 1]]
+        if rng.random() < 0.3 and len(spans) >= 2:  # make two spans touch
+            spans[1] = (spans[0][1], spans[1][1])
         got = pkv.pkv_build_segments(spans, s - q, q)
         want = O.build_segments(spans, s - q, q)
         assert [tuple(r) for r in got.tolist()] == [
@@ -154,6 +156,38 @@ def test_validate_metadata_rejects_what_the_pages_reject(pkv):
     seg = plan.segments_host.copy()
     seg[1, 0] += 1  # gap in the tiling
     bad(segments=seg)
+
+
+def test_validate_metadata_rejects_decreasing_row_limits(pkv):
+    """The kernels bound a row tile's keys by its last row's limit and skip
+    the mask below a wave's first row's, so a segment list whose per-row key
+    limit L(g) drops from one row to the next must be refused (P3's
+    build_segments never makes one: a full segment reaches past its q_end
+    only as the last segment)."""
+    F, C = 1, 0
+
+    def check(seq_len, q_len, segs, query_pos=None, ok=False):
+        nb = (seq_len + 15) // 16
+        kw = dict(query_start_loc=np.array([0, q_len], np.int32), seq_lens=np.array([seq_len], np.int32),
+                  block_table=np.arange(nb, dtype=np.int32)[None, :], num_blocks=nb, block_size=16,
+                  max_query_len=q_len, max_seq_len=seq_len, segments=np.array(segs, np.int32),
+                  segment_start_loc=np.array([0, len(segs)], np.int32),
+                  query_pos=None if query_pos is None else np.array([query_pos], np.int32))
+        if ok:
+            pkv.pkv_validate_metadata_host(**kw)
+        else:
+            with pytest.raises(ValueError, match="decrease"):
+                pkv.pkv_validate_metadata_host(**kw)
+
+    # full rows see 600 keys, the causal rows after them 11 .. 600
+    check(600, 600, [(0, 10, 600, F), (10, 600, 600, C)])
+    # a shard [100, 200) of 300 keys: full rows see 300, the causal rows 151 .. 200
+    check(300, 100, [(100, 150, 300, F), (150, 200, 200, C)], query_pos=100)
+    # two full segments with falling kv_end
+    check(300, 300, [(0, 100, 250, F), (100, 300, 300, C)])
+    # allowed: equal limits across the boundary, and a last full segment reaching past the query
+    check(300, 300, [(0, 10, 11, F), (10, 300, 300, C)], ok=True)
+    check(300, 100, [(100, 150, 150, C), (150, 200, 300, F)], query_pos=100, ok=True)
 
 
 # --------------------------------------------------------------------------- action tokens and staging reuse
@@ -260,6 +294,28 @@ def test_history_staging_decisions_match_oracle(pkv, seed):
         assert (got.enabled, got.reuse, got.first_block) == want
         reused += got.reuse
     assert reused > 0 or _tick_events(seed)[0][2] % 16  # aligned runs must reuse somewhere
+
+
+def test_staging_decide_c_abi(pkv):
+    """pkv_staging_decide on its own: reuse needs the same session id, history,
+    extent and chunk length and a chunk of whole blocks; without reuse
+    first_block is 0; a refused call leaves the state as it was."""
+    from paged_kv_cache_174_amd import _lib as L
+
+    st = L.StagingState(8)
+    table = [5, 6, 7, 9]  # three history blocks, then the chunk's block
+    assert L.pkv_staging_decide(st, 1, table, 48, 16, 64, 16, 64) == (False, 0)
+    assert L.pkv_staging_decide(st, 1, table, 48, 16, 64, 16, 64) == (True, 3)
+    assert L.pkv_staging_decide(st, 2, table, 48, 16, 64, 16, 64) == (False, 0)  # another request
+    assert L.pkv_staging_decide(st, 2, [5, 6, 8, 9], 48, 16, 64, 16, 64) == (False, 0)  # a history block moved
+    with pytest.raises(RuntimeError):
+        L.pkv_staging_decide(st, 2, [5, 6, 8, 9], 48, 16, 80, 16, 64)  # extent past the buffers
+    assert L.pkv_staging_decide(st, 2, [5, 6, 8, 9], 48, 16, 64, 16, 64) == (True, 3)  # state kept
+    # a chunk that shares its first block with the history never reuses
+    assert L.pkv_staging_decide(st, 3, [5, 6, 7], 40, 8, 48, 16, 64) == (False, 0)
+    assert L.pkv_staging_decide(st, 3, [5, 6, 7], 40, 8, 48, 16, 64) == (False, 0)
+    with pytest.raises(ValueError):
+        L.pkv_staging_decide(st, 3, [5], 40, 40, 48, 16, 64)  # the table cannot hold the chunk
 
 
 def test_history_staging_is_off_for_actions_and_batches(pkv):

@@ -182,6 +182,19 @@ def test_segments_golden():
         assert [[s.q_start, s.q_end, s.kv_end, s.mode] for s in segs] == case["segments"], case["why"]
 
 
+def test_segments_of_touching_spans_stay_apart():
+    """Two full spans that touch, [2, 5) and [5, 9), over the query [0, 12):
+    their rows attend K[:5] and K[:9] respectively (P3 module docstring), so
+    they are two full segments, between causal runs [0, 2) and [9, 12)."""
+    segs = O.build_segments([(2, 5), (5, 9)], 0, 12)
+    assert [(g.q_start, g.q_end, g.kv_end, g.mode) for g in segs] == [
+        (0, 2, 2, "causal"), (2, 5, 5, "full"), (5, 9, 9, "full"), (9, 12, 12, "causal")]
+    # a span that starts before the query and one that ends past it keep their own ends
+    segs = O.build_segments([(0, 4), (10, 20)], 3, 9)
+    assert [(g.q_start, g.q_end, g.kv_end, g.mode) for g in segs] == [
+        (3, 4, 4, "full"), (4, 10, 10, "causal"), (10, 12, 20, "full")]
+
+
 def test_row_limits_against_the_docstring_rule_by_enumeration():
     """P3's docstring: a row inside a full span [a, b) sees keys < b; any other
     row is causal and sees keys <= its own position.  Enumerate random span sets
