@@ -81,13 +81,16 @@ using Buf = std::integral_constant<int, B>;
 // lane i's 16 bytes at byte offset off of the descriptor's range land at
 // l + 16 i; offsets at or past the range read zeros.  Inline assembly, so
 // the compiler adds no waits for it (the kernel waits with wait_vmcnt).  It
-// carries the five wait states that a vector-memory read of an SGPR needs
-// after a VALU write of it (v_readfirstlane), which the compiler does not
-// insert for inline assembly, whether or not the descriptor's parts were
-// made on the scalar unit in a given build, and the one after M0.
-__device__ __forceinline__ void dma16_buf(__amdgpu_buffer_rsrc_t r, uint32_t off, const void* l) {
+// carries the one wait state needed after M0 is written.  A vector-memory
+// read of an SGPR also needs five after a VALU write of it (v_readfirstlane),
+// which the compiler does not insert for inline assembly; the descriptors
+// here are built on the scalar unit from values made wave-uniform long
+// before, so no such write comes near a load (the kernel's assembly is
+// checked for it).  Five wait states are twenty cycles of a wave's issue,
+// which would be paid on every load.
+__device__ __forceinline__ void dma16_buf(u32x4 r, uint32_t off, const void* l) {
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)l));
-  asm volatile(PKV_VMEM_SGPR_WAIT "buffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0));
+  asm volatile("s_nop 0\nbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0));
 }
 
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void
@@ -220,23 +223,30 @@ attn_long_kernel(AttnArgs a) {
   auto block_base = [&](int kt) { return entry_base(block_entry(kt)); };
   // (The descriptor must live in SGPRs: its parts are made wave-uniform
   // explicitly, as the compiler cannot prove it for the range.)
-  // The range, (rows of the block below kv_lim) x row_bytes, on the scalar
-  // unit (the compiler would clamp with a vector med3 and multiply).
+  // The descriptor is built by scalar instructions only, whatever the
+  // compiler does around it: base = pool + boff (stride 0), range = (rows of
+  // the block below kv_lim) x row_bytes.  Its inputs are wave-uniform values
+  // (a v_readfirstlane may make them; the scalar unit waits for those, the
+  // direct load reads only what the scalar unit wrote).
   const int kv_lim_w = __builtin_amdgcn_readfirstlane(kv_lim - 16 * w);
   const int row_bytes32 = __builtin_amdgcn_readfirstlane(static_cast<int>(row_bytes));
   auto rsrc = [&](const uint8_t* pool, int64_t boff, int kt) {
-    int bytes;
-    asm("s_sub_i32 %0, %1, %2\n"
-        "s_max_i32 %0, %0, 0\n"
-        "s_min_i32 %0, %0, 16\n"
-        "s_mul_i32 %0, %0, %3"
-        : "=&s"(bytes)
-        : "s"(kv_lim_w), "s"(kt), "s"(row_bytes32)
+    const uint64_t p = reinterpret_cast<uint64_t>(pool);
+    const uint64_t o = static_cast<uint64_t>(boff);
+    uint32_t lo, hi, bytes;
+    asm("s_add_u32 %0, %3, %5\n"
+        "s_addc_u32 %1, %4, %6\n"
+        "s_and_b32 %1, %1, 0xffff\n"
+        "s_sub_i32 %2, %7, %8\n"
+        "s_max_i32 %2, %2, 0\n"
+        "s_min_i32 %2, %2, 16\n"
+        "s_mul_i32 %2, %2, %9"
+        : "=&s"(lo), "=&s"(hi), "=&s"(bytes)
+        : "s"(static_cast<uint32_t>(p)), "s"(static_cast<uint32_t>(p >> 32)), "s"(static_cast<uint32_t>(o)),
+          "s"(static_cast<uint32_t>(o >> 32)), "s"(kv_lim_w), "s"(kt), "s"(row_bytes32)
         : "scc");
-    const uint64_t base = reinterpret_cast<uint64_t>(pool + boff);
-    const uint64_t ubase = (static_cast<uint64_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base >> 32))) << 32) |
-                           static_cast<uint32_t>(__builtin_amdgcn_readfirstlane(static_cast<uint32_t>(base)));
-    return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>(ubase), 0, bytes, kBufferWord3);
+    const u32x4 d = {lo, hi, bytes, static_cast<uint32_t>(kBufferWord3)};
+    return d;
   };
   // Row group st (four rows) of this wave's block into buffer B.
   auto load_k = [&](int kt, auto bufc, int64_t boff, int st) {
@@ -386,7 +396,7 @@ attn_long_kernel(AttnArgs a) {
     constexpr int HQ = BETA ? 0 : 1, HS = 1 - HQ, HP = HQ;
     const uint32_t roff = blk_off(BR, KR);
     const int kt_load = kt_of(t_load);
-    __amdgpu_buffer_rsrc_t drs;
+    u32x4 drs = {0u, 0u, 0u, 0u};
     if constexpr (LOAD != 0) drs = rsrc(LOAD == 1 ? kpool : vpool, boff, kt_load);
     float p[16];
     u32x4 pk[2];
