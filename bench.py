@@ -11,15 +11,19 @@ written (untimed) during setup.
 
 Prints one JSON line.  `value` is algorithmic attention TFLOP/s over whole
 steps (4 * D * Hq * visible query-key pairs per call).  `roofline` is for the
-attention kernel (attn_mfma_kernel), timed with HIP events on the stream the
-library launches on; its `traffic` comes from the committed rocprofv3
-FETCH_SIZE / WRITE_SIZE summary for this workload when that summary was taken
-on the current kernel sources (null otherwise).  `kv_bound` times the same
-kernel on the KV-bound half of the varlen fp8 batch (query length 16) against
-HBM bandwidth.  `parts` reports the write, the merge and the history-staging
-gather on their own (the per-launch pass issues the three calls separately,
-with events between them), the step as three separate calls per layer, and the
-step captured once in a HIP graph and replayed.
+attention kernel (attn_long_kernel for bf16 chunks), timed with HIP events on
+the stream the library launches on; its `traffic` comes from the committed
+rocprofv3 FETCH_SIZE / WRITE_SIZE summary for this workload when that summary
+was taken on the current kernel sources (null otherwise).  `kv_bound` times
+the short-query kernel and its split merge on the KV-bound half of the varlen
+fp8 batch (query length 16) against HBM bandwidth.  `parts` reports the write,
+the merge and the history-staging gather on their own (the per-launch pass
+issues the three calls separately, with events between them), the step as
+three separate calls per layer, the step captured once in a HIP graph and
+replayed, the write and the gather at 1 GiB (HBM figures), and whole steps of
+the other workloads (`configs`: the piecewise GQA chunk, the 40-layer step,
+and the whole varlen fp8 batch against max(FLOPs / MFMA peak, bytes / HBM
+bandwidth)).
 
     python bench.py [--steps K] [--warmup W] [--workload frame_bf16]
 """
@@ -46,7 +50,10 @@ ELT = {"f32": 4, "bf16": 2, "fp8": 1}
 
 
 # Sources whose change invalidates a stored traffic measurement of the attention kernel.
-KERNEL_SOURCES = ("attn_mfma.hip", "attn_common.hpp", "pkv_internal.hpp", "pkv_api.cpp")
+KERNEL_SOURCES = ("attn_long.hip", "attn_mfma.hip", "mfma_util.hpp", "attn_common.hpp", "pkv_internal.hpp",
+                  "pkv_api.cpp")
+# The non-headline workloads reported under parts.configs (each timed as whole steps).
+OTHER_CONFIGS = ("piecewise_gqa_bf16", "ar_step_40L_bf16", "varlen_fp8")
 
 
 def parse():
@@ -58,6 +65,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-kv-bound", action="store_true")
     ap.add_argument("--cpu-budget-s", type=float, default=20.0)
+    ap.add_argument("--no-configs", action="store_true", help="skip the other workloads under parts.configs")
+    ap.add_argument("--no-hbm-copies", action="store_true", help="skip the 1 GiB write and gather figures")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (the gather kernel) a few times, so that a "
                          "counter run can scale FETCH_SIZE / WRITE_SIZE by a known byte count")
@@ -82,7 +91,7 @@ def kernel_source_hash() -> str:
 def stored_traffic(workload: str):
     """HBM bytes per attention launch from the committed counter summary, or
     None when there is none or it was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"attn_mfma_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"attn_long_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -314,6 +323,141 @@ def run_bench(args, geom):
     }
 
 
+def run_config(geom, steps, warmup):
+    """Whole steps of another workload (the fused call per layer), and a
+    per-launch pass of its attention kernel and merge with events between.
+    For a workload that is not MFMA-bound throughout (the varlen fp8 batch
+    mixes 16-row decode-like sequences with 1560-row chunks) the step is also
+    compared with max(F / P, B / BW): its algorithmic FLOPs at the bf16 MFMA
+    peak or its algorithmic bytes at HBM bandwidth, whichever takes longer."""
+    import paged_kv_cache_174_amd as P
+
+    wl, plan, layers, ws = setup(geom)
+    scale = _softmax_scale(geom.head_dim)
+    stream = torch.cuda.current_stream()
+
+    def attn_args(li, pools):
+        return (li.q, pools, plan.block_table, plan.query_start_loc, plan.seq_lens, plan.segments,
+                plan.segment_start_loc, scale, plan.max_query_len, plan.max_seq_len)
+
+    def step():
+        for li, pools, out in layers:
+            P.pkv_paged_write_attn(li.q, li.k_cur, li.v_cur, plan.slot_mapping, pools, plan, scale, out=out,
+                                   workspace=ws)
+
+    settle0 = time.perf_counter()
+    while time.perf_counter() - settle0 < 0.5:
+        step()
+        torch.cuda.synchronize()
+    nl = len(layers)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * nl * steps)]
+    k = 0
+    for _ in range(steps):
+        for li, pools, out in layers:
+            ev[k].record(stream)
+            P.pkv_paged_attn_main(*attn_args(li, pools), out=out, workspace=ws, seq_order=plan.seq_order,
+                                  host_seq_lens=plan.kv_lens)
+            ev[k + 1].record(stream)
+            P.pkv_paged_attn_merge(*attn_args(li, pools), out=out, workspace=ws, seq_order=plan.seq_order,
+                                   host_seq_lens=plan.kv_lens)
+            ev[k + 2].record(stream)
+            k += 3
+    torch.cuda.synchronize()
+    main_ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(0, k, 3)]))
+    merge_ms = float(np.mean([ev[i + 1].elapsed_time(ev[i + 2]) for i in range(0, k, 3)]))
+    for _ in range(warmup):
+        step()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(steps):
+        step()
+    b.record(stream)
+    torch.cuda.synchronize()
+    step_ms = a.elapsed_time(b) / steps
+    flops = plan.attn_flops(geom.num_q_heads, geom.head_dim)
+    abytes = attn_bytes(geom, plan)
+    call_ms = main_ms + merge_ms
+    bound_ms = max(flops / (PEAK_BF16_TFLOPS * 1e12), abytes / (PEAK_HBM_GBPS * 1e9)) * 1e3
+    res = {
+        "layers": nl,
+        "step_ms": round(step_ms, 4),
+        "tflops": round(flops * nl / (step_ms * 1e-3) / 1e12, 2),
+        "attn_call_ms": round(call_ms, 5),
+        "attn_main_ms": round(main_ms, 5),
+        "attn_merge_ms": round(merge_ms, 5),
+        "attn_tflops": round(flops / (call_ms * 1e-3) / 1e12, 2),
+        "attn_frac_of_bf16_peak": round(flops / (call_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "main_tflops": round(flops / (main_ms * 1e-3) / 1e12, 2),
+        "main_frac_of_bf16_peak": round(flops / (main_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
+        "flop_per_call": flops,
+        "bytes_per_call": abytes,
+        "bound_ms": round(bound_ms, 5),
+        "bound": "mfma" if flops / (PEAK_BF16_TFLOPS * 1e12) >= abytes / (PEAK_HBM_GBPS * 1e9) else "hbm",
+        "frac_of_bound": round(bound_ms / call_ms, 4),
+    }
+    del layers, ws, wl
+    torch.cuda.empty_cache()
+    return res
+
+
+def hbm_copies(geom, total_bytes=1 << 30, reps=5):
+    """The write and the gather on their own at HBM scale: one write call
+    scattering `total_bytes` of K+V rows (bf16 into the workload's pool dtype)
+    into a pool twice that size through a shuffled block-granular slot
+    mapping, and one gather of `total_bytes` of K+V blocks by shuffled block
+    ids into a staging buffer.  Both sides are far larger than the caches,
+    so the rates are HBM figures."""
+    import paged_kv_cache_174_amd as P
+
+    dt = {"f32": torch.float32, "bf16": torch.bfloat16, "fp8": torch.uint8}[geom.pool_dtype]
+    B, H, D = geom.block_size, geom.num_kv_heads, geom.head_dim
+    src_elt = 4 if geom.pool_dtype == "f32" else 2
+    tokens = total_bytes // 2 // (H * D * src_elt) // B * B
+    blocks = tokens // B
+    pool_blocks = 2 * blocks
+    g = torch.Generator(device="cuda")
+    g.manual_seed(7)
+    kp = torch.zeros((pool_blocks * B, H, D), dtype=dt, device="cuda")
+    vp = torch.zeros_like(kp)
+    pools = P.Pools(kp, vp, B, 1.0, 1.0, 1.0, 1.0)
+    sdt = torch.float32 if geom.pool_dtype == "f32" else torch.bfloat16
+    k = torch.randn((tokens, H, D), generator=g, device="cuda").to(sdt)
+    v = torch.randn((tokens, H, D), generator=g, device="cuda").to(sdt)
+    perm = torch.randperm(pool_blocks, generator=g, device="cuda")[:blocks]
+    slots = (perm[:, None] * B + torch.arange(B, device="cuda")[None, :]).reshape(-1).to(torch.int64)
+    ids = torch.randperm(pool_blocks, generator=g, device="cuda")[:blocks].to(torch.int32)
+    sk = torch.empty((tokens, H, D), dtype=dt, device="cuda")
+    sv = torch.empty_like(sk)
+    torch.cuda.synchronize()
+
+    def timed(fn):
+        fn()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        for _ in range(reps):
+            fn()
+        b.record()
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / reps
+
+    w_ms = timed(lambda: P.pkv_paged_write(k, v, slots, pools))
+    g_ms = timed(lambda: P.pkv_gather(pools, ids, blocks, 0, sk, sv))
+    pool_elt = kp.element_size()
+    w_bytes = 2 * tokens * H * D * (src_elt + pool_elt) + 8 * tokens
+    g_bytes = 2 * 2 * tokens * H * D * pool_elt + 4 * blocks
+    res = {
+        "paged_write_1gib": {"ms": round(w_ms, 4), "bytes": int(w_bytes), "gbps": round(w_bytes / (w_ms * 1e-3) / 1e9, 1),
+                             "frac_of_hbm": round(w_bytes / (w_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+        "gather_1gib": {"ms": round(g_ms, 4), "bytes": int(g_bytes), "gbps": round(g_bytes / (g_ms * 1e-3) / 1e9, 1),
+                        "frac_of_hbm": round(g_bytes / (g_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS, 4)},
+    }
+    del kp, vp, k, v, sk, sv, pools
+    torch.cuda.empty_cache()
+    return res
+
+
 def copy_calibration(pools, total_bytes=1 << 30, reps=3):
     """A plain device copy of known size for scaling memory counters: the
     gather kernel copying whole blocks of K and V (reads and writes
@@ -364,7 +508,7 @@ def run_kv_bound(args):
             launch(*layer)
     torch.cuda.synchronize()
     n = max(args.steps, 5)
-    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2 * n * len(layers))]
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(3 * n * len(layers))]
     k = 0
     for _ in range(n):
         for layer in layers:
@@ -375,23 +519,28 @@ def run_kv_bound(args):
                                    plan.segments, plan.segment_start_loc, scale, plan.max_query_len,
                                    plan.max_seq_len, out=layer[2], workspace=ws, seq_order=plan.seq_order,
                                    host_seq_lens=plan.kv_lens)
-            k += 2
+            ev[k + 2].record(stream)
+            k += 3
     torch.cuda.synchronize()
-    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 2)]))
+    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 3)]))
+    call_ms = float(np.mean([ev[i].elapsed_time(ev[i + 2]) for i in range(0, len(ev), 3)]))
     abytes = attn_bytes(geom, plan)
     flops = plan.attn_flops(geom.num_q_heads, geom.head_dim)
-    gbps = abytes / (ms * 1e-3) / 1e9
+    gbps = abytes / (call_ms * 1e-3) / 1e9
+    main_gbps = abytes / (ms * 1e-3) / 1e9
     return {
         "workload": geom.name,
-        "kernel": "attn_mfma_kernel<fp8, short rows>",
+        "kernel": "attn_mfma_kernel<fp8, short rows> + attn_combine_kernel",
         "bound": "hbm",
         "achieved": round(gbps, 1),
         "peak": PEAK_HBM_GBPS,
         "unit": "GB/s",
         "frac": round(gbps / PEAK_HBM_GBPS, 4),
-        "bytes_per_launch": abytes,
-        "avg_launch_ms": round(ms, 5),
-        "tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+        "bytes_per_call": abytes,
+        "avg_call_ms": round(call_ms, 5),
+        "main_only": {"avg_launch_ms": round(ms, 5), "gbps": round(main_gbps, 1),
+                      "frac": round(main_gbps / PEAK_HBM_GBPS, 4)},
+        "tflops": round(flops / (call_ms * 1e-3) / 1e12, 2),
         "rotating_pools": len(layers),
         "seq_lens": [int(x) for x in plan.kv_lens],
     }
@@ -431,17 +580,33 @@ def cpu_baseline(geom, budget_s, min_s=10.0):
         if total >= budget_s or (done % len(pairs) == 0 and total >= min_s):
             break
     threads = os.cpu_count()
+    blas = None
     try:
         from threadpoolctl import threadpool_info
 
-        threads = max(int(i.get("num_threads", 0)) for i in threadpool_info()) or threads
+        info = threadpool_info()
+        threads = max(int(i.get("num_threads", 0)) for i in info) or threads
+        libs = [f"{i.get('internal_api')} {i.get('version')} ({i.get('threading_layer', '')})" for i in info
+                if i.get("user_api") == "blas"]
+        blas = ", ".join(libs) or None
     except Exception:
+        pass
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
         pass
     return {
         "value": flops / total / 1e12,
         "unit": "TFLOP/s",
         "cores": threads,
         "kind": "oracle",
+        "cpu_model": cpu_model,
+        "blas": blas,
         "sample": f"layer 0: oracle metadata and pool writes for all {geom.num_seqs} sequences, then attention "
                   f"for {done} (sequence, query head) pairs ({passes} full passes) in float64 numpy; "
                   f"{total:.1f} s wall",
@@ -464,6 +629,13 @@ def main():
     kvb = None if args.no_kv_bound else run_kv_bound(args)
     r = run_bench(args, geom)
     plan = r.pop("plan")
+    configs = {}
+    if not args.no_configs:
+        for name in OTHER_CONFIGS:
+            if name != geom.name:
+                print(f"[bench] config {name}", file=sys.stderr, flush=True)
+                configs[name] = run_config(CONFIGS[name], max(3, args.steps // 2), max(1, args.warmup // 2))
+    copies = None if args.no_hbm_copies else hbm_copies(geom)
     cpu = None if args.no_cpu_baseline else cpu_baseline(geom, args.cpu_budget_s)
     traffic = stored_traffic(geom.name)
     line = {
@@ -498,7 +670,7 @@ def main():
             "unit": "TFLOP/s",
             "frac": round(r["achieved_tflops"] / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
-            "kernel": "attn_mfma_kernel<bf16>",
+            "kernel": "attn_long_kernel (bf16)",
             "flop_per_launch": r["flops"],
             "avg_launch_ms": round(r["main_ms"], 5),
         },
@@ -517,6 +689,8 @@ def main():
             "attn_over_staged_buffer_ms": round(r["staged_attn_ms"], 5),
             "separate_calls_step_ms": round(r["separate_ms"], 5),
             "graph_replay_step_ms": round(r["graph_ms"], 5),
+            "hbm_copies": copies,
+            "configs": configs,
         },
         "cpu_baseline": cpu,
     }
