@@ -1,5 +1,7 @@
-// Paged attention on the gfx950 matrix cores: bf16 queries over bf16 or fp8
-// (OCP e4m3fn) K/V pools, head_dim 128.
+// Paged attention on the gfx950 matrix cores, head_dim 128: bf16 queries over
+// fp8 (OCP e4m3fn) K/V pools, and short query chunks (at most kShortRows rows
+// per KV head) over bf16 or fp8 pools.  Longer chunks over bf16 pools run in
+// attn_long.hip.
 //
 // Work decomposition
 //   A "row" is one (query token, query head) pair of a KV-head group; a
@@ -38,9 +40,7 @@
 //   QK for tile t + 1 next to the exponentials of tile t, then PV of tile t,
 //   while tile t + 3 streams into LDS (staged by waves 0..3 for all eight).
 //
-// Epilogue: O / l rounded to bf16.  The bf16 long kernel stages each wave's
-// 32 rows through LDS and stores whole 256-byte rows (four per instruction);
-// the other kernels store from the accumulator layout.
+// Epilogue: O / l rounded to bf16, stored from the accumulator layout.
 //
 // Split keys: with num_splits > 1 each workgroup writes a partial for its
 // key range to the workspace -- its normalised output O / l in bf16 and
@@ -99,6 +99,7 @@ static_assert(kTableSlice * 16 >= kMaxSplitKeys, "table slice must cover a split
 template <bool FP8, bool SHORT>
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(2, 2))) void
 attn_mfma_kernel(AttnArgs a) {
+  static_assert(FP8 || SHORT, "bf16 pools with long chunks run in attn_long_kernel");
   int32_t* tbl = s_tbl;
   constexpr int ELSZ = FP8 ? 1 : 2;
 
@@ -907,54 +908,10 @@ attn_mfma_kernel(AttnArgs a) {
   // ---- epilogue
   const float lt = SHORT ? lt_merged : sum_halves(l);
   const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
-  if constexpr (!SHORT && !FP8) {
-    // Lane (l32, h2) holds head-dim [32 db + 8 rq + 4 h2, +4) of row l32; a
-    // direct store would write 16 bytes of 32 rows per instruction.  The
-    // rows go through this wave's own 8 KB of the K tile buffers instead
-    // (idle: every wave passed the loop's last barrier, all tiles landed) and
-    // leave as whole 256-byte rows, four rows per store instruction.  LDS
-    // chunk c of row r sits at position c ^ (r mod 16).
-    const bool split = a.num_splits > 1;
-    const float inv = split ? 1.0f / lt : a.v_scale / lt;
-    uint8_t* const reg = &s_k[0][0] + w * (kWaveRows * kRowBytes);
-#pragma unroll
-    for (int db = 0; db < 4; ++db)
-#pragma unroll
-      for (int rq = 0; rq < 4; ++rq) {
-        u32x2 v;
-        v[0] = pack_bf16_rne(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
-        v[1] = pack_bf16_rne(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
-        *reinterpret_cast<u32x2*>(reg + l32 * kRowBytes + 16 * ((4 * db + rq) ^ (l32 & 15)) + 8 * h2) = v;
-      }
-    if (split && h2 == 0 && valid) {
-      const int64_t orow_id = static_cast<int64_t>(t0 + tok) * a.num_q_heads + head;
-      f32x2 ml = {m, lt};
-      *reinterpret_cast<f32x2*>(a.ws_ml + (static_cast<int64_t>(z) * total_rows + orow_id) * 2) = ml;
-    }
-    // Query token of row l32 (int32, as the start offsets are), -1 past the chunk.
-    const int tok_of_row = valid ? t0 + tok : -1;
-    __bf16* const dst = split ? reinterpret_cast<__bf16*>(a.ws_o) + static_cast<int64_t>(z) * total_rows * D
-                              : static_cast<__bf16*>(a.out);
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (lgkmcnt(0))
-    asm volatile("" ::: "memory");
-    const int c = lane & 15;
-#pragma unroll
-    for (int k = 0; k < 8; ++k) {
-      const int rr = 4 * k + (lane >> 4);
-      const u32x4 v = *reinterpret_cast<const u32x4*>(reg + rr * kRowBytes + 16 * (c ^ (rr & 15)));
-      const int tk = __shfl(tok_of_row, rr);
-      if (tk >= 0) {
-        const int hd = hk * G + (wr0 + rr - (tk - t0) * G);  // the row's query head
-        *reinterpret_cast<u32x4*>(dst + (static_cast<int64_t>(tk) * a.num_q_heads + hd) * D + 8 * c) = v;
-      }
-    }
-    return;
-  }
-  // (The fp8 long and the short-query kernels keep direct stores: staging
-  // the fp8 long kernel's rows the same way changed its loop's register
-  // allocation and cost 8% on long fp8 chunks, and the short-query kernels
-  // store only two waves' rows, where it measured no gain.)
+  // Direct stores from the accumulator layout.  (Staging the rows through
+  // LDS to store whole rows, as the bf16 long-chunk kernel does, changed the
+  // fp8 long kernel's loop register allocation and cost 8% on long fp8
+  // chunks; the short-query kernels store only two waves' rows.)
   if (!valid) return;
   const int64_t orow_id = static_cast<int64_t>(t0 + tok) * a.num_q_heads + head;
   if (a.num_splits > 1) {
@@ -1062,8 +1019,9 @@ hipError_t launch_attn_mfma(const AttnArgs& a, bool kv_fp8, bool short_rows, hip
     if (kv_fp8) hipLaunchKernelGGL((attn_mfma_kernel<true, true>), grid, dim3(NT), 0, s, a);
     else hipLaunchKernelGGL((attn_mfma_kernel<false, true>), grid, dim3(NT), 0, s, a);
   } else {
-    if (kv_fp8) hipLaunchKernelGGL((attn_mfma_kernel<true, false>), grid, dim3(NT), 0, s, a);
-    else hipLaunchKernelGGL((attn_mfma_kernel<false, false>), grid, dim3(NT), 0, s, a);
+    // (bf16 pools with long chunks run in attn_long_kernel)
+    if (!kv_fp8) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((attn_mfma_kernel<true, false>), grid, dim3(NT), 0, s, a);
   }
   return hipGetLastError();
 }

@@ -22,11 +22,6 @@ namespace pkv {
 
 namespace {
 thread_local char g_error[1024] = "";
-// (experiment switch: PKV_OLD_LONG=1 selects the two-waves-per-SIMD long kernel)
-bool getenv_flag_old() {
-  static const bool v = [] { const char* e = std::getenv("PKV_OLD_LONG"); return e && e[0] == '1'; }();
-  return v;
-}
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices] = {0};
@@ -434,8 +429,10 @@ int attn_launch(const AttnLaunch& L, unsigned phases, hipStream_t st) {
     return PKV_OK;
   }
   if (phases & kPhaseMain) {
-    const hipError_t e = (!L.fp8 && !L.p.short_rows && !getenv_flag_old()) ? launch_attn_long(L.a, st)
-                                                                          : launch_attn_mfma(L.a, L.fp8, L.p.short_rows, st);
+    // bf16 chunks of more than kShortRows rows per KV head: the one-wave-per-SIMD
+    // kernel; fp8 pools and short chunks: the two-waves-per-SIMD kernels.
+    const hipError_t e = (!L.fp8 && !L.p.short_rows) ? launch_attn_long(L.a, st)
+                                                      : launch_attn_mfma(L.a, L.fp8, L.p.short_rows, st);
     if (e != hipSuccess)
       return fail(PKV_EHIP, "attention launch failed: %s", hipGetErrorString(e));
   }
