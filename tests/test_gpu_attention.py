@@ -185,6 +185,58 @@ def test_ar_step_layers_sampled():
         del pools, out
 
 
+def test_ar_step_fused_call_all_heads_at_tile_edges():
+    """One layer of the 40-layer step through the fused per-layer call
+    (pkv_paged_write_attn: the current chunk's slot writes, then attention
+    and the merge of its key splits) at full size: every one of the 40 query
+    heads, on rows at each 256-row tile edge of both sequences (the last tile
+    holds the 24-row tail), the first and last rows, and random ones.  Every
+    row here sees all 9360 keys, so each one spans every key split."""
+    geom = CONFIGS["ar_step_40L_bf16"]
+    wl = make_workload(geom, device="cuda")
+    plan = G.make_plan(wl)
+    li = wl.layer(7)
+    pools = G.make_pools(geom, li)
+    G.P.pkv_paged_write(li.k_hist, li.v_hist, plan.history_slot_mapping, pools)
+    G.say("fused call", geom.name, "layer 7")
+    out = G.write_attend(plan, pools, li, geom)
+    torch.cuda.synchronize()
+    assert G.workspace_for(plan, geom) is not None  # the keys are split
+    qsl = np.concatenate([[0], np.cumsum(geom.query_lens)])
+    rng = np.random.default_rng(7)
+    rows = set()
+    for b in range(geom.num_seqs):
+        lo, hi = int(qsl[b]), int(qsl[b + 1])
+        for edge in range(0, hi - lo, 256):
+            rows |= {lo + max(edge - 1, 0), lo + edge}
+        rows |= {hi - 1} | set(rng.integers(lo, hi, size=4).tolist())
+    rows = sorted(rows)
+    _, _, _, ref = H.run_layer(wl, li=li, rows=rows)
+    _check(geom, out, ref, rows=rows)
+
+
+def test_varlen_fp8_a_row_block_of_every_sequence():
+    """The whole varlen fp8 batch (16 sequences, 2k..32k keys, chunks of 16
+    and 1560 queries, causal): for every sequence, the rows of one workgroup
+    -- 64 consecutive query tokens (all of a 16-token chunk) times the 4 query
+    heads of a KV head -- for the first and the last KV head."""
+    geom = CONFIGS["varlen_fp8"]
+    wl = make_workload(geom, device="cuda")
+    li = wl.layer(0)
+    G.say("attn full", geom.name, "row block per sequence")
+    _, _, _, out = G.run(wl, li=li)
+    qsl = np.concatenate([[0], np.cumsum(geom.query_lens)])
+    rng = np.random.default_rng(5)
+    rows = []
+    for b in range(geom.num_seqs):
+        lo, hi = int(qsl[b]), int(qsl[b + 1])
+        start = lo if hi - lo <= 64 else lo + 64 * int(rng.integers(0, (hi - lo) // 64))
+        rows.extend(range(start, min(start + 64, hi)))
+    heads = [0, 1, 2, 3, 28, 29, 30, 31]
+    _, _, _, ref = H.run_layer(wl, li=li, rows=rows, heads=heads)
+    _check(geom, out, ref, rows=rows, heads=heads)
+
+
 def test_bad_arguments_raise_before_launch():
     geom = SMALL[2]
     wl = make_workload(geom, device="cuda")
