@@ -88,10 +88,10 @@ def kernel_source_hash() -> str:
     return h.hexdigest()
 
 
-def stored_traffic(workload: str):
+def stored_traffic(workload: str, kernel: str = "attn_long"):
     """HBM bytes per attention launch from the committed counter summary, or
     None when there is none or it was taken on other kernel sources."""
-    path = os.path.join(ROOT, "profiles", f"attn_long_{workload}_traffic.txt")
+    path = os.path.join(ROOT, "profiles", f"{kernel}_{workload}_traffic.txt")
     if not os.path.exists(path):
         return None
     kv = {}
@@ -543,6 +543,7 @@ def run_kv_bound(args):
         "tflops": round(flops / (call_ms * 1e-3) / 1e12, 2),
         "rotating_pools": len(layers),
         "seq_lens": [int(x) for x in plan.kv_lens],
+        "traffic_main": stored_traffic(geom.name, "attn_mfma"),
     }
 
 
