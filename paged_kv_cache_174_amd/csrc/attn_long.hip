@@ -15,28 +15,33 @@
 //   work of a second wave on the same SIMD slows an MFMA stream by about half.
 //   So the softmax of one half runs inside the instruction stream that feeds
 //   the other half's MFMAs.  Per 64-key tile t a wave runs two phases:
-//     alpha(t): softmax of A(t)  beside  QK of B(t) and PV of B(t - 1)
-//     beta(t):  softmax of B(t)  beside  QK of A(t + 1) and PV of A(t)
-//   32 MFMAs per phase; the K and V operand reads of a tile feed both halves.
+//     alpha(u): softmax of A(u)  beside  QK of B(u) and PV of B(u - 1)
+//     beta(u):  softmax of B(u)  beside  QK of A(u + 1) and PV of A(u)
+//   over 32-key sub-tiles u, 18 MFMAs per phase (8 QK, 8 PV, 2 row sums);
+//   the K and V operand reads of a sub-tile feed both halves.
 //
 // Softmax without a per-tile maximum
-//   Probabilities are exp2(s * c - m * c) with the row's running maximum m,
-//   which only moves on a slow path: the wave's first tile takes the exact
-//   maximum, and a later tile whose probabilities sum past 2^32 in some lane
-//   (its scores exceed m by more than 32 / c) recomputes its scores from LDS,
-//   takes their maximum and rescales O and l.  Softmax is exact for any common
-//   offset, so a stale m changes nothing but rounding; it only lets
-//   probabilities grow up to 2^32, far inside fp32 and bf16 range.
+//   Probabilities are exp2(s * c - m * c) with a running maximum m that is
+//   fixed after each half's first 32 keys (their exact maximum): softmax is
+//   exact for any common offset, so a stale m changes nothing but rounding,
+//   and O and l are never rescaled in the loop.  Row sums are taken on the
+//   matrix cores (ones x P^T), i.e. of the bf16-rounded probabilities that
+//   multiply V.  If a row's sum passes kFastSumLimit (2^64) or is not finite --
+//   some later score rose more than 64 / c above the first keys' maximum --
+//   the workgroup recomputes its key range exactly, tile by tile, with the
+//   maximum moving per sub-tile and O and l rescaled.
 //
 // K/V tiles (64 keys) in LDS
 //   Row-major bf16, one 256-byte row per key, 16-byte chunks XOR-permuted
 //   (k_swz / v_swz) so the MFMA operand reads are free of bank conflicts.
 //   Wave w copies the tile's 16-key block w straight from HBM into LDS
-//   (global_load_lds_dwordx4, four rows per load) through the block-table
-//   slice staged in LDS once per workgroup; keys at or past the staged range
-//   read a row of zeros.  Four tile buffers: tile t + 3's K loads go out in
-//   beta(t) and its V loads in alpha(t + 1), into the buffer tile t - 1 left.
-//   One barrier per tile, between the phases.
+//   (buffer_load_dwordx4 ... lds, four rows per load) through the block-table
+//   slice staged in LDS once per workgroup; the buffer descriptor's range
+//   ends at the key limit, so keys past it arrive as zeros.  Four tile
+//   buffers: the four phases after tile X - 3's barrier issue the wave's
+//   eight loads of tile X (K rows 0-7, K 8-15, V 0-7, V 8-15 of its block),
+//   into the buffer tile X - 4 left.  One barrier per tile, before the phase
+//   that first reads the next tile.
 //
 // Epilogue: O / l rounded to bf16, staged through LDS and stored as whole
 // 256-byte rows; with split keys the partial (O / l in bf16, (max, sum) in

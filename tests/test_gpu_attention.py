@@ -237,6 +237,27 @@ def test_varlen_fp8_a_row_block_of_every_sequence():
     _check(geom, out, ref, rows=rows, heads=heads)
 
 
+@pytest.mark.parametrize("gain", [30.0, 8.0])
+def test_scores_far_above_the_first_subtile(gain):
+    """The long-chunk kernel fixes each row's running max after its first
+    32 keys and reruns a workgroup exactly (max moving per sub-tile) when a
+    row's probability sum passes 2^64 or is not finite.  Keys from position
+    500 on are scaled up: with gain 30 their scores (log2 units, std ~40)
+    overflow against the first keys' max and force the rerun; with gain 8
+    (std ~11) the fast path absorbs them.  Both must match the oracle."""
+    geom = small_variant(CONFIGS["frame_bf16"], name=f"rising_scores_{int(gain)}", num_q_heads=2, num_kv_heads=2,
+                         history_lens=(1000,), query_lens=(300,), sink_tokens=(0,), window_tokens=(1 << 30,),
+                         full_spans=(None,))
+    wl = make_workload(geom, device="cuda")
+    li = wl.layer(0)
+    li.k_hist = li.k_hist.clone()
+    li.k_hist[500:] = (li.k_hist[500:].float() * gain).to(li.k_hist.dtype)
+    G.say("rising scores", gain)
+    _, _, _, out = G.run(wl, li=li)
+    _, _, _, ref = H.run_layer(wl, li=li)
+    _check(geom, out, ref)
+
+
 def test_bad_arguments_raise_before_launch():
     geom = SMALL[2]
     wl = make_workload(geom, device="cuda")
