@@ -65,7 +65,7 @@ typedef struct {
   int64_t num_blocks;
   int32_t block_size;   /* 16: the kernels page K/V in 16-token blocks (P1 supported_kernel_block_sizes) */
   int32_t num_kv_heads;
-  int32_t head_dim;     /* 128 for bf16/fp8 pools; 64 or 128 for f32 pools */
+  int32_t head_dim;     /* 64 or 128 (64 runs through the 128-wide kernels with the upper half zero) */
   int32_t dtype;        /* pkv_dtype of the pools */
   float k_scale;        /* dequantisation multipliers: stored value * scale = real value (1 unless FP8) */
   float v_scale;

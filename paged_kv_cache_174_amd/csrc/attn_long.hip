@@ -166,15 +166,18 @@ attn_long_kernel(AttnArgs a) {
   }
 
   // Q^T fragments for S^T = K Q^T: for k-step t the lane holds head-dim
-  // [16 t + 8 h2, +8) of its row.
+  // [16 t + 8 h2, +8) of its row.  head_dim 64 runs through the same 128-wide
+  // kernel with head-dim [64, 128) of Q, K and V zero: it adds nothing to a
+  // score, and the output's upper half is never stored.
+  const int dh = a.head_dim;  // 64 or 128
   bf16x8 qf[2][8];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
-    const __bf16* qr = static_cast<const __bf16*>(a.q) + (static_cast<int64_t>(t0 + tok[h]) * a.num_q_heads + head[h]) * D;
+    const __bf16* qr = static_cast<const __bf16*>(a.q) + (static_cast<int64_t>(t0 + tok[h]) * a.num_q_heads + head[h]) * dh;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (valid[h]) v = *reinterpret_cast<const u32x4*>(qr + 16 * t + 8 * h2);
+      if (valid[h] && 16 * t + 8 * h2 < dh) v = *reinterpret_cast<const u32x4*>(qr + 16 * t + 8 * h2);
       qf[h][t] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -202,18 +205,22 @@ attn_long_kernel(AttnArgs a) {
 
   // ---- staging geometry: wave w copies block w of each tile, rows
   // 16 w + 4 st + lane / 16 (st = 0..3), chunk position lane % 16.
-  const int64_t row_bytes = static_cast<int64_t>(a.num_kv_heads) * D * 2;
+  const int64_t row_bytes = static_cast<int64_t>(a.num_kv_heads) * dh * 2;
   const int64_t block_bytes = 16 * row_bytes;
-  const uint8_t* kpool = static_cast<const uint8_t*>(a.kpool) + static_cast<int64_t>(hk) * D * 2;
-  const uint8_t* vpool = static_cast<const uint8_t*>(a.vpool) + static_cast<int64_t>(hk) * D * 2;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.kpool) + static_cast<int64_t>(hk) * dh * 2;
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.vpool) + static_cast<int64_t>(hk) * dh * 2;
   const int st_pos = lane & 15;
   const int st_sub = lane >> 4;
+  // A chunk past head_dim gets an offset past every descriptor's range (at
+  // most 16 rows of a few KB): it arrives as zeros.
+  constexpr uint32_t kPastRange = 0x40000000u;
   uint32_t k_src_off[4], v_src_off[4];
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
     const int rb = 4 * st + st_sub;  // row inside the block (= tile row - 16 w)
-    k_src_off[st] = static_cast<uint32_t>(rb * row_bytes + 16 * (st_pos ^ k_swz(rb)));
-    v_src_off[st] = static_cast<uint32_t>(rb * row_bytes + 16 * (st_pos ^ v_swz(rb)));
+    const int kc = st_pos ^ k_swz(rb), vc = st_pos ^ v_swz(rb);  // source chunks
+    k_src_off[st] = 16 * kc < 2 * dh ? static_cast<uint32_t>(rb * row_bytes + 16 * kc) : kPastRange;
+    v_src_off[st] = 16 * vc < 2 * dh ? static_cast<uint32_t>(rb * row_bytes + 16 * vc) : kPastRange;
   }
   // Direct loads through a buffer descriptor whose range ends at the last
   // key below kv_lim in this wave's block: rows past it are out of range and
@@ -688,8 +695,10 @@ attn_long_kernel(AttnArgs a) {
     // Query token of the row (int32, as the start offsets are), -1 past the chunk.
     tok_of_row[h] = valid[h] ? t0 + tok[h] : -1;
   }
+  // (Partials keep 128-wide rows, the merge's layout; the output has head_dim.)
   __bf16* const dst = split ? reinterpret_cast<__bf16*>(a.ws_o) + static_cast<int64_t>(z) * total_rows * D
                             : static_cast<__bf16*>(a.out);
+  const int dst_row = split ? D : dh;
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (lgkmcnt(0))
   asm volatile("" ::: "memory");
@@ -700,9 +709,9 @@ attn_long_kernel(AttnArgs a) {
     const int rr = 4 * k + (lane >> 4);  // row of the wave, 0..63
     const u32x4 v = *reinterpret_cast<const u32x4*>(reg + rr * kRowBytes + 16 * (c ^ (rr & 15)));
     const int tk = __shfl(tok_of_row[k >> 3], rr & 31);  // rows 0..31 are half A, 32..63 half B
-    if (tk >= 0) {
+    if (tk >= 0 && 8 * c < dst_row) {
       const int hd = hk * G + (wr0 + rr - (tk - t0) * G);  // the row's query head
-      *reinterpret_cast<u32x4*>(dst + (static_cast<int64_t>(tk) * a.num_q_heads + hd) * D + 8 * c) = v;
+      *reinterpret_cast<u32x4*>(dst + (static_cast<int64_t>(tk) * a.num_q_heads + hd) * dst_row + 8 * c) = v;
     }
   }
 }

@@ -216,15 +216,19 @@ attn_mfma_kernel(AttnArgs a) {
   // (fp8 pools: step t takes head-dim piece 4 (t / 2) + 2 h2 + t % 2 of 8
   // values instead, so that one 16-byte LDS read of K feeds two steps.)
   constexpr bool kF8Lds = FP8;  // fp8 K/V tiles are kept as fp8 in LDS
+  // head_dim 64 runs through the same 128-wide kernel with head-dim
+  // [64, 128) of Q, K and V zero: it adds nothing to a score, and the
+  // output's upper half is never stored.
+  const int dh = a.head_dim;  // 64 or 128
   bf16x8 qf[8];
   {
     const __bf16* qr = static_cast<const __bf16*>(a.q) +
-                       (static_cast<int64_t>(t0 + tok) * a.num_q_heads + head) * D;
+                       (static_cast<int64_t>(t0 + tok) * a.num_q_heads + head) * dh;
 #pragma unroll
     for (int t = 0; t < 8; ++t) {
       const int piece = kF8Lds ? 4 * (t >> 1) + 2 * h2 + (t & 1) : 2 * t + h2;
       u32x4 v = {0u, 0u, 0u, 0u};
-      if (valid) v = *reinterpret_cast<const u32x4*>(qr + 8 * piece);
+      if (valid && 8 * piece < dh) v = *reinterpret_cast<const u32x4*>(qr + 8 * piece);
       qf[t] = __builtin_bit_cast(bf16x8, v);
     }
   }
@@ -252,10 +256,13 @@ attn_mfma_kernel(AttnArgs a) {
   // ---- staging geometry (bf16): wave w stages tile rows [8 w, 8 w + 8) of
   // both the K and the V tile, four rows (one 1 KB direct load) per step; lane
   // i takes row 8 w + 4 step + i / 16 and LDS chunk position i % 16.
-  const int64_t row_bytes = static_cast<int64_t>(a.num_kv_heads) * D * ELSZ;
+  const int64_t row_bytes = static_cast<int64_t>(a.num_kv_heads) * dh * ELSZ;
   const int64_t block_bytes = 16 * row_bytes;
-  const uint8_t* kpool = static_cast<const uint8_t*>(a.kpool) + static_cast<int64_t>(hk) * D * ELSZ;
-  const uint8_t* vpool = static_cast<const uint8_t*>(a.vpool) + static_cast<int64_t>(hk) * D * ELSZ;
+  const uint8_t* kpool = static_cast<const uint8_t*>(a.kpool) + static_cast<int64_t>(hk) * dh * ELSZ;
+  const uint8_t* vpool = static_cast<const uint8_t*>(a.vpool) + static_cast<int64_t>(hk) * dh * ELSZ;
+  // Whether a 16-byte source chunk lies inside head_dim (chunks past it read zeros).
+  const bool full_d = dh == D;
+  auto in_d = [&](int chunk) { return 16 * chunk < dh * ELSZ; };
   const int st_pos = lane & 15;
   int st_row[2], k_src_off[2], v_src_off[2];
 #pragma unroll
@@ -273,31 +280,6 @@ attn_mfma_kernel(AttnArgs a) {
     const int blk = (kt >> 4) + (ws >> 1);
     return (blk < blk_hi) ? tbl[blk - blk_lo] : 0;
   };
-  // bf16: direct loads of the tile at key kt into LDS buffer buf.
-  // Rows 8 ws .. 8 ws + 7 of the K and V tiles (ws = w, or w + 4 when waves
-  // 0..3 stage for all eight: the rows of wave w + 4 sit 32 rows, two blocks,
-  // further on, at the same offsets inside their block).
-  auto stage_load = [&](int kt, auto bufc, int e, int ws) {
-    constexpr int B = decltype(bufc)::value;
-    // The eight rows lie in one 16-key block: its base address is
-    // wave-uniform and lives in SGPRs.
-    const int64_t boff = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(e)) * block_bytes;
-    const uint8_t* kb = kpool + boff;
-    const uint8_t* vb = vpool + boff;
-#pragma unroll
-    for (int st = 0; st < 2; ++st) {
-      const int dst = (8 * ws + 4 * st) * kRowBytes;
-      if (kt + 8 * ws + 4 * st + 4 <= kv_lim) {  // all four rows exist (uniform)
-        dma16(kb, static_cast<uint32_t>(k_src_off[st]), kbuf<B>() + dst);
-        dma16(vb, static_cast<uint32_t>(v_src_off[st]), vbuf<B>() + dst);
-      } else {  // the tile at the end of the staged keys: rows past kv_lim read zeros
-        const bool ok = kt + st_row[st] + 8 * (ws - w) < kv_lim;
-        dma16(ok ? kb + k_src_off[st] : zero_row, kbuf<B>() + dst);
-        dma16(ok ? vb + v_src_off[st] : zero_row, vbuf<B>() + dst);
-      }
-    }
-  };
-
   // ---- MFMA operand addresses (bytes, without the buffer offset)
   // (buffer 0, or the key group's own buffer for SHORT)
   uint32_t k_rd[8];  // LDS address of K row 32 kb + l32, chunk 2 t + h2
@@ -474,13 +456,14 @@ attn_mfma_kernel(AttnArgs a) {
     const int64_t boff = static_cast<int64_t>(__builtin_amdgcn_readfirstlane(e)) * block_bytes;
     uint8_t* kdst = f8k_base + buf * kF8Tile + 8 * ws * D;
     uint8_t* vdst = f8v_base + buf * kF8Tile + 8 * ws * D;
-    if (kt + 8 * ws + 8 <= kv_lim) {  // all eight rows exist (uniform)
+    if (full_d && kt + 8 * ws + 8 <= kv_lim) {  // all eight rows exist (uniform)
       dma16(kpool + boff, dl_k, kdst);
       dma16(vpool + boff, dl_v, vdst);
     } else {
       const bool ok = kt + dl_row + 8 * (ws - w) < kv_lim;
-      dma16(ok ? kpool + boff + dl_k : f8_zero, kdst);
-      dma16(ok ? vpool + boff + dl_v : f8_zero, vdst);
+      const bool kok = ok && in_d(dl_pos ^ f8_swz_k(dl_row)), vok = ok && in_d(dl_pos ^ f8_swz_v(dl_row));
+      dma16(kok ? kpool + boff + dl_k : f8_zero, kdst);
+      dma16(vok ? vpool + boff + dl_v : f8_zero, vdst);
     }
   };
   auto qk8 = [&](int buf, f32x16 (&sacc)[2]) {
@@ -552,13 +535,15 @@ attn_mfma_kernel(AttnArgs a) {
       uint8_t* vdst = f8v_base + (4 * set + kgs) * kTile32 + 16 * ld_part * D;
 #pragma unroll
       for (int sub = 0; sub < 2; ++sub) {
-        if (row0 + 8 * sub + 8 <= kv_lim) {  // all eight rows exist (uniform)
+        if (full_d && row0 + 8 * sub + 8 <= kv_lim) {  // all eight rows exist (uniform)
           dma16(kpool + boff, ld_k[sub], kdst + 8 * sub * D);
           dma16(vpool + boff, ld_v[sub], vdst + 8 * sub * D);
-        } else {  // rows past kv_lim read zeros
+        } else {  // rows past kv_lim, and chunks past head_dim, read zeros
+          const int r = 16 * ld_part + 8 * sub + ld_r8;
           const bool ok = row0 + 8 * sub + ld_r8 < kv_lim;
-          dma16(ok ? kpool + boff + ld_k[sub] : f8_zero, kdst + 8 * sub * D);
-          dma16(ok ? vpool + boff + ld_v[sub] : f8_zero, vdst + 8 * sub * D);
+          const bool kok = ok && in_d(dl_pos ^ f8_swz_k(r)), vok = ok && in_d(dl_pos ^ f8_swz_v(r));
+          dma16(kok ? kpool + boff + ld_k[sub] : f8_zero, kdst + 8 * sub * D);
+          dma16(vok ? vpool + boff + ld_v[sub] : f8_zero, vdst + 8 * sub * D);
         }
       }
     };
@@ -667,7 +652,7 @@ attn_mfma_kernel(AttnArgs a) {
     // ---- bf16 short path: each wave multiplies tile 4 i + kg from buffer kg
     // while the workgroup loads tiles 4 i + 4 .. 4 i + 7 into registers (lane
     // i of wave w: chunk i % 16 of rows 8 w + 4 st + i / 16, at the positions
-    // stage_load uses); after a barrier they are written into buffers 0..3.
+    // k_src_off / v_src_off name); after a barrier they are written into buffers 0..3.
     u32x4 rk[4][2], rv[4][2];
     auto load4 = [&](int t_first) {
       // All four block-table entries first: one LDS round trip, not four.
@@ -684,8 +669,9 @@ attn_mfma_kernel(AttnArgs a) {
 #pragma unroll
         for (int st = 0; st < 2; ++st) {
           const bool ok = kt + st_row[st] < kv_lim;
-          rk[j][st] = ok ? *reinterpret_cast<const u32x4*>(kpool + boff + k_src_off[st]) : zero;
-          rv[j][st] = ok ? *reinterpret_cast<const u32x4*>(vpool + boff + v_src_off[st]) : zero;
+          const bool kok = ok && in_d(st_pos ^ k_swz(st_row[st])), vok = ok && in_d(st_pos ^ v_swz(st_row[st]));
+          rk[j][st] = kok ? *reinterpret_cast<const u32x4*>(kpool + boff + k_src_off[st]) : zero;
+          rv[j][st] = vok ? *reinterpret_cast<const u32x4*>(vpool + boff + v_src_off[st]) : zero;
         }
       }
     };
@@ -776,79 +762,6 @@ attn_mfma_kernel(AttnArgs a) {
       if (t + 6 < ntiles) iteration(Buf<6>{}, t + 6, sA, sB);
       if (t + 7 < ntiles) iteration(Buf<7>{}, t + 7, sB, sA);
     }
-  } else {
-    // ---- bf16 long chunks: software pipeline over tiles t = 0 .. n-1 (tile
-    // t: keys k_begin + 64 t, LDS buffer t % 4).  Iteration t: mask / max of
-    // S(t); S(t+1) = K(t+1) Q^T next to the exponentials of S(t);
-    // O += V(t) P(t); then waves 0..3 stage tile t + 3 into buffer
-    // (t + 3) % 4, which held tile t - 1, last read in iteration t - 1.  The
-    // barrier closing iteration t follows their wait for tile t + 2 (staged in
-    // iteration t - 1), which iteration t + 1 reads.  Waves 0..3 stage all
-    // eight waves' rows: they run ahead of their SIMD partners (older waves
-    // issue first) and would otherwise wait for them at the barrier, while a
-    // direct load stalls the wave that issues it for as long as the CU's
-    // earlier loads are queued.  S(t + 1) of the last tile reads a stale
-    // buffer and is never used.
-    const bool stager = w < 4;
-    auto stage_tile = [&](int t, auto bufc) {
-      stage_load(kt_of(t), bufc, stage_entry(kt_of(t), w), w);
-      stage_load(kt_of(t), bufc, stage_entry(kt_of(t), w + 4), w + 4);
-    };
-    if (stager) {
-      stage_tile(0, Buf<0>{});
-      if (ntiles > 1) stage_tile(1, Buf<1>{});
-      if (ntiles > 2) {
-        stage_tile(2, Buf<2>{});
-        wait_vmcnt<8>();
-      } else {
-        wait_vmcnt<0>();
-      }
-    }
-    lds_barrier();
-    f32x16 sA[2], sB[2];
-    qk(Buf<0>{}, sA);
-
-    // Waves 4..7 start an iteration with QK(t+1) and then take the mask and
-    // maximum of S(t), so their MFMAs run while waves 0..3 compute theirs;
-    // the two orders are two loops, each straight-line code for the
-    // register allocator.
-    auto iteration = [&](auto bufc, int t, f32x16 (&s_cur)[2], f32x16 (&s_next)[2], auto late_c)
-                         __attribute__((always_inline)) {
-      constexpr int B = decltype(bufc)::value;
-      constexpr bool late = decltype(late_c)::value;
-      const int kt = kt_of(t);
-      if (kt < wave_kmax) {
-        bf16x8 pb[2][2];
-        if constexpr (late) {
-          qk(Buf<(B + 1) % kBufs>{}, s_next);
-          mask_and_rescale(kt, s_cur);
-        } else {
-          mask_and_rescale(kt, s_cur);
-          qk(Buf<(B + 1) % kBufs>{}, s_next);
-        }
-        probs(s_cur, pb);
-        pv(bufc, pb);
-      }
-      if constexpr (!late) {
-        if (t + 3 < ntiles) {
-          stage_tile(t + 3, Buf<(B + 3) % kBufs>{});
-          wait_vmcnt<8>();
-        } else {
-          wait_vmcnt<0>();
-        }
-      }
-      lds_barrier();
-    };
-    auto loop = [&](auto late_c) __attribute__((always_inline)) {
-      for (int t = 0; t < ntiles; t += kBufs) {
-        iteration(Buf<0>{}, t, sA, sB, late_c);
-        if (t + 1 < ntiles) iteration(Buf<1>{}, t + 1, sB, sA, late_c);
-        if (t + 2 < ntiles) iteration(Buf<2>{}, t + 2, sA, sB, late_c);
-        if (t + 3 < ntiles) iteration(Buf<3>{}, t + 3, sB, sA, late_c);
-      }
-    };
-    if (stager) loop(std::false_type{});
-    else loop(std::true_type{});
   }
 
   if constexpr (SHORT) {
@@ -935,7 +848,7 @@ attn_mfma_kernel(AttnArgs a) {
     }
   } else {
     const float inv = a.v_scale / lt;
-    __bf16* orow = static_cast<__bf16*>(a.out) + orow_id * D;
+    __bf16* orow = static_cast<__bf16*>(a.out) + orow_id * dh;
 #pragma unroll
     for (int db = 0; db < 4; ++db)
 #pragma unroll
@@ -943,7 +856,7 @@ attn_mfma_kernel(AttnArgs a) {
         u32x2 v;
         v[0] = pack_bf16_rne(o[db][4 * rq] * inv, o[db][4 * rq + 1] * inv);
         v[1] = pack_bf16_rne(o[db][4 * rq + 2] * inv, o[db][4 * rq + 3] * inv);
-        *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * rq + 4 * h2) = v;
+        if (32 * db + 8 * rq + 4 * h2 < dh) *reinterpret_cast<u32x2*>(orow + 32 * db + 8 * rq + 4 * h2) = v;
       }
   }
 }
@@ -1001,7 +914,7 @@ __global__ __launch_bounds__(256) void attn_combine_kernel(AttnArgs a) {
   u32x4 packed;
 #pragma unroll
   for (int e = 0; e < 4; ++e) packed[e] = pack_bf16_rne(num[2 * e] * inv, num[2 * e + 1] * inv);
-  *reinterpret_cast<u32x4*>(static_cast<__bf16*>(a.out) + row * D + 8 * sub) = packed;
+  if (8 * sub < a.head_dim) *reinterpret_cast<u32x4*>(static_cast<__bf16*>(a.out) + row * a.head_dim + 8 * sub) = packed;
 }
 
 }  // namespace

@@ -297,7 +297,8 @@ int pkv_gather(const pkv_pools* pools, const int32_t* block_ids, int32_t n_block
 size_t pkv_paged_attn_workspace_size(int64_t num_q_tokens, int32_t num_q_heads, int32_t num_kv_heads,
                                      int32_t head_dim, int32_t num_seqs, int32_t max_query_len,
                                      int32_t max_seq_len) {
-  if (num_q_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads || head_dim != 128 ||
+  if (num_q_tokens <= 0 || num_q_heads <= 0 || num_kv_heads <= 0 || num_q_heads % num_kv_heads ||
+      (head_dim != 64 && head_dim != 128) ||
       num_seqs <= 0 || max_query_len <= 0 || max_seq_len <= 0)
     return 0;
   SplitPlan p = plan_splits(num_q_tokens, num_q_heads, num_kv_heads, num_seqs, max_query_len, max_seq_len,
@@ -393,8 +394,8 @@ int attn_setup(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num
     L.p = SplitPlan{0, 1, 0, false};
     return PKV_OK;
   }
-  if (pools->head_dim != 128)
-    return fail(PKV_EUNSUPPORTED, "bf16/fp8 attention supports head_dim 128, not %d", pools->head_dim);
+  if (pools->head_dim != 64 && pools->head_dim != 128)
+    return fail(PKV_EUNSUPPORTED, "bf16/fp8 attention supports head_dim 64 and 128, not %d", pools->head_dim);
   const SplitPlan p = plan_splits(num_q_tokens, num_q_heads, pools->num_kv_heads, num_seqs, max_query_len,
                                   max_seq_len, workspace_bytes, workspace != nullptr, host_lens,
                                   pools->dtype == PKV_FP8_E4M3 ? 1 : 2);

@@ -77,6 +77,20 @@ SMALL = [
                   history_lens=(1000, 37), query_lens=(32, 7), sink_tokens=(300, 0), window_tokens=(600, 1 << 30)),
     small_variant(CONFIGS["piecewise_gqa_bf16"], name="short_piecewise_bf16", num_q_heads=2, num_kv_heads=2,
                   history_lens=(200,), query_lens=(60,), full_spans=(((210, 240),),)),
+    # head_dim 64 (P2's geometry: 4 heads, D 64, 16-token blocks) on each MFMA kernel:
+    # bf16 long chunks, bf16 short chunks, fp8 long and short chunks, piecewise GQA.
+    small_variant(CONFIGS["frame_bf16"], name="d64_bf16_long", head_dim=64, num_q_heads=4, num_kv_heads=4,
+                  history_lens=(3000, 37), query_lens=(300, 90), sink_tokens=(0, 0), window_tokens=(1 << 30,) * 2),
+    small_variant(CONFIGS["frame_bf16"], name="d64_bf16_short", head_dim=64, num_q_heads=4, num_kv_heads=4,
+                  history_lens=(2000, 32), query_lens=(16, 16), sink_tokens=(0, 0), window_tokens=(1 << 30,) * 2),
+    small_variant(CONFIGS["varlen_fp8"], name="d64_fp8_long", head_dim=64, num_q_heads=8, num_kv_heads=2,
+                  history_lens=(900, 5), query_lens=(200, 70), sink_tokens=(0,) * 2,
+                  window_tokens=(1 << 30,) * 2, full_spans=(None,) * 2),
+    small_variant(CONFIGS["varlen_fp8"], name="d64_fp8_short", head_dim=64, num_q_heads=8, num_kv_heads=2,
+                  history_lens=(3000, 40), query_lens=(16, 16), sink_tokens=(0,) * 2,
+                  window_tokens=(1 << 30,) * 2, full_spans=(None,) * 2),
+    small_variant(CONFIGS["piecewise_gqa_bf16"], name="d64_piecewise_gqa", head_dim=64, num_q_heads=8,
+                  num_kv_heads=2, history_lens=(100,), query_lens=(300,), full_spans=(((100, 180), (250, 400)),)),
     small_variant(CONFIGS["piecewise_gqa_bf16"], name="causal_hist_split_bf16", num_q_heads=4, num_kv_heads=2,
                   history_lens=(3000, 100), query_lens=(600, 700), full_spans=((), ((100, 500),)), sink_tokens=(0, 0), window_tokens=(1 << 30,) * 2),
 ]
