@@ -377,6 +377,8 @@ attn_long_kernel(AttnArgs a) {
   bf16x8 ones;
 #pragma unroll
   for (int i = 0; i < 8; ++i) ones[i] = static_cast<__bf16>(1.0f);
+  // (opaque from here on: kept in registers rather than rebuilt in every phase)
+  asm volatile("" : "+v"(ones));
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
@@ -554,22 +556,27 @@ attn_long_kernel(AttnArgs a) {
   // boff_load: block offset of this wave's loads of tile t + 2 (looked up
   // in the previous tile); the lookup for tile t + 3 goes before the barrier.
   int64_t boff_load = boff_next;
-  auto tile = [&](auto tc, int t) __attribute__((always_inline)) {
+  // (Two copies of the loop, one for waves with rows and one for waves
+  // without, so that no phase sits behind a branch; the mask checks are
+  // expected false, which keeps the unmasked path straight-line.)
+  auto tile = [&](auto tc, int t, auto act_c) __attribute__((always_inline)) {
     constexpr int T = decltype(tc)::value;
+    constexpr bool ACT = decltype(act_c)::value;
     constexpr int Tp1 = (T + 1) % kBufs, Tp2 = (T + 2) % kBufs, Tp3 = (T + 3) % kBufs;
     const int kt = kt_of(t);
     const bool edge = kt + kTileKeys > wave_kmin;  // some row of the wave masks keys of this tile
-    if (active) {
+    if constexpr (ACT) {
       // alpha(2t): QK B(2t), PV B(2t-1) [vfr 1]; reads V(2t) [T, 0] into vfr 0; K rows 2-3 of tile t+2
-      if (edge) mask(0, kt);
+      if (__builtin_expect(edge, 0)) mask(0, kt);
       phase(Alpha{}, Buf<T>{}, I0{}, I1{}, Soft{}, I1{}, I2{}, Buf<Tp2>{}, t + 2, boff_load);
       // beta(2t): PV A(2t) [vfr 0], QK A(2t+1) (reads K(2t+1) [T, 1]); V rows 0-1 of tile t+2
-      if (edge) mask(1, kt);
+      if (__builtin_expect(edge, 0)) mask(1, kt);
       phase(Beta{}, Buf<T>{}, I1{}, I0{}, Soft{}, I2{}, I0{}, Buf<Tp2>{}, t + 2, boff_load);
       // alpha(2t+1): QK B(2t+1), PV B(2t) [vfr 0]; reads V(2t+1) [T, 1] into vfr 1; V rows 2-3 of tile t+2
-      if (edge) mask(0, kt + 32);
+      if (__builtin_expect(edge, 0)) mask(0, kt + 32);
       phase(Alpha{}, Buf<T>{}, I1{}, I0{}, Soft{}, I2{}, I2{}, Buf<Tp2>{}, t + 2, boff_load);
     } else {
+      (void)edge;
       idle_loads(I1{}, I2{}, Buf<Tp2>{}, t + 2, boff_load);
       idle_loads(I2{}, I0{}, Buf<Tp2>{}, t + 2, boff_load);
       idle_loads(I2{}, I2{}, Buf<Tp2>{}, t + 2, boff_load);
@@ -578,20 +585,24 @@ attn_long_kernel(AttnArgs a) {
     wait_vmcnt<8>();  // tile t + 1 landed (tile t + 2's eight loads may be in flight)
     lds_barrier();
     boff_load = entry_base(e_next);
-    if (active) {
+    if constexpr (ACT) {
       // beta(2t+1): PV A(2t+1) [vfr 1], QK A(2t+2) (reads K(2t+2) [T+1, 0]); K rows 0-1 of tile t+3
-      if (edge) mask(1, kt + 32);
+      if (__builtin_expect(edge, 0)) mask(1, kt + 32);
       phase(Beta{}, Buf<Tp1>{}, I0{}, I1{}, Soft{}, I1{}, I0{}, Buf<Tp3>{}, t + 3, boff_load);
     } else {
       idle_loads(I1{}, I0{}, Buf<Tp3>{}, t + 3, boff_load);
     }
   };
-  for (int t = 1; t < ntiles; t += 4) {
-    tile(Buf<1>{}, t);
-    if (t + 1 < ntiles) tile(Buf<2>{}, t + 1);
-    if (t + 2 < ntiles) tile(Buf<3>{}, t + 2);
-    if (t + 3 < ntiles) tile(Buf<0>{}, t + 3);
-  }
+  auto loop = [&](auto act_c) __attribute__((always_inline)) {
+    for (int t = 1; t < ntiles; t += 4) {
+      tile(Buf<1>{}, t, act_c);
+      if (t + 1 < ntiles) tile(Buf<2>{}, t + 1, act_c);
+      if (t + 2 < ntiles) tile(Buf<3>{}, t + 2, act_c);
+      if (t + 3 < ntiles) tile(Buf<0>{}, t + 3, act_c);
+    }
+  };
+  if (active) loop(std::true_type{});
+  else loop(std::false_type{});
   // Drain: PV B of the last sub-tile (odd: vfr 1).  Every load (including
   // those of tiles past the range, which read zeros) has landed and every
   // wave has finished reading the tiles before the K buffers are reused for
