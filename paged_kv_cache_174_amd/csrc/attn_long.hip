@@ -117,54 +117,71 @@ attn_long_kernel(AttnArgs a) {
   const int z = static_cast<int>(item / static_cast<uint32_t>(a.row_tiles));
   const int hk = static_cast<int>(grp % static_cast<uint32_t>(a.num_kv_heads));
   const int b_pos = static_cast<int>(grp / static_cast<uint32_t>(a.num_kv_heads));
-  const int b = a.seq_order ? a.seq_order[b_pos] : b_pos;
-
+  // ---- the workgroup's sequence and its metadata, in as few dependent
+  // rounds of loads as possible (each is a trip to memory):
+  //   1. the sequence id (seq_order) and, with at most 64 sequences, every
+  //      sequence's entries (lane i loads sequence i's), read out of the
+  //      lanes once the id is known;
+  //   2. the sequence's segments, Q, and the block-table slice of the whole
+  //      key range a split may cover (a bound that needs no segment);
+  // all of it before any early exit, which the compiler cannot hoist loads
+  // across.  Round 1 goes to the vector memory unit as a whole (an opaque
+  // lane offset keeps the sequence-id load there too): scalar loads share
+  // one counter with the argument loads, and a wait for an argument pointer
+  // would also wait for the id and put the per-lane loads in a round of
+  // their own.
+  int b, t0, t1, s, seg0, seg1, qpos;
+  {
+    int vzero = 0;
+    asm volatile("" : "+v"(vzero));
+    const int vb = a.seq_order ? a.seq_order[b_pos + vzero] : b_pos;
+    if (a.num_seqs <= 64) {
+      const int li = min(lane, a.num_seqs - 1);
+      const int v_t0 = a.qsl[li], v_t1 = a.qsl[li + 1], v_s = a.seq_lens[li];
+      const int v_g0 = a.seg_loc[li], v_g1 = a.seg_loc[li + 1];
+      const int v_qp = a.query_pos ? a.query_pos[li] : 0;
+      b = __builtin_amdgcn_readfirstlane(vb);
+      t0 = __builtin_amdgcn_readlane(v_t0, b);
+      t1 = __builtin_amdgcn_readlane(v_t1, b);
+      s = __builtin_amdgcn_readlane(v_s, b);
+      seg0 = __builtin_amdgcn_readlane(v_g0, b);
+      seg1 = __builtin_amdgcn_readlane(v_g1, b);
+      qpos = __builtin_amdgcn_readlane(v_qp, b);
+    } else {
+      b = __builtin_amdgcn_readfirstlane(vb);
+      t0 = a.qsl[b];
+      t1 = a.qsl[b + 1];
+      s = a.seq_lens[b];
+      seg0 = a.seg_loc[b];
+      seg1 = a.seg_loc[b + 1];
+      qpos = a.query_pos ? a.query_pos[b] : 0;
+    }
+  }
   const int G = a.group;
-  const int t0 = a.qsl[b];
-  const int q_len = a.qsl[b + 1] - t0;
-  const int s = a.seq_lens[b];
+  const int q_len = t1 - t0;
   const int R = q_len * G;
   const int r0 = rt * kMfmaRows;
-  if (r0 >= R) return;
-  const int seg0 = a.seg_loc[b], seg1 = a.seg_loc[b + 1];
-  const int gbase = a.query_pos ? a.query_pos[b] : s - q_len;  // key position of the first query row
-  // Row limits are non-decreasing in the row's key position (the metadata
-  // check enforces it), so the tile's last row bounds the workgroup's keys
-  // and a wave's first row its mask-free prefix.
-  const int wg_kmax = row_limit(a.segments, seg0, seg1, gbase + (min(r0 + kMfmaRows, R) - 1) / G);
-  const int k_begin = z * a.split_len;
-  const int k_end = min(k_begin + a.split_len, wg_kmax);
-  const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
-  if (k_begin >= k_end) {
-    // No key of this split is visible to any row of the tile: its partial is
-    // empty (max -inf, sum 0), which the merge skips.
-    if (a.num_splits > 1 && threadIdx.x < kMfmaRows) {
-      const int row = r0 + static_cast<int>(threadIdx.x);
-      if (row < R) {
-        const int64_t orow = static_cast<int64_t>(t0 + row / G) * a.num_q_heads + hk * G + row % G;
-        const f32x2 ml = {-INFINITY, 0.f};
-        *reinterpret_cast<f32x2*>(a.ws_ml + (static_cast<int64_t>(z) * total_rows + orow) * 2) = ml;
-      }
-    }
-    return;
-  }
+  const int gbase = a.query_pos ? qpos : s - q_len;  // key position of the first query row
 
   const int wr0 = r0 + kWaveRows * w;  // first row of this wave
   const bool active = wr0 < R;
-  const int wave_kmin = active ? row_limit(a.segments, seg0, seg1, gbase + wr0 / G) : 0;
 
   // ---- this lane's query row in each half
   bool valid[2];
-  int tok[2], head[2], lrow[2];
+  int tok[2], head[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const int row = wr0 + kHalfRows * h + l32;
     valid[h] = row < R;
     tok[h] = valid[h] ? row / G : 0;
     head[h] = hk * G + (valid[h] ? row % G : 0);
-    lrow[h] = valid[h] ? row_limit(a.segments, seg0, seg1, gbase + tok[h]) : 0;
   }
 
+  // Round 2, in this order (a load's first use waits for it, and the
+  // compiler keeps the loads of separate branches in source order): Q, the
+  // first 256 entries of the block-table slice for the split's whole key
+  // range (a bound that needs no segment), the segments.
+  //
   // Q^T fragments for S^T = K Q^T: for k-step t the lane holds head-dim
   // [16 t + 8 h2, +8) of its row.  head_dim 64 runs through the same 128-wide
   // kernel with head-dim [64, 128) of Q, K and V zero: it adds nothing to a
@@ -181,17 +198,47 @@ attn_long_kernel(AttnArgs a) {
       qf[h][t] = __builtin_bit_cast(bf16x8, v);
     }
   }
-  // ---- block-table slice for this workgroup's keys (no table: the K/V
-  // buffers are one contiguous run, logical block i is block i)
+  // Block-table slice (no table: the K/V buffers are one contiguous run,
+  // logical block i is block i).
+  const int k_begin = z * a.split_len;
   const int nblk = (s + 15) >> 4;
   const int blk_lo = k_begin >> 4;
-  const int blk_hi = min((k_end + 15) >> 4, nblk);
-  if (a.block_table) {
-    const int32_t* table = a.block_table + static_cast<int64_t>(b) * a.table_width;
-    for (int i = threadIdx.x; i < blk_hi - blk_lo; i += NT) s_tbl[i] = table[blk_lo + i];
-  } else {
-    for (int i = threadIdx.x; i < blk_hi - blk_lo; i += NT) s_tbl[i] = blk_lo + i;
+  const int blk_cap = min(min((k_begin + a.split_len + 15) >> 4, nblk), blk_lo + kTableSlice);
+  const int32_t* const table = a.block_table ? a.block_table + static_cast<int64_t>(b) * a.table_width : nullptr;
+  const int tid = static_cast<int>(threadIdx.x);
+  int te = blk_lo + tid;
+  if (table && r0 < R && tid < blk_cap - blk_lo) te = table[blk_lo + tid];
+  const SegCache segc = load_segments(a.segments, seg0, seg1);
+  if (r0 < R) {
+    if (tid < blk_cap - blk_lo) s_tbl[tid] = te;
+    for (int i = tid + NT; i < blk_cap - blk_lo; i += NT) s_tbl[i] = table ? table[blk_lo + i] : blk_lo + i;
   }
+
+  if (r0 >= R) return;
+  // Row limits are non-decreasing in the row's key position (the metadata
+  // check enforces it), so the tile's last row bounds the workgroup's keys
+  // and a wave's first row its mask-free prefix.
+  const int wg_kmax = row_limit(segc, a.segments, seg0, seg1, gbase + (min(r0 + kMfmaRows, R) - 1) / G);
+  const int k_end = min(k_begin + a.split_len, wg_kmax);
+  const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
+  if (k_begin >= k_end) {
+    // No key of this split is visible to any row of the tile: its partial is
+    // empty (max -inf, sum 0), which the merge skips.
+    if (a.num_splits > 1 && threadIdx.x < kMfmaRows) {
+      const int row = r0 + static_cast<int>(threadIdx.x);
+      if (row < R) {
+        const int64_t orow = static_cast<int64_t>(t0 + row / G) * a.num_q_heads + hk * G + row % G;
+        const f32x2 ml = {-INFINITY, 0.f};
+        *reinterpret_cast<f32x2*>(a.ws_ml + (static_cast<int64_t>(z) * total_rows + orow) * 2) = ml;
+      }
+    }
+    return;
+  }
+  const int wave_kmin = active ? row_limit(segc, a.segments, seg0, seg1, gbase + wr0 / G) : 0;
+  int lrow[2];
+#pragma unroll
+  for (int h = 0; h < 2; ++h) lrow[h] = valid[h] ? row_limit(segc, a.segments, seg0, seg1, gbase + tok[h]) : 0;
+  const int blk_hi = min((k_end + 15) >> 4, nblk);
   // Q and the table slice have landed before any K/V load is issued (the
   // compiler cannot see the direct-to-LDS loads, and would otherwise guard a
   // later use of Q with a full vmcnt(0) that drains the K/V prefetch).

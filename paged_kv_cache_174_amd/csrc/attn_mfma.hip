@@ -175,10 +175,11 @@ attn_mfma_kernel(AttnArgs a) {
   const int r0 = rt * kMfmaRows;
   if (r0 >= R) return;
   const int seg0 = a.seg_loc[b], seg1 = a.seg_loc[b + 1];
+  const SegCache segc = load_segments(a.segments, seg0, seg1);
   const int gbase = a.query_pos ? a.query_pos[b] : s - q_len;  // key position of the first query row
   // Row limits are non-decreasing in the row's key position, so the last row
   // bounds the workgroup's key range and the first row of a wave its mask-free prefix.
-  const int wg_kmax = row_limit(a.segments, seg0, seg1, gbase + (min(r0 + kMfmaRows, R) - 1) / G);
+  const int wg_kmax = row_limit(segc, a.segments, seg0, seg1, gbase + (min(r0 + kMfmaRows, R) - 1) / G);
   const int k_begin = z * a.split_len;
   const int k_end = min(k_begin + a.split_len, wg_kmax);
   if (k_begin >= k_end) {
@@ -200,8 +201,8 @@ attn_mfma_kernel(AttnArgs a) {
   const int wr0 = SHORT ? kWaveRows * (w & 1) : r0 + kWaveRows * w;
   int wave_kmin = 0, wave_kmax = 0;
   if (wr0 < R) {
-    wave_kmin = row_limit(a.segments, seg0, seg1, gbase + wr0 / G);
-    wave_kmax = row_limit(a.segments, seg0, seg1, gbase + (min(wr0 + kWaveRows, R) - 1) / G);
+    wave_kmin = row_limit(segc, a.segments, seg0, seg1, gbase + wr0 / G);
+    wave_kmax = row_limit(segc, a.segments, seg0, seg1, gbase + (min(wr0 + kWaveRows, R) - 1) / G);
   }
 
   // ---- this lane's query row
@@ -209,7 +210,7 @@ attn_mfma_kernel(AttnArgs a) {
   const bool valid = row < R;
   const int tok = valid ? row / G : 0;
   const int head = hk * G + (valid ? row % G : 0);
-  const int Lrow = valid ? row_limit(a.segments, seg0, seg1, gbase + tok) : 0;
+  const int Lrow = valid ? row_limit(segc, a.segments, seg0, seg1, gbase + tok) : 0;
 
   // Q^T fragments for S^T = K Q^T: lane holds 8 consecutive head-dim values
   // [16 t + 8 h2, +8) of its query row for each of the 8 k-steps.
