@@ -273,7 +273,6 @@ attn_mfma_kernel(AttnArgs a) {
     k_src_off[st] = static_cast<int>(rb * row_bytes) + (st_pos ^ k_swz(st_row[st])) * 8 * ELSZ;
     v_src_off[st] = static_cast<int>(rb * row_bytes) + (st_pos ^ v_swz(st_row[st])) * 8 * ELSZ;
   }
-  const uint8_t* zero_row = reinterpret_cast<const uint8_t*>(g_zero_row) + 16 * st_pos;
 
   // Block-table entry of the 16 keys whose rows wave ws stages for the tile
   // at key kt (rows 8 ws .. 8 ws + 7 lie in block ws / 2 of the tile).
