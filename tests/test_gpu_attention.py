@@ -77,6 +77,18 @@ SMALL = [
                   history_lens=(1000, 37), query_lens=(32, 7), sink_tokens=(300, 0), window_tokens=(600, 1 << 30)),
     small_variant(CONFIGS["piecewise_gqa_bf16"], name="short_piecewise_bf16", num_q_heads=2, num_kv_heads=2,
                   history_lens=(200,), query_lens=(60,), full_spans=(((210, 240),),)),
+    # More than 64 sequences (the kernels then read each workgroup's sequence entries
+    # directly instead of across the lanes) and more than 8 segments in a sequence
+    # (row limits then come from the segment walk instead of the register copy).
+    small_variant(CONFIGS["frame_bf16"], name="many_seqs_long_bf16", num_q_heads=2, num_kv_heads=1,
+                  history_lens=tuple(20 + 7 * (i % 5) for i in range(70)), query_lens=(40,) * 70,
+                  sink_tokens=(0,) * 70, window_tokens=(1 << 30,) * 70, full_spans=(None,) * 70),
+    small_variant(CONFIGS["varlen_fp8"], name="many_seqs_fp8", num_q_heads=4, num_kv_heads=1,
+                  history_lens=tuple(30 + 11 * (i % 7) for i in range(66)), query_lens=(16,) * 33 + (90,) * 33,
+                  sink_tokens=(0,) * 66, window_tokens=(1 << 30,) * 66, full_spans=(None,) * 66),
+    small_variant(CONFIGS["piecewise_gqa_bf16"], name="many_segments_bf16", num_q_heads=4, num_kv_heads=2,
+                  history_lens=(100,), query_lens=(500,),
+                  full_spans=(((110, 130), (160, 170), (200, 260), (300, 310), (350, 400), (450, 520)),)),
     # head_dim 64 (P2's geometry: 4 heads, D 64, 16-token blocks) on each MFMA kernel:
     # bf16 long chunks, bf16 short chunks, fp8 long and short chunks, piecewise GQA.
     small_variant(CONFIGS["frame_bf16"], name="d64_bf16_long", head_dim=64, num_q_heads=4, num_kv_heads=4,
