@@ -108,6 +108,58 @@ def stored_traffic(workload: str, kernel: str = "attn_long"):
         return None
 
 
+class ClockSampler:
+    """Samples the shader clock the GPU's power management reports (the
+    starred level of ``pp_dpm_sclk``, an SMU average) from a host thread while
+    a block of work runs.  The matrix-core peak assumes 2.4 GHz; the sampled
+    clock says what the chip could deliver during the measurement."""
+
+    def __init__(self, period_s=0.01):
+        import glob
+        import threading
+
+        paths = sorted(glob.glob("/sys/class/drm/card*/device/pp_dpm_sclk"))
+        self.path = paths[0] if paths else None
+        self.period = period_s
+        self.samples = []
+        self._stop = threading.Event()
+        self._thread = threading.Thread(target=self._run, daemon=True)
+
+    def _read(self):
+        try:
+            with open(self.path) as f:
+                for ln in f:
+                    if ln.rstrip().endswith("*"):
+                        return float(ln.split(":")[1].strip().rstrip("*").strip().lower().rstrip("mhz"))
+        except (OSError, ValueError, IndexError):
+            return None
+        return None
+
+    def _run(self):
+        while not self._stop.is_set():
+            v = self._read()
+            if v is not None:
+                self.samples.append(v)
+            self._stop.wait(self.period)
+
+    def __enter__(self):
+        if self.path:
+            self._thread.start()
+        return self
+
+    def __exit__(self, *exc):
+        self._stop.set()
+        if self._thread.is_alive():
+            self._thread.join()
+
+    def summary(self):
+        if not self.samples:
+            return None
+        x = np.asarray(self.samples[len(self.samples) // 4:] or self.samples)
+        return {"median_mhz": round(float(np.median(x)), 1), "min_mhz": round(float(x.min()), 1),
+                "samples": len(x), "source": "pp_dpm_sclk, current level, during the settling steps"}
+
+
 def _softmax_scale(d):
     return float(np.float32(d ** -0.5))
 
@@ -210,10 +262,11 @@ def run_bench(args, geom):
     # management settles the clocks, so short measurements started from idle
     # overstate sustained throughput.)
     settle0 = time.perf_counter()
-    while time.perf_counter() - settle0 < 1.0:
-        for _ in range(16):
-            step()
-        torch.cuda.synchronize()
+    with ClockSampler() as clock:
+        while time.perf_counter() - settle0 < 1.0:
+            for _ in range(16):
+                step()
+            torch.cuda.synchronize()
 
     # Passes for `parts` and the roofline: the separate calls, per launch with
     # events between them and as whole steps.
@@ -229,6 +282,7 @@ def run_bench(args, geom):
         return float(np.mean([e[4 * i + a].elapsed_time(e[4 * i + b]) for e in evs for i in range(nl)]))
 
     write_ms, main_ms, merge_ms = mean_gap(0, 1), mean_gap(1, 2), mean_gap(2, 3)
+    plan_desc = P.pkv_last_attn_plan()
     separate_ms = timed(separate_step)
 
     # whole-step timing (the number `value` is computed from): W warm-up
@@ -319,7 +373,9 @@ def run_bench(args, geom):
         "separate_ms": separate_ms,
         "graph_ms": graph_ms,
         "plan": plan,
+        "plan_desc": plan_desc,
         "layers": nl,
+        "clock": clock.summary(),
     }
 
 
@@ -522,6 +578,7 @@ def run_kv_bound(args):
             ev[k + 2].record(stream)
             k += 3
     torch.cuda.synchronize()
+    plan_desc = P.pkv_last_attn_plan()
     ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 3)]))
     call_ms = float(np.mean([ev[i].elapsed_time(ev[i + 2]) for i in range(0, len(ev), 3)]))
     abytes = attn_bytes(geom, plan)
@@ -531,6 +588,7 @@ def run_kv_bound(args):
     return {
         "workload": geom.name,
         "kernel": "attn_mfma_kernel<fp8, short rows> + attn_combine_kernel",
+        "plan": plan_desc,
         "bound": "hbm",
         "achieved": round(gbps, 1),
         "peak": PEAK_HBM_GBPS,
@@ -672,8 +730,12 @@ def main():
             "frac": round(r["achieved_tflops"] / PEAK_BF16_TFLOPS, 4),
             "traffic": traffic,
             "kernel": "attn_long_kernel (bf16)",
+            "plan": r["plan_desc"],
             "flop_per_launch": r["flops"],
             "avg_launch_ms": round(r["main_ms"], 5),
+            "shader_clock": r["clock"],
+            "frac_of_peak_at_clock": (round(r["achieved_tflops"] / (PEAK_BF16_TFLOPS * r["clock"]["median_mhz"] / 2400.0), 4)
+                                      if r["clock"] else None),
         },
         "kv": {
             "achieved_gbps": round(r["kv_gbps"], 1),

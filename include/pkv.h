@@ -508,6 +508,11 @@ int pkv_wm_block_table(const pkv_window_manager* wm, int32_t request, int32_t* o
 /* Thread-local description of the last error returned on this thread ("" if none). */
 const char* pkv_last_error(void);
 
+/* Thread-local description of the kernel plan the last attention call on this
+   thread chose (after its checks passed): "long", "short" or "fp8" with the key
+   splits and their length, or "f32".  Diagnostic only: the format may change. */
+const char* pkv_last_attn_plan(void);
+
 /* Library version string. */
 const char* pkv_version(void);
 

@@ -20,6 +20,7 @@ from ._lib import (  # noqa: F401
     pkv_action_table,
     pkv_build_segments,
     pkv_gather,
+    pkv_last_attn_plan,
     pkv_last_error,
     pkv_paged_attn,
     pkv_paged_attn_main,

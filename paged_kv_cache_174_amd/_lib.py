@@ -154,6 +154,7 @@ _SIGNATURES = {
     "pkv_wm_info": (ctypes.c_int, [_P, _I32, _PI64]),
     "pkv_wm_block_table": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32]),
     "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_last_attn_plan": (ctypes.c_char_p, []),
     "pkv_version": (ctypes.c_char_p, []),
 }
 
@@ -627,6 +628,10 @@ def pkv_validate_metadata_host(query_start_loc, seq_lens, block_table, num_block
 
 def pkv_last_error() -> str:
     return lib().pkv_last_error().decode()
+
+
+def pkv_last_attn_plan() -> str:
+    return lib().pkv_last_attn_plan().decode()
 
 
 def pkv_version() -> str:

@@ -22,6 +22,7 @@ namespace pkv {
 
 namespace {
 thread_local char g_error[1024] = "";
+thread_local char g_plan[160] = "";
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices] = {0};
@@ -275,6 +276,8 @@ extern "C" {
 
 const char* pkv_last_error(void) { return g_error; }
 
+const char* pkv_last_attn_plan(void) { return g_plan; }
+
 const char* pkv_version(void) { return "pkv 0.1.0 (gfx950)"; }
 
 int pkv_paged_write(const void* key, const void* value, int32_t src_dtype, int64_t num_tokens,
@@ -392,6 +395,7 @@ int attn_setup(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num
     a.row_tiles = 0;
     a.split_len = 0;
     L.p = SplitPlan{0, 1, 0, false};
+    std::snprintf(g_plan, sizeof(g_plan), "f32");
     return PKV_OK;
   }
   if (pools->head_dim != 64 && pools->head_dim != 128)
@@ -411,6 +415,9 @@ int attn_setup(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num
   a.num_splits = p.splits;
   a.split_len = p.split_len;
   a.packed = p.packed ? 1 : 0;
+  std::snprintf(g_plan, sizeof(g_plan), "%s splits=%d split_len=%d row_tiles=%d packed=%d",
+                !L.fp8 && !p.short_rows ? "long" : p.short_rows ? "short" : "fp8", p.splits, p.split_len,
+                p.row_tiles, p.packed ? 1 : 0);
   if (p.splits > 1) {
     const int64_t rows = num_q_tokens * num_q_heads;
     a.ws_o = static_cast<float*>(workspace);
