@@ -116,44 +116,57 @@ attn_mfma_kernel(AttnArgs a) {
   // fastest) goes to XCD g % 8, which spreads every sequence over the XCDs
   // and keeps their loads balanced.
   int rt, z, hk, b;
+  // (packed: the sequence's entries, read across the lanes with the item)
+  int p_t0 = 0, p_t1 = 0, p_s = 0, p_g0 = 0, p_g1 = 0, p_qp = 0;
   if (SHORT && a.packed) {
     // Short query chunks planned from the sequences' lengths (one row tile):
     // the key ranges (sequence in seq_order, split z < ceil(seq_len /
     // split_len), KV head fastest) come first, then the empty ranges of every
-    // sequence, which only record empty partials.  Each workgroup finds its
-    // own item by walking the sequences (few: the host caps their number).
+    // sequence, which only record empty partials.  The host plans this only
+    // for at most 64 sequences, so lane i holds sequence i's entries and
+    // sequence position i's range count, and one round of loads finds the
+    // workgroup's item (a scan and a ballot over the lanes).
     const int H = a.num_kv_heads;
-    int i = static_cast<int>(blockIdx.x);
-    if (i >= a.num_seqs * H * a.num_splits) return;
-    int found = -1, loc = 0;
-    for (int bp = 0; bp < a.num_seqs && found < 0; ++bp) {
-      const int bb = a.seq_order ? a.seq_order[bp] : bp;
-      const int n = min(a.num_splits, (max(a.seq_lens[bb], 1) + a.split_len - 1) / a.split_len);
-      if (i < n * H) {
-        found = bb;
-        loc = i;
-      } else {
-        i -= n * H;
+    const int ns = a.num_seqs;
+    const int64_t i = blockIdx.x;
+    if (i >= static_cast<int64_t>(ns) * H * a.num_splits) return;
+    const int li = min(lane, ns - 1);
+    const int v_ord = a.seq_order ? a.seq_order[li] : li;
+    const int v_len = a.seq_lens[li];
+    const int v_t0 = a.qsl[li], v_t1 = a.qsl[li + 1];
+    const int v_g0 = a.seg_loc[li], v_g1 = a.seg_loc[li + 1];
+    const int v_qp = a.query_pos ? a.query_pos[li] : 0;
+    const int len_bp = __shfl(v_len, v_ord, 64);  // length of the sequence at position lane
+    const int n = lane < ns ? min(a.num_splits, (max(len_bp, 1) + a.split_len - 1) / a.split_len) : 0;
+    // inclusive scans over the positions of the non-empty and the empty ranges
+    int inc_full = n * H, inc_empty = lane < ns ? (a.num_splits - n) * H : 0;
+#pragma unroll
+    for (int d = 1; d < 64; d <<= 1) {
+      const int uf = __shfl_up(inc_full, d, 64), ue = __shfl_up(inc_empty, d, 64);
+      if (lane >= d) {
+        inc_full += uf;
+        inc_empty += ue;
       }
     }
-    if (found < 0) {  // an empty range
-      for (int bp = 0; bp < a.num_seqs && found < 0; ++bp) {
-        const int bb = a.seq_order ? a.seq_order[bp] : bp;
-        const int n = min(a.num_splits, (max(a.seq_lens[bb], 1) + a.split_len - 1) / a.split_len);
-        const int empties = (a.num_splits - n) * H;
-        if (i < empties) {
-          found = bb;
-          loc = n * H + i;
-        } else {
-          i -= empties;
-        }
-      }
-      if (found < 0) return;
-    }
-    b = found;
+    const int total_full = __builtin_amdgcn_readlane(inc_full, 63);
+    const bool empty_range = i >= total_full;
+    const int64_t k = empty_range ? i - total_full : i;  // rank among its kind
+    const int inc = empty_range ? inc_empty : inc_full;
+    // position: the first lane whose inclusive count passes k
+    const int bp = static_cast<int>(__builtin_popcountll(__builtin_amdgcn_ballot_w64(lane < ns && inc <= k)));
+    const int before = bp > 0 ? __builtin_amdgcn_readlane(inc, bp - 1) : 0;
+    const int n_bp = __builtin_amdgcn_readlane(n, bp);
+    const int loc = static_cast<int>(k - before) + (empty_range ? n_bp * H : 0);
+    b = __builtin_amdgcn_readlane(v_ord, bp);
     rt = 0;
     z = loc / H;
     hk = loc % H;
+    p_t0 = __builtin_amdgcn_readlane(v_t0, b);
+    p_t1 = __builtin_amdgcn_readlane(v_t1, b);
+    p_s = __builtin_amdgcn_readlane(v_len, b);
+    p_g0 = __builtin_amdgcn_readlane(v_g0, b);
+    p_g1 = __builtin_amdgcn_readlane(v_g1, b);
+    p_qp = __builtin_amdgcn_readlane(v_qp, b);
   } else {
     const uint32_t xcd = blockIdx.x & 7u, pos = blockIdx.x >> 3;
     const uint32_t per_group = static_cast<uint32_t>(a.num_splits) * static_cast<uint32_t>(a.row_tiles);
@@ -168,15 +181,17 @@ attn_mfma_kernel(AttnArgs a) {
   }
 
   const int G = a.group;
-  const int t0 = a.qsl[b];
-  const int q_len = a.qsl[b + 1] - t0;
-  const int s = a.seq_lens[b];
+  const bool pk = SHORT && a.packed;
+  const int t0 = pk ? p_t0 : a.qsl[b];
+  const int q_len = (pk ? p_t1 : a.qsl[b + 1]) - t0;
+  const int s = pk ? p_s : a.seq_lens[b];
   const int R = q_len * G;
   const int r0 = rt * kMfmaRows;
   if (r0 >= R) return;
-  const int seg0 = a.seg_loc[b], seg1 = a.seg_loc[b + 1];
+  const int seg0 = pk ? p_g0 : a.seg_loc[b], seg1 = pk ? p_g1 : a.seg_loc[b + 1];
   const SegCache segc = load_segments(a.segments, seg0, seg1);
-  const int gbase = a.query_pos ? a.query_pos[b] : s - q_len;  // key position of the first query row
+  // key position of the first query row
+  const int gbase = a.query_pos ? (pk ? p_qp : a.query_pos[b]) : s - q_len;
   // Row limits are non-decreasing in the row's key position, so the last row
   // bounds the workgroup's key range and the first row of a wave its mask-free prefix.
   const int wg_kmax = row_limit(segc, a.segments, seg0, seg1, gbase + (min(r0 + kMfmaRows, R) - 1) / G);
