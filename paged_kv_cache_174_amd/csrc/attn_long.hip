@@ -25,8 +25,8 @@
 //   fixed after each half's first 32 keys (their exact maximum): softmax is
 //   exact for any common offset, so a stale m changes nothing but rounding,
 //   and O and l are never rescaled in the loop.  Row sums are taken on the
-//   matrix cores (ones x P^T), i.e. of the bf16-rounded probabilities that
-//   multiply V.  If a row's sum passes kFastSumLimit (2^64) or is not finite --
+//   matrix cores (a 16x16x32 MFMA of a 0/1 selector with P^T), i.e. of the
+//   bf16-rounded probabilities that multiply V.  If a row's sum passes kFastSumLimit (2^64) or is not finite --
 //   some later score rose more than 64 / c above the first keys' maximum --
 //   the workgroup recomputes its key range exactly, tile by tile, with the
 //   maximum moving per sub-tile and O and l rescaled.
@@ -417,19 +417,28 @@ attn_long_kernel(AttnArgs a) {
   // ([k16][db]), alternating with the sub-tile's parity.
   bf16x8 kfr[8];
   bf16x8 vfr[2][2][4];
-  // Row sums on the matrix cores: rs[h] += ones x P^T puts the sum of a
-  // row's bf16 probabilities -- exactly the weights that multiply V -- in
-  // every element of the row's lane (both lane halves hold all of it).
-  f32x16 rs[2];
-  bf16x8 ones;
+  // Row sums on the matrix cores, of the bf16 probabilities -- exactly the
+  // weights that multiply V.  A PV operand pb (16 keys of 32 rows; lane l
+  // holds row l % 32, keys 8 (l / 32) .. + 7) read as the B operand of the
+  // 16x16x32 MFMA gives column n = l % 16 the lanes n, n + 16, n + 32, n + 48,
+  // i.e. rows n and n + 16, each with both key halves.  The selector A takes
+  // lane groups 0 and 2 (row n) into output rows 0..7 and groups 1 and 3
+  // (row n + 16) into 8..15, so rs[h] += sel x pb puts row n's sum in lanes n
+  // and n + 16 and row n + 16's in lanes n + 32 and n + 48, at half the
+  // matrix work of a 32x32x16 product.
+  f32x4 rs[2];
+  bf16x8 sel;
+  {
+    const bool lower = (lane & 15) < 8, even_group = ((lane >> 4) & 1) == 0;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) ones[i] = static_cast<__bf16>(1.0f);
+    for (int i = 0; i < 8; ++i) sel[i] = static_cast<__bf16>(lower == even_group ? 1.0f : 0.0f);
+  }
   // (opaque from here on: kept in registers rather than rebuilt in every phase)
-  asm volatile("" : "+v"(ones));
+  asm volatile("" : "+v"(sel));
 #pragma unroll
   for (int h = 0; h < 2; ++h)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) rs[h][r] = 0.f;
+    for (int r = 0; r < 4; ++r) rs[h][r] = 0.f;
 
   // One phase: 18 slots, each one MFMA plus at most ~28 cycles of other
   // issue (a 32-cycle MFMA hides that much of its own wave's work; a wave
@@ -473,13 +482,13 @@ attn_long_kernel(AttnArgs a) {
           const int q = j >> 1;  // PV operand (k16, db) = (q / 4, q % 4)
           o[HP][q & 3] = mfma(vfr[VPV][q >> 2][q & 3], pb[HP][q >> 2], o[HP][q & 3]);
         } else {
-          rs[HP] = mfma(ones, pb[HP][j - 16], rs[HP]);
+          rs[HP] = mfma16(sel, pb[HP][j - 16], rs[HP]);
         }
       } else {
         if (j < 8) {
           o[HP][j & 3] = mfma(vfr[VPV][j >> 2][j & 3], pb[HP][j >> 2], o[HP][j & 3]);
         } else if (j < 10) {
-          rs[HP] = mfma(ones, pb[HP][j - 8], rs[HP]);
+          rs[HP] = mfma16(sel, pb[HP][j - 8], rs[HP]);
         } else {
           sc[HQ] = mfma(kfr[j - 10], qf[HQ][j - 10], sc[HQ]);
         }
@@ -659,12 +668,15 @@ attn_long_kernel(AttnArgs a) {
     for (int k16 = 0; k16 < 2; ++k16) {
 #pragma unroll
       for (int db = 0; db < 4; ++db) o[1][db] = mfma(vfr[1][k16][db], pb[1][k16], o[1][db]);
-      rs[1] = mfma(ones, pb[1][k16], rs[1]);
+      rs[1] = mfma16(sel, pb[1][k16], rs[1]);
     }
   }
-  // Row sums (the whole row's, in every lane of it).
-  l[0] = rs[0][0];
-  l[1] = rs[1][0];
+  // Row sums into the lanes of their rows (lane l32 and l32 + 32 hold row l32).
+  {
+    const int src = l32 < 16 ? l32 : l32 + 16;
+    l[0] = __shfl(rs[0][0], src, 64);
+    l[1] = __shfl(rs[1][0], src, 64);
+  }
   const bool overflow = __builtin_amdgcn_ballot_w64(active && !(fmaxf(l[0], l[1]) <= kFastSumLimit)) != 0;
   wait_vmcnt<0>();
   if (lane == 0) s_overflow[w] = overflow ? 1 : 0;

@@ -94,6 +94,10 @@ __device__ __forceinline__ void wait_vmcnt() {
 __device__ __forceinline__ f32x16 mfma(bf16x8 a, bf16x8 b, f32x16 c) {
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
+// The 16x16x32 bf16 MFMA (half the matrix work of the 32x32x16 one).
+__device__ __forceinline__ f32x4 mfma16(bf16x8 a, bf16x8 b, f32x4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
 
 // Lanes l and l ^ 32 hold the two key halves of one query row in the S^T
 // accumulator layout.  v_permlane32_swap exchanges the upper half of its first
