@@ -441,15 +441,16 @@ attn_long_kernel(AttnArgs a) {
     for (int r = 0; r < 4; ++r) rs[h][r] = 0.f;
 
   // One phase: 18 slots, each one MFMA plus at most ~28 cycles of other
-  // issue (a 32-cycle MFMA hides that much of its own wave's work; a wave
-  // issues in order, so more, or an instruction waiting on a result, idles
-  // the matrix pipe).  Two forms:
-  //   alpha(u) (BETA false): slots 0-15 alternate QK B(u) (from kfr) and
-  //     PV B(u - 1) (from vfr[VPV]); 16-17 its row sums; slots 0-7 each read
-  //     one V(u) operand (tile buffer BR, key block KR) into vfr[1 - VPV].
+  // issue (a 32-cycle MFMA hides that much of its own wave's work, a
+  // 16-cycle row-sum MFMA about 12; a wave issues in order, so more, or an
+  // instruction waiting on a result, idles the matrix pipe).  Two forms:
+  //   alpha(u) (BETA false): slots 0-7 and 10-17 alternate QK B(u) (from kfr)
+  //     and PV B(u - 1) (from vfr[VPV]); 8-9 B(u - 1)'s row sums; slots 0-7
+  //     each read one V(u) operand (tile buffer BR, key block KR) into
+  //     vfr[1 - VPV].
   //   beta(u) (BETA true): slots 0-7 PV A(u) (from vfr[VPV]), each reading
-  //     one K operand of u + 1 (BR, KR) into kfr; 8-9 the row sums; 10-17
-  //     QK A(u + 1) from those operands.
+  //     one K operand of u + 1 (BR, KR) into kfr; 8-15 QK A(u + 1) from those
+  //     operands; 16-17 A(u)'s row sums.
   // With SOFT the probabilities of the other half (HS) from its scores:
   // scale-and-shift of two scores in each of slots 0-7, their exponentials
   // in slots 8-15 and their bf16 packs in slots 10-17, each stage a slot or
@@ -476,21 +477,24 @@ attn_long_kernel(AttnArgs a) {
     for (int j = 0; j < 18; ++j) {
       // the slot's MFMA
       if constexpr (!BETA) {
-        if (j < 16 && (j & 1) == 0) {
-          sc[HQ] = mfma(kfr[j >> 1], qf[HQ][j >> 1], sc[HQ]);
-        } else if (j < 16) {
-          const int q = j >> 1;  // PV operand (k16, db) = (q / 4, q % 4)
-          o[HP][q & 3] = mfma(vfr[VPV][q >> 2][q & 3], pb[HP][q >> 2], o[HP][q & 3]);
+        if (j == 8 || j == 9) {
+          rs[HP] = mfma16(sel, pb[HP][j - 8], rs[HP]);
         } else {
-          rs[HP] = mfma16(sel, pb[HP][j - 16], rs[HP]);
+          const int jj = j < 8 ? j : j - 2;
+          if ((jj & 1) == 0) {
+            sc[HQ] = mfma(kfr[jj >> 1], qf[HQ][jj >> 1], sc[HQ]);
+          } else {
+            const int q = jj >> 1;  // PV operand (k16, db) = (q / 4, q % 4)
+            o[HP][q & 3] = mfma(vfr[VPV][q >> 2][q & 3], pb[HP][q >> 2], o[HP][q & 3]);
+          }
         }
       } else {
         if (j < 8) {
           o[HP][j & 3] = mfma(vfr[VPV][j >> 2][j & 3], pb[HP][j >> 2], o[HP][j & 3]);
-        } else if (j < 10) {
-          rs[HP] = mfma16(sel, pb[HP][j - 8], rs[HP]);
+        } else if (j < 16) {
+          sc[HQ] = mfma(kfr[j - 8], qf[HQ][j - 8], sc[HQ]);
         } else {
-          sc[HQ] = mfma(kfr[j - 10], qf[HQ][j - 10], sc[HQ]);
+          rs[HP] = mfma16(sel, pb[HP][j - 16], rs[HP]);
         }
       }
       // LDS operand reads
