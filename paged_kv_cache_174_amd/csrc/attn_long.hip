@@ -625,6 +625,9 @@ attn_long_kernel(AttnArgs a) {
     constexpr int Tp1 = (T + 1) % kBufs, Tp2 = (T + 2) % kBufs, Tp3 = (T + 3) % kBufs;
     const int kt = kt_of(t);
     const bool edge = kt + kTileKeys > wave_kmin;  // some row of the wave masks keys of this tile
+    // Block of this wave's loads of tile t + 3, read from LDS here so that
+    // its latency passes under the phases instead of in front of the barrier.
+    const int e_next = block_entry(kt_of(t + 3));
     if constexpr (ACT) {
       // alpha(2t): QK B(2t), PV B(2t-1) [vfr 1]; reads V(2t) [T, 0] into vfr 0; K rows 2-3 of tile t+2
       if (__builtin_expect(edge, 0)) mask(0, kt);
@@ -641,7 +644,6 @@ attn_long_kernel(AttnArgs a) {
       idle_loads(I2{}, I0{}, Buf<Tp2>{}, t + 2, boff_load);
       idle_loads(I2{}, I2{}, Buf<Tp2>{}, t + 2, boff_load);
     }
-    const int e_next = block_entry(kt_of(t + 3));
     wait_vmcnt<8>();  // tile t + 1 landed (tile t + 2's eight loads may be in flight)
     lds_barrier();
     boff_load = entry_base(e_next);
