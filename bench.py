@@ -605,6 +605,50 @@ def run_kv_bound(args):
     }
 
 
+def measured_peaks(reps=5):
+    """The chip's sustained bf16 matrix-core rate and HBM read rate, from the
+    library's two probe kernels (independent MFMA chains on every SIMD; one
+    grid-stride read of 2 GiB), each the median of `reps` launches timed with
+    events after two untimed ones."""
+    import paged_kv_cache_174_amd as P
+
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    stream = torch.cuda.current_stream()
+
+    def median_ms(fn):
+        for _ in range(2):
+            fn()
+        ts = []
+        for _ in range(reps):
+            a = torch.cuda.Event(enable_timing=True)
+            b = torch.cuda.Event(enable_timing=True)
+            a.record(stream)
+            fn()
+            b.record(stream)
+            b.synchronize()
+            ts.append(a.elapsed_time(b))
+        return float(np.median(ts))
+
+    sink = torch.empty(512 * cus, dtype=torch.float32, device="cuda")
+    flop = [0]
+
+    def mfma():
+        flop[0] = P.pkv_probe_mfma(40000, sink)
+
+    mfma_ms = median_ms(mfma)
+    buf = torch.empty(2 << 30, dtype=torch.uint8, device="cuda")
+    sink8 = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    read_ms = median_ms(lambda: P.pkv_probe_stream(buf, sink8))
+    del buf
+    torch.cuda.empty_cache()
+    return {
+        "mfma_bf16_tflops": round(flop[0] / (mfma_ms * 1e-3) / 1e12, 1),
+        "hbm_read_gbps": round((2 << 30) / (read_ms * 1e-3) / 1e9, 1),
+        "method": "pkv_probe_mfma (4 independent 32x32x16 bf16 chains per wave, 2 waves per SIMD) and "
+                  "pkv_probe_stream (one read of 2 GiB, a contiguous chunk per workgroup), median of 5 event-timed launches",
+    }
+
+
 def cpu_baseline(geom, budget_s, min_s=10.0):
     """The float64 oracle on the host cores, on a bounded sample of the same
     workload: layer 0's oracle metadata, its pool writes and its attention,
@@ -695,6 +739,9 @@ def main():
                 print(f"[bench] config {name}", file=sys.stderr, flush=True)
                 configs[name] = run_config(CONFIGS[name], max(3, args.steps // 2), max(1, args.warmup // 2))
     copies = None if args.no_hbm_copies else hbm_copies(geom)
+    peaks = measured_peaks()
+    if kvb is not None:
+        kvb["frac_of_measured_peak"] = round(kvb["achieved"] / peaks["hbm_read_gbps"], 4)
     cpu = None if args.no_cpu_baseline else cpu_baseline(geom, args.cpu_budget_s)
     traffic = stored_traffic(geom.name)
     line = {
@@ -736,6 +783,7 @@ def main():
             "shader_clock": r["clock"],
             "frac_of_peak_at_clock": (round(r["achieved_tflops"] / (PEAK_BF16_TFLOPS * r["clock"]["median_mhz"] / 2400.0), 4)
                                       if r["clock"] else None),
+            "frac_of_measured_peak": round(r["achieved_tflops"] / peaks["mfma_bf16_tflops"], 4),
         },
         "kv": {
             "achieved_gbps": round(r["kv_gbps"], 1),
@@ -744,6 +792,7 @@ def main():
             "bytes_per_launch": r["attn_bytes"],
         },
         "kv_bound": kvb,
+        "measured_peaks": peaks,
         "parts": {
             "paged_write": {"ms": round(r["write_ms"], 5), "gbps": round(r["write_gbps"], 1)},
             "split_merge_ms": round(r["merge_ms"], 5),

@@ -513,6 +513,26 @@ const char* pkv_last_error(void);
    splits and their length, or "f32".  Diagnostic only: the format may change. */
 const char* pkv_last_attn_plan(void);
 
+/*
+ * Measured peaks (diagnostics for stating fractions against what this GPU
+ * sustains; not part of the attention path).  Both only enqueue work on
+ * `stream`: the caller times it (events) and synchronises.
+ *
+ * pkv_probe_mfma: every SIMD issues `iters` x 4 independent bf16
+ *   v_mfma_f32_32x32x16 products (two waves per SIMD, one workgroup of four
+ *   waves per half CU).  *out_flop receives the floating-point operations the
+ *   launch performs.  sink: device float scratch of at least 512 x (CU count)
+ *   floats (the products' sums land there).
+ * pkv_probe_stream: reads `bytes` (a multiple of 16) of device memory at `src`
+ *   once, each workgroup its own contiguous chunk, 16 bytes per lane with eight
+ *   loads in flight; sink: device scratch of at least 4 KB (written only in a
+ *   case that never occurs in practice).
+ * Errors: PKV_EINVAL for null pointers or sizes out of range, PKV_EHIP when no
+ * device is current or the launch fails.
+ */
+int pkv_probe_mfma(int64_t iters, void* sink, int64_t sink_floats, int64_t* out_flop, void* stream);
+int pkv_probe_stream(const void* src, int64_t bytes, void* sink, void* stream);
+
 /* Library version string. */
 const char* pkv_version(void);
 

@@ -29,6 +29,8 @@ from ._lib import (  # noqa: F401
     pkv_paged_attn_workspace_size,
     pkv_paged_write,
     pkv_paged_write_attn,
+    pkv_probe_mfma,
+    pkv_probe_stream,
     pkv_slot_mapping,
     pkv_validate_metadata_host,
     pkv_version,

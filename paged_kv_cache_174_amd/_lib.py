@@ -155,6 +155,8 @@ _SIGNATURES = {
     "pkv_wm_block_table": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32]),
     "pkv_last_error": (ctypes.c_char_p, []),
     "pkv_last_attn_plan": (ctypes.c_char_p, []),
+    "pkv_probe_mfma": (ctypes.c_int, [ctypes.c_int64, _P, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64), _P]),
+    "pkv_probe_stream": (ctypes.c_int, [_P, ctypes.c_int64, _P, _P]),
     "pkv_version": (ctypes.c_char_p, []),
 }
 
@@ -628,6 +630,24 @@ def pkv_validate_metadata_host(query_start_loc, seq_lens, block_table, num_block
 
 def pkv_last_error() -> str:
     return lib().pkv_last_error().decode()
+
+
+def pkv_probe_mfma(iters: int, sink: torch.Tensor, stream=None) -> int:
+    """Enqueues the matrix-core peak probe; returns the FLOP it performs.
+    sink: a float32 device tensor of at least 512 x CU-count elements."""
+    flop = ctypes.c_int64(0)
+    _check(lib().pkv_probe_mfma(int(iters), _dev(sink, "sink", torch.float32), sink.numel(), ctypes.byref(flop),
+                                _stream(stream)))
+    return int(flop.value)
+
+
+def pkv_probe_stream(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Enqueues one read of src's bytes (the HBM read-rate probe); sink: a
+    device tensor of at least 4 KB."""
+    if sink.numel() * sink.element_size() < 4096:
+        raise ValueError("sink must hold at least 4 KB")
+    _check(lib().pkv_probe_stream(_dev(src, "src"), src.numel() * src.element_size(), _dev(sink, "sink"),
+                                  _stream(stream)))
 
 
 def pkv_last_attn_plan() -> str:

@@ -7,6 +7,7 @@ import pytest
 import torch
 
 import oracle as O
+import paged_kv_cache_174_amd as P
 from oracle import harness as H
 from workloads import CONFIGS, make_workload, small_variant
 from workloads.configs import Workload
@@ -276,3 +277,31 @@ def test_length_hint_changes_only_the_work_split():
         got = G.as_f64(o)
         assert np.isfinite(got).all() and np.max(np.abs(got - ref)) <= 6e-2
         assert np.max(np.abs(got - G.as_f64(outs[0]))) <= 2e-2
+
+
+def test_peak_probes_report_plausible_rates():
+    """The diagnostic probes bench.py states its measured-peak fractions against:
+    the bf16 matrix-core rate lies between a tenth of and the vendor's 2.5
+    PFLOP/s, the HBM read rate between a tenth of and the vendor's 8 TB/s."""
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    sink = torch.empty(512 * cus, dtype=torch.float32, device="cuda")
+    flop = P.pkv_probe_mfma(2000, sink)
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    flop = P.pkv_probe_mfma(20000, sink)
+    b.record()
+    b.synchronize()
+    tflops = flop / (a.elapsed_time(b) * 1e-3) / 1e12
+    assert 250 < tflops <= 2500 * 1.02, tflops
+    assert torch.isfinite(sink).all()
+    buf = torch.ones(1 << 30, dtype=torch.uint8, device="cuda")  # four times the last-level cache
+    sink8 = torch.zeros(4096, dtype=torch.uint8, device="cuda")
+    P.pkv_probe_stream(buf, sink8)
+    torch.cuda.synchronize()
+    a.record()
+    P.pkv_probe_stream(buf, sink8)
+    b.record()
+    b.synchronize()
+    gbps = buf.numel() / (a.elapsed_time(b) * 1e-3) / 1e9
+    assert 800 < gbps <= 8000 * 1.05, gbps
