@@ -518,11 +518,11 @@ const char* pkv_last_attn_plan(void);
  * sustains; not part of the attention path).  Both only enqueue work on
  * `stream`: the caller times it (events) and synchronises.
  *
- * pkv_probe_mfma: every SIMD issues `iters` x 4 independent bf16
- *   v_mfma_f32_32x32x16 products (two waves per SIMD, one workgroup of four
- *   waves per half CU).  *out_flop receives the floating-point operations the
- *   launch performs.  sink: device float scratch of at least 512 x (CU count)
- *   floats (the products' sums land there).
+ * pkv_probe_mfma: two workgroups of four waves per CU (two waves per SIMD),
+ *   each wave issuing `iters` x 4 independent bf16 v_mfma_f32_32x32x16
+ *   products.  *out_flop receives the floating-point operations the launch
+ *   performs.  sink: device float scratch of at least 512 x (CU count) floats
+ *   (the products' sums land there).
  * pkv_probe_stream: reads `bytes` (a multiple of 16) of device memory at `src`
  *   once, each workgroup its own contiguous chunk, 16 bytes per lane with eight
  *   loads in flight; sink: device scratch of at least 4 KB (written only in a
