@@ -367,3 +367,30 @@ def test_shards_are_checked_like_the_pages_check_them(pkv):
         pkv.pkv_validate_metadata_host(bad.query_start_host, bad.kv_lens, bad.block_table_host, 10, 16,
                                        bad.max_query_len, bad.max_seq_len, bad.segments_host,
                                        bad.segment_start_host, query_pos=[70])
+
+
+def test_probe_entry_points_check_their_arguments(pkv):
+    """The measured-peak probes refuse null pointers and sizes out of range
+    before touching a device (no GPU needed)."""
+    lib = pkv.lib()
+    flop = ctypes.c_int64(0)
+    assert lib.pkv_probe_mfma(0, ctypes.c_void_p(16), 1 << 20, ctypes.byref(flop), None) == pkv._lib.PKV_EINVAL
+    assert lib.pkv_probe_mfma(10, None, 1 << 20, ctypes.byref(flop), None) == pkv._lib.PKV_EINVAL
+    assert lib.pkv_probe_mfma(10, ctypes.c_void_p(16), 1 << 20, None, None) == pkv._lib.PKV_EINVAL
+    assert "pkv_probe_mfma" in pkv.pkv_last_error()
+    assert lib.pkv_probe_stream(None, 1 << 20, ctypes.c_void_p(16), None) == pkv._lib.PKV_EINVAL
+    assert lib.pkv_probe_stream(ctypes.c_void_p(16), 15, ctypes.c_void_p(16), None) == pkv._lib.PKV_EINVAL
+    assert lib.pkv_probe_stream(ctypes.c_void_p(16), 1 << 20, None, None) == pkv._lib.PKV_EINVAL
+    assert "pkv_probe_stream" in pkv.pkv_last_error()
+
+
+def test_last_attn_plan_is_empty_before_any_attention_call(pkv):
+    """The plan diagnostic is a thread-local string; on a thread that made no
+    attention call it is empty."""
+    import threading
+
+    seen = []
+    t = threading.Thread(target=lambda: seen.append(pkv.pkv_last_attn_plan()))
+    t.start()
+    t.join()
+    assert seen == [""]
