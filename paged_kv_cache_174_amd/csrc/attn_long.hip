@@ -78,6 +78,10 @@ __shared__ int32_t s_overflow[NW];      // per wave: some row's probability sum 
 
 // Fourth word of a raw buffer descriptor on gfx9 (32-bit data format).
 constexpr int kBufferWord3 = 0x00020000;
+// A lane offset past every descriptor's range (a K/V descriptor spans at most
+// 16 rows of a few KB, the Q descriptor exactly this, with offsets below 65
+// tokens of one chunk): the lane's 16 bytes arrive as zeros.
+constexpr uint32_t kPastRange = 0x40000000u;
 
 template <int B>
 using Buf = std::integral_constant<int, B>;
@@ -97,7 +101,6 @@ __device__ __forceinline__ void dma16_buf(u32x4 r, uint32_t off, const void* l) 
   const uint32_t m0 = static_cast<uint32_t>(reinterpret_cast<uintptr_t>((lds_ptr)l));
   asm volatile("s_nop 0\nbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(off), "s"(r), "{m0}"(m0));
 }
-
 __global__ __attribute__((amdgpu_flat_work_group_size(NT, NT), amdgpu_waves_per_eu(1, 1))) void
 attn_long_kernel(AttnArgs a) {
   const int lane = threadIdx.x & 63;
@@ -122,10 +125,12 @@ attn_long_kernel(AttnArgs a) {
   //   1. the sequence id (seq_order) and, with at most 64 sequences, every
   //      sequence's entries (lane i loads sequence i's), read out of the
   //      lanes once the id is known;
-  //   2. the sequence's segments, Q, and the block-table slice of the whole
-  //      key range a split may cover (a bound that needs no segment);
-  // all of it before any early exit, which the compiler cannot hoist loads
-  // across.  Round 1 goes to the vector memory unit as a whole (an opaque
+  //   2. the sequence's segments, the block-table slice of the whole key
+  //      range a split may cover (a bound that needs no segment) and Q;
+  // all of it into registers and used up before the first direct-to-LDS
+  // load goes out (the compiler waits for a load of its own with a vmcnt
+  // that would also drain every direct load issued before the wait).
+  // Round 1 goes to the vector memory unit as a whole (an opaque
   // lane offset keeps the sequence-id load there too): scalar loads share
   // one counter with the argument loads, and a wait for an argument pointer
   // would also wait for the id and put the per-lane loads in a round of
@@ -177,29 +182,9 @@ attn_long_kernel(AttnArgs a) {
     head[h] = hk * G + (valid[h] ? row % G : 0);
   }
 
-  // Round 2, in this order (a load's first use waits for it, and the
-  // compiler keeps the loads of separate branches in source order): Q, the
-  // first 256 entries of the block-table slice for the split's whole key
-  // range (a bound that needs no segment), the segments.
-  //
-  // Q^T fragments for S^T = K Q^T: for k-step t the lane holds head-dim
-  // [16 t + 8 h2, +8) of its row.  head_dim 64 runs through the same 128-wide
-  // kernel with head-dim [64, 128) of Q, K and V zero: it adds nothing to a
-  // score, and the output's upper half is never stored.
-  const int dh = a.head_dim;  // 64 or 128
-  bf16x8 qf[2][8];
-#pragma unroll
-  for (int h = 0; h < 2; ++h) {
-    const __bf16* qr = static_cast<const __bf16*>(a.q) + (static_cast<int64_t>(t0 + tok[h]) * a.num_q_heads + head[h]) * dh;
-#pragma unroll
-    for (int t = 0; t < 8; ++t) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (valid[h] && 16 * t + 8 * h2 < dh) v = *reinterpret_cast<const u32x4*>(qr + 16 * t + 8 * h2);
-      qf[h][t] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-  // Block-table slice (no table: the K/V buffers are one contiguous run,
-  // logical block i is block i).
+  if (r0 >= R) return;
+  // Round 2.  Block-table slice (no table: the K/V buffers are one
+  // contiguous run, logical block i is block i).
   const int k_begin = z * a.split_len;
   const int nblk = (s + 15) >> 4;
   const int blk_lo = k_begin >> 4;
@@ -207,14 +192,48 @@ attn_long_kernel(AttnArgs a) {
   const int32_t* const table = a.block_table ? a.block_table + static_cast<int64_t>(b) * a.table_width : nullptr;
   const int tid = static_cast<int>(threadIdx.x);
   int te = blk_lo + tid;
-  if (table && r0 < R && tid < blk_cap - blk_lo) te = table[blk_lo + tid];
+  if (table && tid < blk_cap - blk_lo) te = table[blk_lo + tid];
   const SegCache segc = load_segments(a.segments, seg0, seg1);
-  if (r0 < R) {
-    if (tid < blk_cap - blk_lo) s_tbl[tid] = te;
-    for (int i = tid + NT; i < blk_cap - blk_lo; i += NT) s_tbl[i] = table ? table[blk_lo + i] : blk_lo + i;
+  // Q by whole rows: load st brings rows 4 st + lane / 16 of the wave, 16
+  // bytes (chunk lane % 16) per lane, so each load is 1 KB of consecutive
+  // 256-byte rows.  (A load in the MFMA operand layout would take 32 bytes
+  // of each of 32 rows, pieces whose address processing makes Q arrive
+  // several times later than the table slice.)  Buffer loads, so that the
+  // sixteen go out unconditionally, together with the table and segment
+  // loads: rows past the chunk and chunks past head_dim get an offset past
+  // the descriptor's range and read zeros.  head_dim 64 runs through the same
+  // 128-wide kernel with head-dim [64, 128) of Q, K and V zero: it adds
+  // nothing to a score, and the output's upper half is never stored.
+  const int dh = a.head_dim;  // 64 or 128
+  u32x4 qv[16];
+  {
+    const int tok_w0 = wr0 / G;
+    const uint8_t* const qbase = static_cast<const uint8_t*>(a.q) +
+                                 (static_cast<int64_t>(t0 + tok_w0) * a.num_q_heads + hk * G) * 2 * dh;
+    const __amdgpu_buffer_rsrc_t qrs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<uint8_t*>(qbase), 0, static_cast<int>(kPastRange), kBufferWord3);
+    // The lane's row of load st is head g of its token; roff is the row's
+    // byte offset from qbase.
+    const int head_b = 2 * dh, tok_b = a.num_q_heads * head_b;
+    const int gr = wr0 + (lane >> 4);
+    int g = gr % G;
+    int roff = (gr / G - tok_w0) * tok_b + g * head_b;
+    const int step_g = 4 % G, step_off = (4 / G) * tok_b + step_g * head_b, wrap_off = tok_b - G * head_b;
+    const bool in_row = 16 * (lane & 15) < head_b;
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const bool ok = wr0 + 4 * st + (lane >> 4) < R && in_row;
+      qv[st] = __builtin_amdgcn_raw_buffer_load_b128(qrs, ok ? roff + 16 * (lane & 15) : static_cast<int>(kPastRange), 0, 0);
+      g += step_g;
+      roff += step_off;
+      if (g >= G) {
+        g -= G;
+        roff += wrap_off;
+      }
+    }
   }
-
-  if (r0 >= R) return;
+  if (tid < blk_cap - blk_lo) s_tbl[tid] = te;
+  for (int i = tid + NT; i < blk_cap - blk_lo; i += NT) s_tbl[i] = table ? table[blk_lo + i] : blk_lo + i;
   // Row limits are non-decreasing in the row's key position (the metadata
   // check enforces it), so the tile's last row bounds the workgroup's keys
   // and a wave's first row its mask-free prefix.
@@ -239,10 +258,36 @@ attn_long_kernel(AttnArgs a) {
 #pragma unroll
   for (int h = 0; h < 2; ++h) lrow[h] = valid[h] ? row_limit(segc, a.segments, seg0, seg1, gbase + tok[h]) : 0;
   const int blk_hi = min((k_end + 15) >> 4, nblk);
-  // Q and the table slice have landed before any K/V load is issued (the
-  // compiler cannot see the direct-to-LDS loads, and would otherwise guard a
-  // later use of Q with a full vmcnt(0) that drains the K/V prefetch).
-  wait_vmcnt<0>();
+
+  // Q^T fragments for S^T = K Q^T: for k-step t the lane holds head-dim
+  // [16 t + 8 h2, +8) of the wave's row 32 h + l32.  They go through LDS:
+  // the wave's row r to tile row 16 w + r % 16 of K buffer r / 16 in the K
+  // tile layout (where the wave later stages its own key block of tiles 0-3,
+  // so no other wave writes there), and are read back like K's operands,
+  // straight into AGPRs, which the QK products read them from (copied there
+  // later, the register allocator spreads them over both register files and
+  // moves them back in every phase).
+  bf16x8 qf[2][8];
+  {
+#pragma unroll
+    for (int st = 0; st < 16; ++st) {
+      const int rr = 4 * (st & 3) + (lane >> 4);  // tile row - 16 w
+      *reinterpret_cast<__attribute__((address_space(3))) u32x4*>(
+          lds_addr(s_k[st >> 2]) + (16 * w + rr) * kRowBytes + 16 * ((lane & 15) ^ k_swz(rr))) = qv[st];
+    }
+    const int rq = l32 & 15;
+    const uint32_t qrd = lds_addr(s_k[l32 >> 4]) + (16 * w + rq) * kRowBytes;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) qf[h][t] = *lds_at<bf16x8>(qrd + 2 * h * kTileBytes + 16 * ((2 * t + h2) ^ k_swz(rq)));
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int t = 0; t < 8; ++t) asm volatile("" : "+a"(qf[h][t]));
+  }
+  // The table slice is in LDS, and every wave has its Q fragments (a wave's
+  // tile loads overwrite its Q rows).
   lds_barrier();
   // Keys at or past kv_lim are staged as zeros: past seq_len they do not
   // exist (their slots may hold anything), past the slice every row of the
@@ -258,9 +303,8 @@ attn_long_kernel(AttnArgs a) {
   const uint8_t* vpool = static_cast<const uint8_t*>(a.vpool) + static_cast<int64_t>(hk) * dh * 2;
   const int st_pos = lane & 15;
   const int st_sub = lane >> 4;
-  // A chunk past head_dim gets an offset past every descriptor's range (at
-  // most 16 rows of a few KB): it arrives as zeros.
-  constexpr uint32_t kPastRange = 0x40000000u;
+  // A chunk past head_dim gets an offset past the descriptor's range: it
+  // arrives as zeros.
   uint32_t k_src_off[4], v_src_off[4];
 #pragma unroll
   for (int st = 0; st < 4; ++st) {
