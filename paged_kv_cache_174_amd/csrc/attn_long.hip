@@ -792,7 +792,6 @@ attn_long_kernel(AttnArgs a) {
   // stores them back as whole 256-byte rows, four rows per instruction.
   const bool split = a.num_splits > 1;
   uint8_t* const reg = &s_k[0][0] + w * (kWaveRows * kRowBytes);
-  int tok_of_row[2];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
     const float lt = l[h];
@@ -812,8 +811,6 @@ attn_long_kernel(AttnArgs a) {
       const f32x2 ml = {m[h], lt};
       *reinterpret_cast<f32x2*>(a.ws_ml + (static_cast<int64_t>(z) * total_rows + orow_id) * 2) = ml;
     }
-    // Query token of the row (int32, as the start offsets are), -1 past the chunk.
-    tok_of_row[h] = valid[h] ? t0 + tok[h] : -1;
   }
   // (Partials keep 128-wide rows, the merge's layout; the output has head_dim.)
   __bf16* const dst = split ? reinterpret_cast<__bf16*>(a.ws_o) + static_cast<int64_t>(z) * total_rows * D
@@ -823,15 +820,41 @@ attn_long_kernel(AttnArgs a) {
   __builtin_amdgcn_s_waitcnt(0xC07F);  // this wave's LDS writes are done (lgkmcnt(0))
   asm volatile("" ::: "memory");
   if (!active) return;
+  // Store k carries rows 4 k + lane / 16 of the wave, 16 bytes (chunk lane %
+  // 16) per lane: all sixteen LDS reads go out first, then the sixteen
+  // stores, through a buffer descriptor based at the wave's first row, so
+  // that the per-row offsets are 32-bit and rows past the chunk (and chunks
+  // past the row) are dropped by the range check instead of a branch.
   const int c = lane & 15;
+  u32x4 ov[16];
 #pragma unroll
   for (int k = 0; k < 16; ++k) {
     const int rr = 4 * k + (lane >> 4);  // row of the wave, 0..63
-    const u32x4 v = *reinterpret_cast<const u32x4*>(reg + rr * kRowBytes + 16 * (c ^ (rr & 15)));
-    const int tk = __shfl(tok_of_row[k >> 3], rr & 31);  // rows 0..31 are half A, 32..63 half B
-    if (tk >= 0 && 8 * c < dst_row) {
-      const int hd = hk * G + (wr0 + rr - (tk - t0) * G);  // the row's query head
-      *reinterpret_cast<u32x4*>(dst + (static_cast<int64_t>(tk) * a.num_q_heads + hd) * dst_row + 8 * c) = v;
+    ov[k] = *lds_at<u32x4>(lds_addr(reg) + rr * kRowBytes + 16 * (c ^ (rr & 15)));
+  }
+  {
+    const int tok_w0 = wr0 / G;
+    const __amdgpu_buffer_rsrc_t ors = __builtin_amdgcn_make_buffer_rsrc(
+        dst + (static_cast<int64_t>(t0 + tok_w0) * a.num_q_heads + hk * G) * dst_row, 0, static_cast<int>(kPastRange),
+        kBufferWord3);
+    // The lane's row of store k is head g of its token; roff is the row's
+    // byte offset from the descriptor's base.
+    const int head_b = 2 * dst_row, tok_b = a.num_q_heads * head_b;
+    const int gr = wr0 + (lane >> 4);
+    int g = gr % G;
+    int roff = (gr / G - tok_w0) * tok_b + g * head_b;
+    const int step_g = 4 % G, step_off = (4 / G) * tok_b + step_g * head_b, wrap_off = tok_b - G * head_b;
+    const bool in_row = 16 * c < head_b;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+      const bool ok = wr0 + 4 * k + (lane >> 4) < R && in_row;
+      __builtin_amdgcn_raw_buffer_store_b128(ov[k], ors, ok ? roff + 16 * c : static_cast<int>(kPastRange), 0, 0);
+      g += step_g;
+      roff += step_off;
+      if (g >= G) {
+        g -= G;
+        roff += wrap_off;
+      }
     }
   }
 }

@@ -106,12 +106,25 @@ SMALL = [
                   num_kv_heads=2, history_lens=(100,), query_lens=(300,), full_spans=(((100, 180), (250, 400)),)),
     small_variant(CONFIGS["piecewise_gqa_bf16"], name="causal_hist_split_bf16", num_q_heads=4, num_kv_heads=2,
                   history_lens=(3000, 100), query_lens=(600, 700), full_spans=((), ((100, 500),)), sink_tokens=(0, 0), window_tokens=(1 << 30,) * 2),
+    # Long chunks with 3, 4, 6 and 8 query heads per KV head: a workgroup's and
+    # a wave's rows start mid-token and cross token boundaries in every pattern
+    # (Q is loaded and the output stored four rows at a time).
+    small_variant(CONFIGS["frame_bf16"], name="gqa3_long_bf16", num_q_heads=6, num_kv_heads=2,
+                  history_lens=(500, 40), query_lens=(150, 31), sink_tokens=(0, 0), window_tokens=(1 << 30,) * 2),
+    small_variant(CONFIGS["frame_bf16"], name="gqa4_long_bf16", num_q_heads=8, num_kv_heads=2,
+                  history_lens=(700, 0), query_lens=(77, 130), sink_tokens=(0, 0), window_tokens=(1 << 30,) * 2),
+    small_variant(CONFIGS["piecewise_gqa_bf16"], name="gqa6_long_bf16", num_q_heads=12, num_kv_heads=2,
+                  history_lens=(300,), query_lens=(53,), full_spans=(((310, 330),),)),
+    small_variant(CONFIGS["frame_bf16"], name="gqa8_long_bf16", num_q_heads=16, num_kv_heads=2,
+                  history_lens=(1000, 64), query_lens=(40, 9), sink_tokens=(0, 0), window_tokens=(1 << 30,) * 2),
 ]
 
 
 PLAN_KERNEL = {
     "tiny_f32": "f32",
     "frame_small_bf16": "long",
+    "gqa3_long_bf16": "long",
+    "gqa8_long_bf16": "long",
     "short_window_bf16": "short",
     "short_fp8_gqa": "short",
     "varlen_small_fp8": "fp8",
