@@ -204,6 +204,23 @@ def attn_bytes(geom, plan):
     return kv + qo + table
 
 
+def back_to_back_ms(stream, fn, reps, per_rep):
+    """Average duration of one launch: `reps` calls of `fn` (each `per_rep`
+    launches of the kernel measured, one after another on `stream`) between
+    two events.  Unlike an event pair around every launch, this leaves out the
+    events' own packets and the dispatch latency they expose (about 5 us per
+    launch here), and keeps the gaps between back-to-back launches."""
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    fn()
+    torch.cuda.synchronize()
+    a.record(stream)
+    for _ in range(reps):
+        fn()
+    b.record(stream)
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / (reps * per_rep)
+
+
 def write_bytes(geom):
     t = sum(geom.query_lens) * geom.num_kv_heads * geom.head_dim
     return 2 * t * (ELT[geom.q_dtype] + ELT[geom.pool_dtype]) + 8 * sum(geom.query_lens)
@@ -281,8 +298,16 @@ def run_bench(args, geom):
     def mean_gap(a, b):
         return float(np.mean([e[4 * i + a].elapsed_time(e[4 * i + b]) for e in evs for i in range(nl)]))
 
-    write_ms, main_ms, merge_ms = mean_gap(0, 1), mean_gap(1, 2), mean_gap(2, 3)
+    write_ms, main_bracketed_ms, merge_ms = mean_gap(0, 1), mean_gap(1, 2), mean_gap(2, 3)
     plan_desc = P.pkv_last_attn_plan()
+
+    def mains():
+        for li, pools, out in layers:
+            P.pkv_paged_attn_main(*attn_args(li, pools), out=out, workspace=ws, seq_order=plan.seq_order,
+                                  host_seq_lens=plan.kv_lens)
+
+    # the attention kernel's average launch, back to back over the layers
+    main_ms = back_to_back_ms(stream, mains, args.steps, nl)
     separate_ms = timed(separate_step)
 
     # whole-step timing (the number `value` is computed from): W warm-up
@@ -361,6 +386,7 @@ def run_bench(args, geom):
         "value": flops * nl / (step_ms * 1e-3) / 1e12,
         "flops": flops,
         "main_ms": main_ms,
+        "main_bracketed_ms": main_bracketed_ms,
         "merge_ms": merge_ms,
         "achieved_tflops": flops / (main_ms * 1e-3) / 1e12,
         "attn_bytes": abytes,
@@ -419,8 +445,21 @@ def run_config(geom, steps, warmup):
             ev[k + 2].record(stream)
             k += 3
     torch.cuda.synchronize()
-    main_ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(0, k, 3)]))
+    main_bracketed_ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(0, k, 3)]))
     merge_ms = float(np.mean([ev[i + 1].elapsed_time(ev[i + 2]) for i in range(0, k, 3)]))
+
+    def mains(merge):
+        for li, pools, out in layers:
+            P.pkv_paged_attn_main(*attn_args(li, pools), out=out, workspace=ws, seq_order=plan.seq_order,
+                                  host_seq_lens=plan.kv_lens)
+            if merge:
+                P.pkv_paged_attn_merge(*attn_args(li, pools), out=out, workspace=ws, seq_order=plan.seq_order,
+                                       host_seq_lens=plan.kv_lens)
+
+    # average launches, back to back over the layers: the kernel alone, and
+    # the kernel with its merge
+    main_ms = back_to_back_ms(stream, lambda: mains(False), steps, nl)
+    call_ms = back_to_back_ms(stream, lambda: mains(True), steps, nl)
     for _ in range(warmup):
         step()
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
@@ -433,7 +472,6 @@ def run_config(geom, steps, warmup):
     step_ms = a.elapsed_time(b) / steps
     flops = plan.attn_flops(geom.num_q_heads, geom.head_dim)
     abytes = attn_bytes(geom, plan)
-    call_ms = main_ms + merge_ms
     bound_ms = max(flops / (PEAK_BF16_TFLOPS * 1e12), abytes / (PEAK_HBM_GBPS * 1e9)) * 1e3
     res = {
         "layers": nl,
@@ -441,7 +479,8 @@ def run_config(geom, steps, warmup):
         "tflops": round(flops * nl / (step_ms * 1e-3) / 1e12, 2),
         "attn_call_ms": round(call_ms, 5),
         "attn_main_ms": round(main_ms, 5),
-        "attn_merge_ms": round(merge_ms, 5),
+        "attn_main_ms_bracketed": round(main_bracketed_ms, 5),
+        "attn_merge_ms_bracketed": round(merge_ms, 5),
         "attn_tflops": round(flops / (call_ms * 1e-3) / 1e12, 2),
         "attn_frac_of_bf16_peak": round(flops / (call_ms * 1e-3) / 1e12 / PEAK_BF16_TFLOPS, 4),
         "main_tflops": round(flops / (main_ms * 1e-3) / 1e12, 2),
@@ -579,8 +618,22 @@ def run_kv_bound(args):
             k += 3
     torch.cuda.synchronize()
     plan_desc = P.pkv_last_attn_plan()
-    ms = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 3)]))
-    call_ms = float(np.mean([ev[i].elapsed_time(ev[i + 2]) for i in range(0, len(ev), 3)]))
+    ms_bracketed = float(np.mean([ev[i].elapsed_time(ev[i + 1]) for i in range(0, len(ev), 3)]))
+    call_ms_bracketed = float(np.mean([ev[i].elapsed_time(ev[i + 2]) for i in range(0, len(ev), 3)]))
+
+    def calls(merge):
+        for layer in layers:
+            launch(*layer)
+            if merge:
+                P.pkv_paged_attn_merge(layer[0].q, layer[1], plan.block_table, plan.query_start_loc,
+                                       plan.seq_lens, plan.segments, plan.segment_start_loc, scale,
+                                       plan.max_query_len, plan.max_seq_len, out=layer[2], workspace=ws,
+                                       seq_order=plan.seq_order, host_seq_lens=plan.kv_lens)
+
+    # average launches, back to back over the rotating pools: the kernel
+    # alone, and the kernel with its merge (the figure `achieved` is from)
+    ms = back_to_back_ms(stream, lambda: calls(False), n, len(layers))
+    call_ms = back_to_back_ms(stream, lambda: calls(True), n, len(layers))
     abytes = attn_bytes(geom, plan)
     flops = plan.attn_flops(geom.num_q_heads, geom.head_dim)
     gbps = abytes / (call_ms * 1e-3) / 1e9
@@ -596,8 +649,10 @@ def run_kv_bound(args):
         "frac": round(gbps / PEAK_HBM_GBPS, 4),
         "bytes_per_call": abytes,
         "avg_call_ms": round(call_ms, 5),
+        "avg_call_ms_bracketed": round(call_ms_bracketed, 5),
         "main_only": {"avg_launch_ms": round(ms, 5), "gbps": round(main_gbps, 1),
-                      "frac": round(main_gbps / PEAK_HBM_GBPS, 4)},
+                      "frac": round(main_gbps / PEAK_HBM_GBPS, 4),
+                      "avg_launch_ms_bracketed": round(ms_bracketed, 5)},
         "tflops": round(flops / (call_ms * 1e-3) / 1e12, 2),
         "rotating_pools": len(layers),
         "seq_lens": [int(x) for x in plan.kv_lens],
@@ -780,6 +835,7 @@ def main():
             "plan": r["plan_desc"],
             "flop_per_launch": r["flops"],
             "avg_launch_ms": round(r["main_ms"], 5),
+            "avg_launch_ms_bracketed": round(r["main_bracketed_ms"], 5),
             "shader_clock": r["clock"],
             "frac_of_peak_at_clock": (round(r["achieved_tflops"] / (PEAK_BF16_TFLOPS * r["clock"]["median_mhz"] / 2400.0), 4)
                                       if r["clock"] else None),
@@ -796,7 +852,7 @@ def main():
         "parts": {
             "paged_write": {"ms": round(r["write_ms"], 5), "gbps": round(r["write_gbps"], 1)},
             "split_merge_ms": round(r["merge_ms"], 5),
-            "paged_attn_call_ms": round(r["main_ms"] + r["merge_ms"], 5),
+            "paged_attn_call_ms": round(r["main_bracketed_ms"] + r["merge_ms"], 5),
             "gather_whole_window": {"ms": round(r["gather_ms"], 5), "gbps": round(r["gather_gbps"], 1)},
             "attn_over_staged_buffer_ms": round(r["staged_attn_ms"], 5),
             "separate_calls_step_ms": round(r["separate_ms"], 5),
