@@ -6,7 +6,8 @@
 //   major, so the G = Hq / Hkv heads that share a K/V tile are computed from
 //   one LDS copy of it (GQA).  A workgroup of four waves -- one per SIMD --
 //   owns 256 consecutive rows of one (sequence, KV head) and, when the key
-//   range is split, one range of keys.  Each wave owns 64 rows as two halves
+//   range is split, one range of keys (the host's split_cut; the ranges may
+//   differ in length, longest first).  Each wave owns 64 rows as two halves
 //   A and B of 32 rows, each one column block of the 32x32x16 bf16 MFMA.
 //
 // Why one wave per SIMD, two halves per wave
@@ -111,13 +112,19 @@ attn_long_kernel(AttnArgs a) {
   // ---- work item.  Workgroups are dealt to the 8 XCDs round-robin by id;
   // all workgroups of one (sequence, KV head) go to one XCD (they share its
   // L2 for the group's K/V), and consecutive groups to different XCDs.
+  // Inside an XCD the items go out split by split -- every group's split 0,
+  // then split 1, ... -- and within a split from the last row tile to the
+  // first.  Split lengths never increase with z, and a later row tile never
+  // sees fewer keys than an earlier one, so the longest items go first and the
+  // short ones fill in behind them.
   const uint32_t xcd = blockIdx.x & 7u, pos = blockIdx.x >> 3;
-  const uint32_t per_group = static_cast<uint32_t>(a.num_splits) * static_cast<uint32_t>(a.row_tiles);
-  const uint32_t grp = xcd + 8u * (pos / per_group);
-  if (grp >= static_cast<uint32_t>(a.num_seqs) * static_cast<uint32_t>(a.num_kv_heads)) return;
-  const uint32_t item = pos % per_group;
-  const int rt = static_cast<int>(item % static_cast<uint32_t>(a.row_tiles));
-  const int z = static_cast<int>(item / static_cast<uint32_t>(a.row_tiles));
+  const uint32_t groups = static_cast<uint32_t>(a.num_seqs) * static_cast<uint32_t>(a.num_kv_heads);
+  const uint32_t per_split = (groups + 7u) / 8u * static_cast<uint32_t>(a.row_tiles);
+  const int z = static_cast<int>(pos / per_split);
+  const uint32_t rem = pos % per_split;
+  const uint32_t grp = xcd + 8u * (rem / static_cast<uint32_t>(a.row_tiles));
+  if (grp >= groups) return;
+  const int rt = a.row_tiles - 1 - static_cast<int>(rem % static_cast<uint32_t>(a.row_tiles));
   const int hk = static_cast<int>(grp % static_cast<uint32_t>(a.num_kv_heads));
   const int b_pos = static_cast<int>(grp / static_cast<uint32_t>(a.num_kv_heads));
   // ---- the workgroup's sequence and its metadata, in as few dependent
@@ -185,10 +192,10 @@ attn_long_kernel(AttnArgs a) {
   if (r0 >= R) return;
   // Round 2.  Block-table slice (no table: the K/V buffers are one
   // contiguous run, logical block i is block i).
-  const int k_begin = z * a.split_len;
+  const int k_begin = a.split_cut[z], k_stop = a.split_cut[z + 1];
   const int nblk = (s + 15) >> 4;
   const int blk_lo = k_begin >> 4;
-  const int blk_cap = min(min((k_begin + a.split_len + 15) >> 4, nblk), blk_lo + kTableSlice);
+  const int blk_cap = min(min((k_stop + 15) >> 4, nblk), blk_lo + kTableSlice);
   const int32_t* const table = a.block_table ? a.block_table + static_cast<int64_t>(b) * a.table_width : nullptr;
   const int tid = static_cast<int>(threadIdx.x);
   int te = blk_lo + tid;
@@ -238,7 +245,7 @@ attn_long_kernel(AttnArgs a) {
   // check enforces it), so the tile's last row bounds the workgroup's keys
   // and a wave's first row its mask-free prefix.
   const int wg_kmax = row_limit(segc, a.segments, seg0, seg1, gbase + (min(r0 + kMfmaRows, R) - 1) / G);
-  const int k_end = min(k_begin + a.split_len, wg_kmax);
+  const int k_end = min(k_stop, wg_kmax);
   const int64_t total_rows = a.num_q_tokens * a.num_q_heads;
   if (k_begin >= k_end) {
     // No key of this split is visible to any row of the tile: its partial is

@@ -22,7 +22,7 @@ namespace pkv {
 
 namespace {
 thread_local char g_error[1024] = "";
-thread_local char g_plan[160] = "";
+thread_local char g_plan[256] = "";
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxDevices = 64;
 int g_cu_count[kMaxDevices] = {0};
@@ -67,6 +67,9 @@ struct SplitPlan {
   int split_len;
   bool short_rows;  // the short-query kernel (at most kShortRows rows per KV head)
   bool packed;      // short rows: the launch hands out real work first (see plan_short_packed)
+  // Long bf16 kernel: 64-key tiles of each split, non-increasing (the last
+  // split also runs on to max_seq_len).  Other kernels: split_len keys each.
+  int tiles[kMaxSplits];
 };
 
 // Number of key splits for the MFMA kernel.  One workgroup occupies a CU, so
@@ -120,12 +123,113 @@ bool plan_short_packed(SplitPlan& p, int64_t num_q_tokens, int num_q_heads, int 
   p.split_len = best_l;
   p.splits = (max_seq_len + best_l - 1) / best_l;
   p.packed = p.splits > 1;
+  for (int z = 0; z < p.splits && z < kMaxSplits; ++z) p.tiles[z] = best_l / kMfmaKeyTile;
   return true;
 }
 
-SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, int num_seqs, int max_query_len,
-                      int max_seq_len, size_t workspace_bytes, bool have_workspace, const int32_t* host_lens = nullptr,
-                      int kv_elem_bytes = 2) {
+// The long bf16 kernel's launch, modelled.  XCD x runs the workgroups of the
+// (sequence, KV head) groups x, x + 8, ..., split by split (see the kernel's
+// work mapping).  A workgroup costs a fixed start-up and epilogue plus a time
+// per 64-key tile (6 us and 1.5 us at the sustained clock, fitted to launches
+// of the frame and 40-layer workloads).  How the XCD hands workgroups to its
+// CUs is not documented, and measurements fit neither of two simple rules on
+// every plan: the next workgroup to the first CU to come free, or workgroups
+// dealt in turn to four groups of CUs, each taking its next one on its first
+// free CU.  The model takes the later of the two finishing times, which ranked
+// every measured plan in the right order.  Returns the busiest XCD's time.
+double model_long_launch(const int* tiles, int splits, int64_t groups_per_xcd, int row_tiles, int cus_per_xcd) {
+  constexpr double kTile = 1.5e-6, kWorkgroup = 6e-6;
+  constexpr int kCuGroups = 4;
+  const int cus = std::max(kCuGroups, cus_per_xcd);
+  auto later = [](double x, double y) { return x > y; };
+  std::vector<double> any(static_cast<size_t>(cus), 0.0);  // min-heaps of CU free times
+  std::vector<std::vector<double>> dealt(kCuGroups, std::vector<double>(static_cast<size_t>(cus / kCuGroups), 0.0));
+  auto take = [&](std::vector<double>& h, double cost) {
+    std::pop_heap(h.begin(), h.end(), later);
+    h.back() += cost;
+    std::push_heap(h.begin(), h.end(), later);
+  };
+  const int64_t per_split = groups_per_xcd * row_tiles;
+  int64_t i = 0;
+  for (int z = 0; z < splits; ++z) {
+    const double cost = tiles[z] * kTile + kWorkgroup;
+    for (int64_t k = 0; k < per_split; ++k, ++i) {
+      take(any, cost);
+      take(dealt[static_cast<size_t>(i % kCuGroups)], cost);
+    }
+  }
+  double t = *std::max_element(any.begin(), any.end());
+  for (const auto& h : dealt) t = std::max(t, *std::max_element(h.begin(), h.end()));
+  return t;
+}
+
+// Key splits of the long bf16 kernel.  Candidates: for each split count, the
+// first splits of A tiles each and a last one of the remaining tiles (1 to A),
+// so that the short last split's workgroups fill in where the launch's last
+// round would leave CUs idle.  Each is scored by model_long_launch plus the
+// partials' round trip; a split must buy a clear gain.  plan_len is the
+// longest sequence (the host lengths when given, else max_seq_len); the last
+// split runs on to max_seq_len, and no split may span more keys than a
+// workgroup's block-table slice holds.
+void plan_long_splits(SplitPlan& p, int64_t num_q_tokens, int num_q_heads, int num_kv_heads, int num_seqs,
+                      int max_seq_len, int plan_len, size_t workspace_bytes, bool have_workspace) {
+  const int cus = cu_count();
+  const int64_t groups_per_xcd = (static_cast<int64_t>(num_seqs) * num_kv_heads + 7) / 8;
+  const int64_t per_split_bytes = num_q_tokens * num_q_heads * kPartialRowBytes;
+  constexpr double kPartialBw = 5.0e12;    // B/s for writing and re-reading the partials
+  constexpr double kCombineLaunch = 3e-6;  // s
+  const int T = (plan_len + kMfmaKeyTile - 1) / kMfmaKeyTile;
+  const int max_sp = std::max(1, std::min(kMaxSplits, std::min(T, plan_len / 512)));
+  double best_t = 1e30;
+  int best_sp = 0, best_a = T;
+  for (int sp = 1; sp <= max_sp; ++sp) {
+    if (sp > 1 && (!have_workspace || workspace_bytes < static_cast<size_t>(per_split_bytes) * sp)) break;
+    const int a_lo = (T + sp - 1) / sp, a_hi = sp == 1 ? T : (T - 1) / (sp - 1);
+    const int step = std::max(1, (a_hi - a_lo) / 24);
+    for (int A = a_lo; A <= a_hi; A += step) {
+      int tiles[kMaxSplits];
+      for (int z = 0; z + 1 < sp; ++z) tiles[z] = A;
+      tiles[sp - 1] = T - (sp - 1) * A;
+      if (tiles[sp - 1] < 1 || tiles[sp - 1] > A) continue;
+      // The last split's range, [cut, max_seq_len), must fit the table slice.
+      if (max_seq_len - (sp - 1) * A * kMfmaKeyTile > kMaxSplitKeys || A * kMfmaKeyTile > kMaxSplitKeys) continue;
+      double t = model_long_launch(tiles, sp, groups_per_xcd, p.row_tiles, cus / 8);
+      if (sp > 1) t += 2.0 * per_split_bytes * sp / kPartialBw + kCombineLaunch;
+      if (t < best_t * (sp > best_sp ? 0.98 : 1.0) || best_sp == 0) {
+        best_t = t;
+        best_sp = sp;
+        best_a = A;
+      }
+    }
+  }
+  if (best_sp == 0) {  // nothing fits the table slice: equal splits of at most kMaxSplitKeys
+    best_sp = std::min(kMaxSplits, (max_seq_len + kMaxSplitKeys - 1) / kMaxSplitKeys);
+    best_a = ((max_seq_len + best_sp - 1) / best_sp + kMfmaKeyTile - 1) / kMfmaKeyTile;
+  }
+  p.splits = best_sp;
+  for (int z = 0; z < best_sp; ++z) p.tiles[z] = z + 1 < best_sp ? best_a : std::max(1, T - (best_sp - 1) * best_a);
+  p.split_len = best_a * kMfmaKeyTile;
+}
+
+// Plans are cached per thread (the same metadata serves every layer of a
+// step, and the long kernel's search is not free).
+struct PlanKey {
+  int64_t num_q_tokens;
+  int num_q_heads, num_kv_heads, num_seqs, max_query_len, max_seq_len, plan_len, kv_elem_bytes, cus;
+  int64_t host_hash;
+  size_t workspace_bytes;
+  bool have_workspace;
+  bool operator==(const PlanKey& o) const {
+    return num_q_tokens == o.num_q_tokens && num_q_heads == o.num_q_heads && num_kv_heads == o.num_kv_heads &&
+           num_seqs == o.num_seqs && max_query_len == o.max_query_len && max_seq_len == o.max_seq_len &&
+           plan_len == o.plan_len && kv_elem_bytes == o.kv_elem_bytes && cus == o.cus && host_hash == o.host_hash &&
+           workspace_bytes == o.workspace_bytes && have_workspace == o.have_workspace;
+  }
+};
+
+SplitPlan plan_splits_uncached(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, int num_seqs,
+                               int max_query_len, int max_seq_len, size_t workspace_bytes, bool have_workspace,
+                               const int32_t* host_lens, int kv_elem_bytes, int plan_len) {
   SplitPlan p{};
   const int group = num_q_heads / num_kv_heads;
   p.short_rows = static_cast<int64_t>(max_query_len) * group <= kShortRows;
@@ -133,6 +237,11 @@ SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, i
   if (p.short_rows && plan_short_packed(p, num_q_tokens, num_q_heads, num_kv_heads, num_seqs, max_seq_len, host_lens,
                                         workspace_bytes, have_workspace, kv_elem_bytes))
     return p;
+  if (!p.short_rows && kv_elem_bytes == 2) {
+    plan_long_splits(p, num_q_tokens, num_q_heads, num_kv_heads, num_seqs, max_seq_len, plan_len, workspace_bytes,
+                     have_workspace);
+    return p;
+  }
   const int64_t base = static_cast<int64_t>(num_seqs) * num_kv_heads * p.row_tiles;
   const int cus = cu_count();
   const int max_by_len = std::max(1, max_seq_len / 512);
@@ -163,6 +272,51 @@ SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, i
   const int per = (max_seq_len + best - 1) / best;
   p.split_len = ((per + kMfmaKeyTile - 1) / kMfmaKeyTile) * kMfmaKeyTile;
   if (p.split_len <= 0) p.split_len = kMfmaKeyTile;
+  for (int z = 0; z < p.splits && z < kMaxSplits; ++z) p.tiles[z] = p.split_len / kMfmaKeyTile;
+  return p;
+}
+
+SplitPlan plan_splits(int64_t num_q_tokens, int num_q_heads, int num_kv_heads, int num_seqs, int max_query_len,
+                      int max_seq_len, size_t workspace_bytes, bool have_workspace, const int32_t* host_lens = nullptr,
+                      int kv_elem_bytes = 2) {
+  PlanKey k{};
+  k.num_q_tokens = num_q_tokens;
+  k.num_q_heads = num_q_heads;
+  k.num_kv_heads = num_kv_heads;
+  k.num_seqs = num_seqs;
+  k.max_query_len = max_query_len;
+  k.max_seq_len = max_seq_len;
+  k.kv_elem_bytes = kv_elem_bytes;
+  k.cus = cu_count();
+  k.workspace_bytes = workspace_bytes;
+  k.have_workspace = have_workspace;
+  // The long kernel plans from the longest sequence; the short kernel's packing
+  // uses every length.
+  int plan_len = max_seq_len;
+  if (host_lens) {
+    int longest = 1;
+    uint64_t h = 1469598103934665603ull;
+    for (int b = 0; b < num_seqs; ++b) {
+      longest = std::max(longest, host_lens[b]);
+      h = (h ^ static_cast<uint32_t>(host_lens[b])) * 1099511628211ull;
+    }
+    plan_len = std::min(longest, max_seq_len);
+    k.host_hash = static_cast<int64_t>(h);
+  }
+  k.plan_len = plan_len;
+  constexpr int kCache = 8;
+  thread_local PlanKey keys[kCache];
+  thread_local SplitPlan plans[kCache];
+  thread_local int used = 0, next = 0;
+  for (int i = 0; i < used; ++i)
+    if (keys[i] == k) return plans[i];
+  const SplitPlan p = plan_splits_uncached(num_q_tokens, num_q_heads, num_kv_heads, num_seqs, max_query_len,
+                                           max_seq_len, workspace_bytes, have_workspace, host_lens, kv_elem_bytes,
+                                           plan_len);
+  keys[next] = k;
+  plans[next] = p;
+  next = (next + 1) % kCache;
+  used = std::min(used + 1, kCache);
   return p;
 }
 
@@ -394,7 +548,8 @@ int attn_setup(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num
     a.num_splits = 1;
     a.row_tiles = 0;
     a.split_len = 0;
-    L.p = SplitPlan{0, 1, 0, false};
+    L.p = SplitPlan{};
+    L.p.splits = 1;
     std::snprintf(g_plan, sizeof(g_plan), "f32");
     return PKV_OK;
   }
@@ -415,9 +570,20 @@ int attn_setup(const void* q, int32_t q_dtype, int64_t num_q_tokens, int32_t num
   a.num_splits = p.splits;
   a.split_len = p.split_len;
   a.packed = p.packed ? 1 : 0;
+  for (int z = 0, cut = 0; z <= p.splits; ++z) {
+    a.split_cut[z] = z == p.splits ? max_seq_len : std::min(cut, max_seq_len);
+    if (z < p.splits) cut += p.tiles[z] * kMfmaKeyTile;
+  }
   std::snprintf(g_plan, sizeof(g_plan), "%s splits=%d split_len=%d row_tiles=%d packed=%d",
                 !L.fp8 && !p.short_rows ? "long" : p.short_rows ? "short" : "fp8", p.splits, p.split_len,
                 p.row_tiles, p.packed ? 1 : 0);
+  if (!L.fp8 && !p.short_rows && p.splits > 1) {
+    for (int z = 1; z < p.splits; ++z) {
+      const size_t n = std::strlen(g_plan);
+      if (n + 16 >= sizeof(g_plan)) break;
+      std::snprintf(g_plan + n, sizeof(g_plan) - n, z > 1 ? ",%d" : " cut=%d", a.split_cut[z]);
+    }
+  }
   if (p.splits > 1) {
     const int64_t rows = num_q_tokens * num_q_heads;
     a.ws_o = static_cast<float*>(workspace);

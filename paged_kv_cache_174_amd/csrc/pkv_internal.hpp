@@ -58,6 +58,12 @@ hipError_t launch_gather(const GatherArgs& a, hipStream_t s);
 
 // ----------------------------------------------------------------- attention
 
+// Rows (query token x query head of one KV group) one MFMA workgroup covers.
+constexpr int kMfmaRows = 256;
+constexpr int kMfmaKeyTile = 64;
+// Most key splits one attention call uses (the combine kernel holds one partial per split in registers).
+constexpr int kMaxSplits = 16;
+
 struct AttnArgs {
   const void* q;
   void* out;
@@ -82,17 +88,16 @@ struct AttnArgs {
   int32_t block_size;
   int32_t row_tiles;  // query-row tiles per (sequence, KV head)
   int32_t num_splits;
-  int32_t split_len;  // keys per split, a multiple of the key tile
+  int32_t split_len;  // keys per split, a multiple of the key tile (fp8 and short-row kernels)
+  // Long bf16 kernel: split z covers keys [split_cut[z], split_cut[z + 1]);
+  // the cuts are multiples of the key tile except the last, which is
+  // max_seq_len, and the lengths never increase with z.
+  int32_t split_cut[kMaxSplits + 1];
   int32_t packed;     // short rows: workgroups take the non-empty key ranges first
   float scale_log2;   // softmax_scale * k_scale * log2(e)
   float v_scale;
 };
 
-// Rows (query token x query head of one KV group) one MFMA workgroup covers.
-constexpr int kMfmaRows = 256;
-constexpr int kMfmaKeyTile = 64;
-// Most key splits one attention call uses (the combine kernel holds one partial per split in registers).
-constexpr int kMaxSplits = 16;
 // Block-table entries one MFMA workgroup stages in LDS, so one key split spans at most
 // kTableSlice * 16 keys (minus one block for a split that starts mid-block).
 constexpr int kTableSlice = 4096;
