@@ -169,9 +169,13 @@ def setup(geom, device="cuda"):
     from workloads import make_workload
 
     wl = make_workload(geom, device=device)
+    # AR workloads with a sliding window get P1 build_block_table's fixed-shape
+    # metadata (table width and max_seq_len at the window's capacity); the
+    # real lengths go to the library as its planning hint.
+    windowed = max(geom.window_tokens) < (1 << 29)
     plan = P.ForwardPlan.build(
         wl.block_ids, geom.history_lens, geom.query_lens, geom.sink_tokens, geom.window_tokens,
-        geom.full_spans, geom.causal_default, geom.block_size, device=device,
+        geom.full_spans, geom.causal_default, geom.block_size, device=device, fixed_capacity=windowed,
     )
     plan.validate(geom.pool_blocks())
     rows = geom.pool_blocks() * geom.block_size

@@ -381,6 +381,24 @@ int pkv_action_table(int32_t* table, int32_t capacity, int32_t* count, int32_t* 
                      int32_t block_size);
 
 /*
+ * Fixed table capacity (P1 ARDiffusionPagedForwardContext.max_video_blocks
+ * and build_block_table): the most table entries a visible window can span,
+ * plus the action scratch blocks, so that the block table keeps one width and
+ * max_seq_len one value (capacity * block_size) while the window fills.  The
+ * sink [0, sink_tokens) and the recent window_tokens are rounded up to blocks
+ * separately (each can straddle a block edge on its own); the recent range
+ * starts at a whole number of chunks, so at most
+ * block_size - gcd(chunk_size, block_size) tokens past a block edge, and
+ * needs ceil((window_tokens + that) / block_size) blocks.  Action scratch
+ * takes max(1, ceil(action_tokens / block_size)) blocks (P1 keeps one even
+ * without actions).  *out_blocks receives the total.
+ * Errors: PKV_EINVAL for block_size or chunk_size <= 0, negative token counts,
+ * or a NULL out_blocks.
+ */
+int pkv_window_capacity(int64_t sink_tokens, int64_t window_tokens, int32_t chunk_size, int32_t block_size,
+                        int64_t action_tokens, int64_t* out_blocks);
+
+/*
  * Piecewise segments (P3 build_segments): full_spans (host, [num_spans][2],
  * half-open, key coordinates, sorted and disjoint) are clipped to the query
  * range [query_offset, query_offset + query_len); rows before a clipped span

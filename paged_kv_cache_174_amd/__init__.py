@@ -34,6 +34,7 @@ from ._lib import (  # noqa: F401
     pkv_slot_mapping,
     pkv_validate_metadata_host,
     pkv_version,
+    pkv_window_capacity,
     pkv_window_table,
 )
 from .plan import ForwardPlan, HistoryStaging, StagingDecision  # noqa: F401

@@ -154,6 +154,10 @@ _SIGNATURES = {
     "pkv_wm_info": (ctypes.c_int, [_P, _I32, _PI64]),
     "pkv_wm_block_table": (ctypes.c_int, [_P, _I32, _PI32, _I32, _PI32]),
     "pkv_last_error": (ctypes.c_char_p, []),
+    "pkv_window_capacity": (
+        ctypes.c_int,
+        [ctypes.c_int64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64)],
+    ),
     "pkv_last_attn_plan": (ctypes.c_char_p, []),
     "pkv_probe_mfma": (ctypes.c_int, [ctypes.c_int64, _P, ctypes.c_int64, ctypes.POINTER(ctypes.c_int64), _P]),
     "pkv_probe_stream": (ctypes.c_int, [_P, ctypes.c_int64, _P, _P]),
@@ -564,6 +568,13 @@ def pkv_window_table(block_ids, history_tokens, query_tokens, sink_tokens, windo
         )
     )
     return table[: count.value].copy(), int(kv_len.value)
+
+
+def pkv_window_capacity(sink_tokens, window_tokens, chunk_size, block_size=16, action_tokens=0) -> int:
+    out = ctypes.c_int64(0)
+    _check(lib().pkv_window_capacity(int(sink_tokens), int(window_tokens), int(chunk_size), int(block_size),
+                                     int(action_tokens), ctypes.byref(out)))
+    return int(out.value)
 
 
 def pkv_build_segments(full_spans, query_offset: int, query_len: int) -> np.ndarray:

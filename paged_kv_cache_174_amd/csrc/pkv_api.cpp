@@ -799,6 +799,26 @@ int pkv_action_table(int32_t* table, int32_t capacity, int32_t* count, int32_t* 
   return PKV_OK;
 }
 
+int pkv_window_capacity(int64_t sink_tokens, int64_t window_tokens, int32_t chunk_size, int32_t block_size,
+                        int64_t action_tokens, int64_t* out_blocks) {
+  g_error[0] = '\0';
+  if (!out_blocks) return fail(PKV_EINVAL, "NULL pointer");
+  if (block_size <= 0 || chunk_size <= 0 || sink_tokens < 0 || window_tokens < 0 || action_tokens < 0)
+    return fail(PKV_EINVAL, "bad sizes");
+  int64_t g = chunk_size, r = block_size;  // gcd(chunk_size, block_size)
+  while (r) {
+    const int64_t t = g % r;
+    g = r;
+    r = t;
+  }
+  const int64_t lead = block_size - g;  // furthest a chunk boundary sits past a block edge
+  const int64_t sink_blocks = (sink_tokens + block_size - 1) / block_size;
+  const int64_t recent_blocks = (window_tokens + lead + block_size - 1) / block_size;
+  const int64_t action_blocks = std::max<int64_t>(1, (action_tokens + block_size - 1) / block_size);
+  *out_blocks = sink_blocks + recent_blocks + action_blocks;
+  return PKV_OK;
+}
+
 int pkv_build_segments(const int32_t* full_spans, int32_t num_spans, int32_t query_offset, int32_t query_len,
                        int32_t* out_segments, int32_t capacity, int32_t* out_count) {
   g_error[0] = '\0';

@@ -80,12 +80,21 @@ class ForwardPlan:
         device=None,
         action_lens=None,
         action_block_ids=None,
+        fixed_capacity: bool = False,
     ) -> "ForwardPlan":
         """``query_lens`` are the current video chunks.  With ``action_lens``
         (per sequence) and ``action_block_ids`` (each sequence's scratch
         blocks), the action K/V is listed after the window and the query of a
         sequence is its video chunk followed by its action tokens (P1
-        build_block_table, P2 action tests)."""
+        build_block_table, P2 action tests).
+
+        ``fixed_capacity`` sizes the metadata as P1 ``build_block_table`` does:
+        the table width is the window's capacity in blocks (pkv_window_capacity:
+        sink and recent range rounded separately, plus the action scratch) and
+        ``max_seq_len`` that capacity in tokens, so both stay constant while the
+        window fills; the real lengths go to the library as its planning hint
+        (``kv_lens``).  Otherwise the width is the longest table and
+        ``max_seq_len`` the longest sequence."""
         n = len(query_lens)
         acts = [0] * n if action_lens is None else [int(a) for a in action_lens]
         tables, kv_lens, segs, seg_start = [], [], [], [0]
@@ -109,6 +118,14 @@ class ForwardPlan:
             segs.append(sg)
             seg_start.append(seg_start[-1] + len(sg))
         rows_per_seq = [int(q) + a for q, a in zip(query_lens, acts)]
+        if fixed_capacity:
+            caps = [L.pkv_window_capacity(sink_tokens[b], window_tokens[b], query_lens[b], block_size, acts[b])
+                    for b in range(n)]
+            width = max(max(caps), max(len(t) for t in tables))
+            if table_width is None:
+                table_width = width
+            if max_seq_len is None:
+                max_seq_len = max(caps) * block_size
         width = max(len(t) for t in tables) if table_width is None else int(table_width)
         bt = np.zeros((n, width), dtype=np.int32)  # tail padding with block 0, never read
         for b, t in enumerate(tables):

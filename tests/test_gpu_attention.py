@@ -65,8 +65,8 @@ SMALL = [
                   history_lens=(128,), query_lens=(64,), sink_tokens=(0,), window_tokens=(1 << 30,),
                   full_spans=(None,)),
     # Long causal chunks: the key range is split, and early row tiles see fewer
-    # keys than one split holds (one split writes the output alone) while later
-    # ones span several splits (merged by the last split to finish).
+    # keys than one split holds (later splits are empty for them) while later
+    # ones span several splits (merged by the separate merge launch).
     small_variant(CONFIGS["piecewise_gqa_bf16"], name="causal_long_split_bf16", num_q_heads=2, num_kv_heads=2,
                   history_lens=(0,), query_lens=(1200,), full_spans=((),)),
     # Short query chunks (at most 64 rows per KV head): the kernel that splits
@@ -245,25 +245,29 @@ def test_ar_step_layers_sampled():
         del pools, out
 
 
-def test_ar_step_fused_call_all_heads_at_tile_edges():
-    """One layer of the 40-layer step through the fused per-layer call
-    (pkv_paged_write_attn: the current chunk's slot writes, then attention
-    and the merge of its key splits) at full size: every one of the 40 query
-    heads, on rows at each 256-row tile edge of both sequences (the last tile
-    holds the 24-row tail), the first and last rows, and random ones.  Every
-    row here sees all 9360 keys, so each one spans every key split."""
-    geom = CONFIGS["ar_step_40L_bf16"]
+@pytest.mark.parametrize("name,layer,capacity", [("ar_step_40L_bf16", 7, 587), ("frame_bf16", 0, 392)])
+def test_fused_call_all_heads_at_tile_edges(name, layer, capacity):
+    """One layer of the 40-layer step, and the frame layer, through the fused
+    per-layer call (pkv_paged_write_attn: the current chunk's slot writes,
+    then attention and the merge of its key splits) at full size and with the
+    metadata P1 build_block_table passes (table width and max_seq_len fixed
+    at the window's capacity; the bench times the same): every query head, on
+    rows at each 256-row tile edge of both sequences (the last tile holds the
+    24-row tail), the first and last rows, and random ones.  Every row here
+    sees all keys, so each one spans every key split."""
+    geom = CONFIGS[name]
     wl = make_workload(geom, device="cuda")
-    plan = G.make_plan(wl)
-    li = wl.layer(7)
+    plan = G.make_plan(wl, fixed_capacity=True)
+    assert plan.block_table.shape[1] == capacity and plan.max_seq_len == 16 * capacity
+    li = wl.layer(layer)
     pools = G.make_pools(geom, li)
     G.P.pkv_paged_write(li.k_hist, li.v_hist, plan.history_slot_mapping, pools)
-    G.say("fused call", geom.name, "layer 7")
+    G.say("fused call", geom.name, "layer", layer)
     out = G.write_attend(plan, pools, li, geom)
     torch.cuda.synchronize()
     assert G.workspace_for(plan, geom) is not None  # the keys are split
     qsl = np.concatenate([[0], np.cumsum(geom.query_lens)])
-    rng = np.random.default_rng(7)
+    rng = np.random.default_rng(layer)
     rows = set()
     for b in range(geom.num_seqs):
         lo, hi = int(qsl[b]), int(qsl[b + 1])

@@ -75,6 +75,36 @@ def test_fused_call_matches_oracle(geom):
     _err(geom, out, ref)
 
 
+CAPACITY = [
+    small_variant(CONFIGS["frame_bf16"], name="bf16_actions_windowed", num_q_heads=4, num_kv_heads=2,
+                  history_lens=(64, 96), query_lens=(32, 48), sink_tokens=(16, 0), window_tokens=(64, 144),
+                  action_lens=(3, 17)),
+    FUSED[3],
+]
+
+
+@pytest.mark.parametrize("geom", CAPACITY, ids=[g.name for g in CAPACITY])
+def test_fused_call_with_fixed_capacity_metadata(geom):
+    """P1 build_block_table's fixed-shape metadata: the table padded with block
+    0 to the window's capacity and max_seq_len that capacity, larger than
+    every sequence; the kernels read only ceil(seq_len / 16) entries and the
+    planner works from the real lengths, so the result is the oracle's."""
+    wl = make_workload(geom, device="cuda")
+    li = wl.layer(0)
+    plan = G.make_plan(wl, fixed_capacity=True)
+    width = plan.block_table.shape[1]
+    assert plan.max_seq_len == 16 * width > max(plan.kv_lens) and min(len(t) for t in plan.tables) < width
+    pools = G.make_pools(geom, li)
+    G.say("fused fixed capacity", geom.name)
+    if li.k_hist.shape[0]:
+        G.P.pkv_paged_write(li.k_hist, li.v_hist, plan.history_slot_mapping, pools)
+    out = G.write_attend(plan, pools, li, geom)
+    torch.cuda.synchronize()
+    _, k_ref, v_ref, ref = H.run_layer(wl, li=li)
+    assert G.bits_equal(pools.key, k_ref) and G.bits_equal(pools.value, v_ref)
+    _err(geom, out, ref)
+
+
 def test_fused_call_equals_the_separate_calls():
     geom = FUSED[2]
     wl = make_workload(geom, device="cuda")

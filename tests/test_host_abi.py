@@ -85,6 +85,36 @@ def test_window_table_errors(pkv):
         pkv.pkv_window_table(ids[:1], 0, 40, 0, 40, 16)  # too few block ids
 
 
+def test_window_capacity_worked_example(pkv):
+    """P1 max_video_blocks' own case: at 1560 tokens per frame a 9-frame sink and
+    a 9-frame window are each 8 tokens past a block edge, 28080 tokens
+    together: rounding the sum once (1755 blocks) is a block short, rounding
+    each range on its own gives 878 + 878.  One action block comes on top even
+    without actions (P1 build_block_table)."""
+    assert pkv.pkv_window_capacity(9 * 1560, 9 * 1560, 1560, 16, 0) == 878 + 878 + 1
+    assert -(-(18 * 1560) // 16) == 1755
+    assert pkv.pkv_window_capacity(1560, 4680, 1560, 16, 0) == 98 + 293 + 1  # the frame workload: 392 blocks
+    assert pkv.pkv_window_capacity(0, 64, 32, 16, 40) == 0 + 4 + 3  # whole-block chunks never straddle
+    with pytest.raises(ValueError):
+        pkv.pkv_window_capacity(0, 64, 0, 16)
+
+
+@pytest.mark.parametrize("chunk,sink_chunks,window_chunks", [(1560, 1, 3), (24, 1, 2), (40, 2, 3), (7, 3, 5), (48, 0, 4), (30, 1, 1)])
+def test_window_capacity_bounds_every_tick_and_is_reached(pkv, chunk, sink_chunks, window_chunks):
+    """Brute force over AR ticks: the blocks holding a kept position (the sink,
+    and the recent window ending at the chunk's end, which sits on a whole
+    number of chunks) never outnumber the capacity's video part, and some tick
+    needs all of it once the recent range has slid past the sink."""
+    B, S, W = 16, sink_chunks * chunk, window_chunks * chunk
+    video_cap = pkv.pkv_window_capacity(S, W, chunk, B, 0) - 1
+    most = 0
+    for tick in range(64):
+        end = (tick + 1) * chunk
+        kept = set(range(min(S, end))) | set(range(max(0, end - W), end))
+        most = max(most, len({p // B for p in kept}))
+    assert most == video_cap
+
+
 def test_segments_match_oracle(pkv):
     rng = np.random.default_rng(11)
     for _ in range(300):
