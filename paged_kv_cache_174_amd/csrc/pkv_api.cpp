@@ -202,9 +202,14 @@ void plan_long_splits(SplitPlan& p, int64_t num_q_tokens, int num_q_heads, int n
       }
     }
   }
-  if (best_sp == 0) {  // nothing fits the table slice: equal splits of at most kMaxSplitKeys
-    best_sp = std::min(kMaxSplits, (max_seq_len + kMaxSplitKeys - 1) / kMaxSplitKeys);
-    best_a = ((max_seq_len + best_sp - 1) / best_sp + kMfmaKeyTile - 1) / kMfmaKeyTile;
+  if (best_sp == 0) {
+    // Nothing fits (no workspace for the splits the table slice needs, or more
+    // than kMaxSplits of them): the smallest split count that fits the slice,
+    // which the caller then refuses for want of a workspace or as unsupported.
+    p.splits = (max_seq_len + kMaxSplitKeys - 1) / kMaxSplitKeys;
+    p.split_len = kMaxSplitKeys / kMfmaKeyTile * kMfmaKeyTile;
+    for (int z = 0; z < std::min(p.splits, kMaxSplits); ++z) p.tiles[z] = p.split_len / kMfmaKeyTile;
+    return;
   }
   p.splits = best_sp;
   for (int z = 0; z < best_sp; ++z) p.tiles[z] = z + 1 < best_sp ? best_a : std::max(1, T - (best_sp - 1) * best_a);

@@ -88,6 +88,12 @@ def test_more_key_splits_than_supported_are_refused():
     with pytest.raises(G.P.PkvError):
         G.P.pkv_paged_attn(li.q, pools, table, plan.query_start_loc, plan.seq_lens, plan.segments,
                            plan.segment_start_loc, 0.1, plan.max_query_len, max_seq_len)
+    # with a workspace for any number of splits it is still refused (unsupported), not run
+    ws = torch.empty(32 * sum(plan.query_lens) * geom.num_q_heads * 264, dtype=torch.uint8, device="cuda")
+    with pytest.raises(G.P.PkvError) as err:
+        G.P.pkv_paged_attn(li.q, pools, table, plan.query_start_loc, plan.seq_lens, plan.segments,
+                           plan.segment_start_loc, 0.1, plan.max_query_len, max_seq_len, workspace=ws)
+    assert err.value.status == G.P._lib.PKV_EUNSUPPORTED
 
 
 def test_gqa_rows_straddling_waves_with_key_splits():

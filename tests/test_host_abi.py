@@ -115,6 +115,51 @@ def test_window_capacity_bounds_every_tick_and_is_reached(pkv, chunk, sink_chunk
     assert most == video_cap
 
 
+def _attn_on_fake_pointers(pkv, num_seqs, q_len, hq, hkv, max_seq_len, host=None, workspace_bytes=1 << 40):
+    """pkv_paged_attn with placeholder device pointers: the host checks and the
+    split planner run, and a call they refuse returns before any launch."""
+    lib = pkv.lib()
+    pools = pkv._lib._Pools(key=16, value=16, num_blocks=1 << 22, block_size=16, num_kv_heads=hkv, head_dim=128,
+                             dtype=pkv.PKV_BF16, k_scale=1.0, v_scale=1.0, k_inv_scale=1.0, v_inv_scale=1.0)
+    hl = (ctypes.c_int32 * num_seqs)(*host) if host else None
+    p = ctypes.c_void_p(16)
+    return lib.pkv_paged_attn(p, pkv.PKV_BF16, num_seqs * q_len, hq, ctypes.byref(pools), p, (max_seq_len + 15) // 16,
+                              p, p, num_seqs, q_len, max_seq_len, p, p, None, hl, 0.088, p, p, workspace_bytes, None)
+
+
+def test_more_key_splits_than_the_kernels_take_are_refused_before_launch(pkv):
+    """A key range needing more than 16 splits of one workgroup's table slice
+    (4095 blocks) is refused on the host even with a workspace for them."""
+    split_keys = 4095 * 16
+    assert _attn_on_fake_pointers(pkv, 1, 64, 2, 2, 16 * split_keys + 16) == pkv._lib.PKV_EUNSUPPORTED
+    assert "16 key splits" in pkv.pkv_last_error()
+
+
+@pytest.mark.parametrize("num_seqs,q_len,hq,hkv,max_seq_len,host", [
+    (2, 1560, 12, 12, 6272, [6240, 6240]), (2, 1560, 40, 40, 9392, [9360, 9360]), (1, 4680, 40, 8, 6240, None),
+    (3, 700, 8, 2, 200000, [150000, 90000, 3000]), (2, 300, 4, 4, 70000, None), (1, 2000, 4, 1, 1000000, None)])
+def test_long_split_plans_cover_the_keys(pkv, num_seqs, q_len, hq, hkv, max_seq_len, host):
+    """The long bf16 kernel's split plan: cuts on 64-key tiles from 0, split
+    lengths that never increase, no split longer than one table slice, and the
+    last split running on to max_seq_len.  (Read from the plan string of a call
+    whose launch fails: CPU only, it would launch on a GPU.)"""
+    import torch
+
+    if torch.cuda.device_count() > 0:
+        pytest.skip("the call would launch on placeholder pointers")
+    rc = _attn_on_fake_pointers(pkv, num_seqs, q_len, hq, hkv, max_seq_len, host)
+    assert rc == pkv._lib.PKV_EHIP  # the checks and the plan passed; only the launch failed
+    plan = pkv.pkv_last_attn_plan()
+    fields = dict(f.split("=") for f in plan.split()[1:])
+    assert plan.startswith("long ")
+    splits = int(fields["splits"])
+    cuts = [0] + ([int(c) for c in fields["cut"].split(",")] if splits > 1 else []) + [max_seq_len]
+    assert len(cuts) == splits + 1 and all(c % 64 == 0 for c in cuts[:-1])
+    lens = [b - a for a, b in zip(cuts, cuts[1:])]
+    assert all(x > 0 for x in lens) and all(x <= 4095 * 16 for x in lens)
+    assert all(a >= b for a, b in zip(lens[:-2], lens[1:-1]))  # the last one also runs on past the plan
+
+
 def test_segments_match_oracle(pkv):
     rng = np.random.default_rng(11)
     for _ in range(300):
