@@ -173,7 +173,9 @@ attn_mfma_kernel(AttnArgs a) {
     const uint32_t grp = xcd + 8u * (pos / per_group);
     if (grp >= static_cast<uint32_t>(a.num_seqs) * static_cast<uint32_t>(a.num_kv_heads)) return;
     const uint32_t item = pos % per_group;
-    rt = static_cast<int>(item % static_cast<uint32_t>(a.row_tiles));
+    // last row tile first: a later row tile never sees fewer keys, so the
+    // longest items of a causal chunk go out first and the short ones fill in
+    rt = a.row_tiles - 1 - static_cast<int>(item % static_cast<uint32_t>(a.row_tiles));
     z = static_cast<int>(item / static_cast<uint32_t>(a.row_tiles));
     hk = static_cast<int>(grp % static_cast<uint32_t>(a.num_kv_heads));
     const int b_pos = static_cast<int>(grp / static_cast<uint32_t>(a.num_kv_heads));
