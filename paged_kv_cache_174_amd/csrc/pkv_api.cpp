@@ -136,11 +136,23 @@ bool plan_short_packed(SplitPlan& p, int64_t num_q_tokens, int num_q_heads, int 
 // every plan: the next workgroup to the first CU to come free, or workgroups
 // dealt in turn to four groups of CUs, each taking its next one on its first
 // free CU.  The model takes the later of the two finishing times, which ranked
-// every measured plan in the right order.  Returns the busiest XCD's time.
+// every measured plan in the right order.  With more than eight workgroups per
+// CU the order hardly matters and the model is the fluid bound (the work
+// spread evenly, plus half the longest workgroup).  Returns the busiest XCD's
+// time.
 double model_long_launch(const int* tiles, int splits, int64_t groups_per_xcd, int row_tiles, int cus_per_xcd) {
   constexpr double kTile = 1.5e-6, kWorkgroup = 6e-6;
   constexpr int kCuGroups = 4;
   const int cus = std::max(kCuGroups, cus_per_xcd);
+  if (groups_per_xcd * row_tiles * splits > 8LL * cus) {
+    double total = 0.0, longest = 0.0;
+    for (int z = 0; z < splits; ++z) {
+      const double cost = tiles[z] * kTile + kWorkgroup;
+      total += cost * static_cast<double>(groups_per_xcd * row_tiles);
+      longest = std::max(longest, cost);
+    }
+    return total / cus + 0.5 * longest;
+  }
   auto later = [](double x, double y) { return x > y; };
   std::vector<double> any(static_cast<size_t>(cus), 0.0);  // min-heaps of CU free times
   std::vector<std::vector<double>> dealt(kCuGroups, std::vector<double>(static_cast<size_t>(cus / kCuGroups), 0.0));
@@ -166,7 +178,8 @@ double model_long_launch(const int* tiles, int splits, int64_t groups_per_xcd, i
 // Key splits of the long bf16 kernel.  Candidates: for each split count, the
 // first splits of A tiles each and a last one of the remaining tiles (1 to A),
 // so that the short last split's workgroups fill in where the launch's last
-// round would leave CUs idle.  Each is scored by model_long_launch plus the
+// round would leave CUs idle (A swept in about a dozen steps for two to four
+// splits; equal splits for more, where the rounds are already short).  Each is scored by model_long_launch plus the
 // partials' round trip; a split must buy a clear gain.  plan_len is the
 // longest sequence (the host lengths when given, else max_seq_len); the last
 // split runs on to max_seq_len, and no split may span more keys than a
@@ -184,8 +197,8 @@ void plan_long_splits(SplitPlan& p, int64_t num_q_tokens, int num_q_heads, int n
   int best_sp = 0, best_a = T;
   for (int sp = 1; sp <= max_sp; ++sp) {
     if (sp > 1 && (!have_workspace || workspace_bytes < static_cast<size_t>(per_split_bytes) * sp)) break;
-    const int a_lo = (T + sp - 1) / sp, a_hi = sp == 1 ? T : (T - 1) / (sp - 1);
-    const int step = std::max(1, (a_hi - a_lo) / 24);
+    const int a_lo = (T + sp - 1) / sp, a_hi = (sp == 1 || sp > 4) ? a_lo : (T - 1) / (sp - 1);
+    const int step = std::max(1, (a_hi - a_lo) / 12);
     for (int A = a_lo; A <= a_hi; A += step) {
       int tiles[kMaxSplits];
       for (int z = 0; z + 1 < sp; ++z) tiles[z] = A;
