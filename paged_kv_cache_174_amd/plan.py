@@ -22,6 +22,10 @@ import torch
 
 from . import _lib as L
 
+# A fixed-capacity table wider than this many blocks (4M tokens of 16) is a
+# window that does not bound the history, not a capacity.
+MAX_FIXED_CAPACITY_BLOCKS = 1 << 18
+
 
 @dataclass
 class ForwardPlan:
@@ -121,6 +125,10 @@ class ForwardPlan:
         if fixed_capacity:
             caps = [L.pkv_window_capacity(sink_tokens[b], window_tokens[b], query_lens[b], block_size, acts[b])
                     for b in range(n)]
+            if max(caps) > MAX_FIXED_CAPACITY_BLOCKS:
+                raise ValueError(
+                    f"fixed_capacity needs a bounded window: sequence {int(np.argmax(caps))} would take a "
+                    f"{max(caps)}-entry table (at most {MAX_FIXED_CAPACITY_BLOCKS})")
             width = max(max(caps), max(len(t) for t in tables))
             if table_width is None:
                 table_width = width

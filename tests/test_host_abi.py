@@ -115,6 +115,23 @@ def test_window_capacity_bounds_every_tick_and_is_reached(pkv, chunk, sink_chunk
     assert most == video_cap
 
 
+def test_fixed_capacity_plan_needs_a_bounded_window(pkv):
+    """P1's fixed-shape metadata: width and max_seq_len from the window's
+    capacity; a window that keeps everything has no capacity to pad to."""
+    geom = CONFIGS["frame_bf16"]
+    wl = make_workload(geom, device="cpu")
+    plan = pkv.ForwardPlan.build(wl.block_ids, geom.history_lens, geom.query_lens, geom.sink_tokens,
+                                 geom.window_tokens, geom.full_spans, geom.causal_default, geom.block_size,
+                                 fixed_capacity=True)
+    assert plan.block_table_host.shape == (2, 392) and plan.max_seq_len == 392 * 16 and plan.kv_lens == [6240, 6240]
+    assert (plan.block_table_host[:, 390:] == 0).all()  # tail padding with block 0, never read
+    big = small_variant(geom, name="unbounded", window_tokens=(1 << 30, 1 << 30), sink_tokens=(0, 0))
+    wl = make_workload(big, device="cpu")
+    with pytest.raises(ValueError, match="bounded window"):
+        pkv.ForwardPlan.build(wl.block_ids, big.history_lens, big.query_lens, big.sink_tokens, big.window_tokens,
+                              big.full_spans, big.causal_default, big.block_size, fixed_capacity=True)
+
+
 def _attn_on_fake_pointers(pkv, num_seqs, q_len, hq, hkv, max_seq_len, host=None, workspace_bytes=1 << 40):
     """pkv_paged_attn with placeholder device pointers: the host checks and the
     split planner run, and a call they refuse returns before any launch."""
