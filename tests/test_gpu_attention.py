@@ -301,6 +301,32 @@ def test_varlen_fp8_a_row_block_of_every_sequence():
     _check(geom, out, ref, rows=rows, heads=heads)
 
 
+UNEVEN = [
+    small_variant(CONFIGS["frame_bf16"], name="uneven_splits_full_bf16", num_q_heads=24, num_kv_heads=24,
+                  history_lens=(1720, 1720), query_lens=(280, 280), sink_tokens=(0, 0),
+                  window_tokens=(1 << 30, 1 << 30), full_spans=(None, None)),
+    small_variant(CONFIGS["frame_bf16"], name="uneven_splits_causal_bf16", num_q_heads=24, num_kv_heads=24,
+                  history_lens=(1720, 1720), query_lens=(280, 280), sink_tokens=(0, 0),
+                  window_tokens=(1 << 30, 1 << 30), full_spans=((), ()), causal_default=True),
+]
+
+
+@pytest.mark.parametrize("geom", UNEVEN, ids=[g.name for g in UNEVEN])
+def test_key_splits_of_unequal_length(geom):
+    """The long kernel's planner cuts this launch's 2000 keys into splits of
+    896, 896 and 208 keys (the short one fills in behind the others), and
+    each head's 280 rows are a full row tile and a 24-row tail.  Every row of
+    every head against the oracle; with causal rows the last split is empty
+    for the chunk's early rows, which write an empty partial."""
+    wl = make_workload(geom, device="cuda")
+    li = wl.layer(0)
+    G.say("uneven splits", geom.name)
+    _, _, _, out = G.run(wl, li=li)
+    assert "splits=3" in pkv.pkv_last_attn_plan() and "cut=896,1792" in pkv.pkv_last_attn_plan()
+    _, _, _, ref = H.run_layer(wl, li=li)
+    _check(geom, out, ref)
+
+
 @pytest.mark.parametrize("gain", [30.0, 8.0])
 def test_scores_far_above_the_first_subtile(gain):
     """The long-chunk kernel fixes each row's running max after its first
