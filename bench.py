@@ -5,9 +5,11 @@ layer (pkv_paged_write_attn): the current chunk's K/V is scattered into the
 pools through the slot mapping, then the chunk's queries attend over the
 visible history through the block table (the attention kernel, then the merge
 of key splits).  The 40-layer workload runs that call once per layer, each
-layer with its own pools and inputs, all sharing one metadata plan.  Inputs,
-pools and metadata are resident in HBM before timing starts; the history is
-written (untimed) during setup.
+layer with its own pools and inputs, all sharing one metadata plan; workloads
+with a sliding window get the pages' fixed-capacity metadata (table width and
+max_seq_len at the window's capacity).  Inputs, pools and metadata are
+resident in HBM before timing starts; the history is written (untimed) during
+setup.
 
 Prints one JSON line.  `value` is algorithmic attention TFLOP/s over whole
 steps (4 * D * Hq * visible query-key pairs per call).  `roofline` is for the

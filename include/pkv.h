@@ -528,7 +528,9 @@ const char* pkv_last_error(void);
 
 /* Thread-local description of the kernel plan the last attention call on this
    thread chose (after its checks passed): "long", "short" or "fp8" with the key
-   splits and their length, or "f32".  Diagnostic only: the format may change. */
+   splits and their length (for "long", the keys where splits 1, 2, ... start:
+   the splits may differ in length), or "f32".  Diagnostic only: the format may
+   change. */
 const char* pkv_last_attn_plan(void);
 
 /*
