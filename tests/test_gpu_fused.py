@@ -172,7 +172,8 @@ def test_staged_fused_call_restages_then_reuses(pool):
     B = geom.block_size
     wl = make_workload(geom, device="cuda")
     cap_blocks = -(-geom.sink_tokens[0] // B) + -(-geom.window_tokens[0] // B) + 1  # + one action block
-    plan = G.make_plan(wl, table_width=cap_blocks, max_seq_len=cap_blocks * B)
+    plan = G.make_plan(wl, fixed_capacity=True)  # P1 build_block_table's fixed shape (whole-block chunks)
+    assert plan.block_table.shape[1] == cap_blocks and plan.max_seq_len == cap_blocks * B
     n_blocks = plan.max_seq_len // B
     dt = G.TORCH_DT[pool]
     shape = (plan.max_seq_len + 2 * B, geom.num_kv_heads, geom.head_dim)
@@ -279,8 +280,8 @@ def test_fused_call_replays_in_a_hip_graph_across_ticks(pool):
         g = small_variant(geom, history_lens=(h, h), num_blocks=geom.num_blocks)
         wl = Workload(geom=g, device="cuda", block_ids=ids, action_block_ids=[np.zeros(0, np.int64)] * 2)
         plan = G.P.ForwardPlan.build(ids, g.history_lens, g.query_lens, g.sink_tokens, g.window_tokens,
-                                     g.full_spans, g.causal_default, B, table_width=width, max_seq_len=max_seq,
-                                     device="cuda")
+                                     g.full_spans, g.causal_default, B, fixed_capacity=True, device="cuda")
+        assert plan.block_table.shape[1] == width and plan.max_seq_len == max_seq  # one shape for every tick
         plan.validate(g.pool_blocks())
         q = _draw((2 * chunk, Hq, D), 100 + t, act)
         k = _draw((2 * chunk, Hkv, D), 200 + t, act)
@@ -362,7 +363,8 @@ def test_staged_calls_replay_in_two_graphs():
     geom = _staged_geom("bf16", chunk)
     cap_blocks = -(-geom.sink_tokens[0] // B) + -(-geom.window_tokens[0] // B) + 1
     wl = make_workload(geom, device="cuda")
-    plan = G.make_plan(wl, table_width=cap_blocks, max_seq_len=cap_blocks * B)
+    plan = G.make_plan(wl, fixed_capacity=True)
+    assert plan.block_table.shape[1] == cap_blocks and plan.max_seq_len == cap_blocks * B
     li0 = wl.layer(0)
     pools = G.make_pools(geom, li0)
     G.P.pkv_paged_write(li0.k_hist, li0.v_hist, plan.history_slot_mapping, pools)
